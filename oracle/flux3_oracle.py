@@ -1,0 +1,359 @@
+"""Plain CPU oracle for the FLUX.3 Image Klein transformer block.
+
+TEST INFRASTRUCTURE ONLY.  This module is the correctness reference that the
+HIP path is compared against.  Only the test suite, the package entry's
+smoke check and the benchmark's CPU-baseline leg may import or call it; the
+product path never does, and nothing here is shared with the HIP kernels or
+their host code.
+
+Sources (the release pages; cited by page title and section):
+
+* [P1]  "FLUX.3 Image Klein Is Now Available in Diffusers" (15jq.com),
+        section "Speed, architecture, and how the tokens move".
+* [P3]  The Chinese translation of the Diffusers release post (everytik.com):
+        the `block(x, shift, scale, gate)` listing and the RoPE position
+        table under the model walk-through.
+* [P4]  "How to Run FLUX 3 Image Klein Locally" (rohitghumare.com), sections
+        "Inside the transformer", "The latent space and the VAE",
+        "What step distillation removed".
+* [P5]  The ifeeling.app summary, architecture paragraphs (reference offset
+        runs negatively along l).
+
+Readings where the pages are silent (each is a parameter or a documented
+constant): LayerNorm/RMSNorm epsilon 1e-6; RMSNorm per 128-dim head with a
+learned [128] scale; RoPE base theta = 10000 with adjacent pairs (2i, 2i+1)
+and axis a owning head dims [32a, 32a+32); image/reference h, w = row/2,
+col/2 taken as real division on the token-grid index (hw_scale = 0.5);
+attention scale 1/sqrt(128); an output projection after attention; no
+biases; SwiGLU with silu on the gate branch; shift, scale, gate order.
+
+Precision: float64 by default (pass dtype=np.float32 for the large timing
+runs).  Every function follows its definition directly; the only blocking is
+an optional split of attention over independent query rows, which does not
+change any sum.
+
+Parity status per function (pins live in tests/test_oracle_pins.py):
+  token_positions, rope_tables, apply_rope, layer_norm, modulate,
+  rms_norm_heads, attention, silu, swiglu_mlp, block_forward,
+  block_forward_rows, stack_forward, timestep_embedding,
+  modulation_from_t, shifted_sigmas: all pinned.
+"""
+import numpy as np
+
+EPS_LN = 1e-6
+EPS_RMS = 1e-6
+THETA = 10000.0
+HW_SCALE = 0.5
+ROPE_AXES = 4          # (t, h, w, l)   [P1], [P3] RoPE table
+AXIS_DIM = 32          # a quarter of each 128-dim head per axis   [P1]
+
+MODE_TEXT, MODE_IMAGE, MODE_REF = 0, 1, 2
+
+
+# --------------------------------------------------------------------------
+# helpers
+# --------------------------------------------------------------------------
+def as_float(a, dtype=np.float64):
+    """Weights arrive either as float arrays or as bfloat16 bit patterns
+    (uint16).  A bfloat16 value is the upper half of an IEEE binary32, so
+    the bits are widened by a 16-bit shift and reinterpreted."""
+    a = np.asarray(a)
+    if a.dtype == np.uint16:
+        a = (a.astype(np.uint32) << 16).view(np.float32)
+    return a.astype(dtype)
+
+
+# --------------------------------------------------------------------------
+# positions and rotary tables    [P1] RoPE paragraph, [P3] RoPE table, [P5]
+# --------------------------------------------------------------------------
+def token_positions(n_text, grid_h, grid_w, refs=(), hw_scale=HW_SCALE):
+    """(t, h, w, l) for every token, in sequence order [text | image | refs].
+
+    Text token i sits at (0, 0, 0, i).  The noisy-image token at grid
+    (row, col) sits at (0, row/2, col/2, 0).  Token (row, col) of reference
+    k (0-based) sits at (0, row/2, col/2, -(k+1)).  Image rows are in raster
+    order (row-major), the flattening of the packed latent grid [P4 "The
+    latent space and the VAE"].  hw_scale=0.5 is the row/2 reading.
+    """
+    pos = []
+    for i in range(n_text):
+        pos.append((0.0, 0.0, 0.0, float(i)))
+    for row in range(grid_h):
+        for col in range(grid_w):
+            pos.append((0.0, row * hw_scale, col * hw_scale, 0.0))
+    for k, (rh, rw) in enumerate(refs):
+        for row in range(rh):
+            for col in range(rw):
+                pos.append((0.0, row * hw_scale, col * hw_scale, float(-(k + 1))))
+    return np.array(pos, dtype=np.float64).reshape(-1, 4)
+
+
+def rope_tables(positions, theta=THETA):
+    """cos/sin table [N][64][2] in float32, computed in float64, rounded once.
+
+    Pair p = 16*a + j of a head belongs to axis a (t, h, w, l) and rotates
+    by angle positions[:, a] * theta**(-2j/32): the standard rotary
+    frequencies over a 32-dim sub-space, one sub-space per axis [P1].
+    """
+    positions = np.asarray(positions, dtype=np.float64)
+    n = positions.shape[0]
+    half = AXIS_DIM // 2
+    table = np.zeros((n, ROPE_AXES * half, 2), dtype=np.float64)
+    for a in range(ROPE_AXES):
+        for j in range(half):
+            omega = theta ** (-2.0 * j / AXIS_DIM)
+            phi = positions[:, a] * omega
+            table[:, a * half + j, 0] = np.cos(phi)
+            table[:, a * half + j, 1] = np.sin(phi)
+    return table.astype(np.float32)
+
+
+def apply_rope(x, table):
+    """Rotate each adjacent pair (2p, 2p+1) of every head by the table angle.
+
+    x: [N][H][128]; table: [N][64][2] (cos, sin).  (x0, x1) becomes
+    (x0 cos - x1 sin, x0 sin + x1 cos).
+    """
+    x = np.asarray(x)
+    cos = np.asarray(table[:, None, :, 0], dtype=x.dtype)
+    sin = np.asarray(table[:, None, :, 1], dtype=x.dtype)
+    x0 = x[..., 0::2]
+    x1 = x[..., 1::2]
+    out = np.empty_like(x)
+    out[..., 0::2] = x0 * cos - x1 * sin
+    out[..., 1::2] = x0 * sin + x1 * cos
+    return out
+
+
+# --------------------------------------------------------------------------
+# block pieces    [P3] block listing, [P1], [P4 "Inside the transformer"]
+# --------------------------------------------------------------------------
+def layer_norm(x, eps=EPS_LN):
+    """LayerNorm over the last axis with no learned scale or shift."""
+    mu = x.mean(axis=-1, keepdims=True)
+    var = ((x - mu) ** 2).mean(axis=-1, keepdims=True)
+    return (x - mu) / np.sqrt(var + eps)
+
+
+def modulate(hhat, shift, scale):
+    """adaLN modulation (1 + scale) * h + shift."""
+    return (1.0 + scale) * hhat + shift
+
+
+def rms_norm_heads(x, weight, eps=EPS_RMS):
+    """RMS normalisation over each head's 128 dims, times a [128] scale."""
+    ms = (x ** 2).mean(axis=-1, keepdims=True)
+    return x / np.sqrt(ms + eps) * weight
+
+
+def attention(q, k, v, chunk=None):
+    """Full bidirectional softmax attention per head, no mask.
+
+    q, k, v: [N][H][128] (q may have fewer rows than k, v).  Scores are
+    q.k / sqrt(128), softmax over all keys (max subtracted), times v.
+    Returns [Nq][H][128].  chunk splits the query rows (each row's softmax
+    is still taken over every key in one piece).
+    """
+    nq, n_heads, hd = q.shape
+    scale = 1.0 / np.sqrt(hd)
+    out = np.empty((nq, n_heads, hd), dtype=q.dtype)
+    step = nq if not chunk else chunk
+    for h in range(n_heads):
+        kh = k[:, h, :]
+        vh = v[:, h, :]
+        for r0 in range(0, nq, max(step, 1)):
+            qh = q[r0:r0 + step, h, :]
+            s = (qh @ kh.T) * scale
+            s = s - s.max(axis=-1, keepdims=True)
+            p = np.exp(s)
+            p = p / p.sum(axis=-1, keepdims=True)
+            out[r0:r0 + step, h, :] = p @ vh
+    return out
+
+
+def silu(z):
+    """z * sigmoid(z)."""
+    return z / (1.0 + np.exp(-z))
+
+
+def swiglu_mlp(h, w_gate, w_up, w_down):
+    """SwiGLU feed-forward: (silu(h W_gate^T) * (h W_up^T)) W_down^T."""
+    return (silu(h @ w_gate.T) * (h @ w_up.T)) @ w_down.T
+
+
+def _row_modulation(segs, mod, n, dtype):
+    """Expand per-segment (shift, scale, gate) to per-row arrays [N][D]."""
+    mod = np.asarray(mod, dtype=dtype)
+    width = mod.shape[-1]
+    shift = np.zeros((n, width), dtype)
+    scale = np.zeros((n, width), dtype)
+    gate = np.zeros((n, width), dtype)
+    covered = np.zeros(n, bool)
+    for s, (start, count, _mode) in enumerate(segs):
+        shift[start:start + count] = mod[s, 0]
+        scale[start:start + count] = mod[s, 1]
+        gate[start:start + count] = mod[s, 2]
+        covered[start:start + count] = True
+    if not covered.all():
+        raise ValueError("segments must cover every token")
+    return shift, scale, gate
+
+
+def _weights(w, dtype):
+    return {name: as_float(val, dtype) for name, val in w.items()}
+
+
+def block_forward(x, w, segs, mod, rope, heads=None, dtype=np.float64,
+                  eps_ln=EPS_LN, eps_rms=EPS_RMS, keep=False, attn_chunk=None):
+    """One transformer block, following the release's block listing [P3]:
+
+      h = layer_norm(x)                       (no learned affine)
+      h = (1 + scale) * h + shift             (per-segment modulation)
+      q, k, v = to_q(h), to_k(h), to_v(h)
+      q, k = rope(rms_norm(q)), rope(rms_norm(k))
+      out = to_out(attention(q, k, v)) + mlp(h)      (parallel; SwiGLU)
+      return x + gate * out
+
+    x: [N][D]; w: dict of weights (torch Linear layout [out][in]); segs:
+    list of (start, count, mode) covering [0, N); mod: [n_segs][3][D]
+    (shift, scale, gate) for each segment -- each token type gets its own
+    vectors [P1]; rope: [N][64][2] table.  keep=True also returns the
+    intermediates {h, q, k, v, o, act, out}.
+    """
+    x = np.asarray(x, dtype=dtype)
+    n, width = x.shape
+    wf = _weights(w, dtype)
+    hd = wf["q_norm"].shape[0]
+    if heads is None:
+        heads = width // hd
+    shift, scale, gate = _row_modulation(segs, mod, n, dtype)
+
+    h = modulate(layer_norm(x, eps_ln), shift, scale)
+    q = (h @ wf["wq"].T).reshape(n, heads, hd)
+    k = (h @ wf["wk"].T).reshape(n, heads, hd)
+    v = (h @ wf["wv"].T).reshape(n, heads, hd)
+    q = apply_rope(rms_norm_heads(q, wf["q_norm"], eps_rms), rope)
+    k = apply_rope(rms_norm_heads(k, wf["k_norm"], eps_rms), rope)
+    o = attention(q, k, v, chunk=attn_chunk).reshape(n, width)
+    a = o @ wf["wo"].T
+    act = silu(h @ wf["w_gate"].T) * (h @ wf["w_up"].T)
+    m = act @ wf["w_down"].T
+    out = a + m
+    x_new = x + gate * out
+    if keep:
+        return x_new, {"h": h, "q": q, "k": k, "v": v, "o": o, "act": act,
+                       "out": out}
+    return x_new
+
+
+def block_forward_rows(x, w, segs, mod, rope, rows, heads=None,
+                       dtype=np.float64, eps_ln=EPS_LN, eps_rms=EPS_RMS,
+                       attn_chunk=None):
+    """block_forward evaluated only at the output rows listed in `rows`.
+
+    The same steps as block_forward: keys and values are computed for every
+    token (attention reads all of them), queries, attention, the MLP and
+    the residual only for the requested rows.  Returns [len(rows)][D].
+    """
+    x = np.asarray(x, dtype=dtype)
+    rows = np.asarray(rows, dtype=np.int64)
+    n, width = x.shape
+    wf = _weights(w, dtype)
+    hd = wf["q_norm"].shape[0]
+    if heads is None:
+        heads = width // hd
+    shift, scale, gate = _row_modulation(segs, mod, n, dtype)
+
+    h = modulate(layer_norm(x, eps_ln), shift, scale)
+    k = (h @ wf["wk"].T).reshape(n, heads, hd)
+    v = (h @ wf["wv"].T).reshape(n, heads, hd)
+    k = apply_rope(rms_norm_heads(k, wf["k_norm"], eps_rms), rope)
+    hr = h[rows]
+    q = (hr @ wf["wq"].T).reshape(len(rows), heads, hd)
+    q = apply_rope(rms_norm_heads(q, wf["q_norm"], eps_rms), rope[rows])
+    o = attention(q, k, v, chunk=attn_chunk).reshape(len(rows), width)
+    out = o @ wf["wo"].T + swiglu_mlp(hr, wf["w_gate"], wf["w_up"], wf["w_down"])
+    return x[rows] + gate[rows] * out
+
+
+def stack_forward(x, per_mode, joint, segs, mod_stage1, mod_stage2, rope,
+                  dtype=np.float64, per_block_mod=False):
+    """The two-stage stack [P1], [P4 "Inside the transformer"].
+
+    Stage 1: every segment (stream) runs the per-mode blocks of its own mode
+    on its rows alone, attending only to itself.  Stage 2: the concatenated
+    sequence [text | image | refs] runs the joint blocks, all tokens sharing
+    the weights while each segment keeps its own modulation.
+
+    per_mode[mode] is a list of block weight dicts (5 each); joint is a list
+    (28).  mod_stage1 / mod_stage2: [n_segs][3][D] shared by every block of
+    the stage, or, with per_block_mod, [n_blocks][n_segs][3][D].
+    """
+    out = np.array(x, dtype=dtype, copy=True)
+    for s, (start, count, mode) in enumerate(segs):
+        rows = slice(start, start + count)
+        for b, wb in enumerate(per_mode[mode]):
+            m1 = mod_stage1[b] if per_block_mod else mod_stage1
+            out[rows] = block_forward(out[rows], wb, [(0, count, mode)],
+                                      np.asarray(m1)[s:s + 1], rope[rows],
+                                      dtype=dtype)
+    for b, wb in enumerate(joint):
+        m2 = mod_stage2[b] if per_block_mod else mod_stage2
+        out = block_forward(out, wb, segs, m2, rope, dtype=dtype)
+    return out
+
+
+# --------------------------------------------------------------------------
+# timestep modulation (input side of the hot path)
+#   [P1] modulation paragraphs, [P4 "Inside the transformer",
+#   "What step distillation removed"], [P3] sampler notes on sigma*1000
+# --------------------------------------------------------------------------
+def timestep_embedding(t, dim=256, max_period=10000.0):
+    """Sinusoidal embedding of tau = 1000 * t: [cos(tau f_i), sin(tau f_i)],
+    f_i = max_period**(-i/(dim/2)), i < dim/2 (the transformer positional
+    encoding of Vaswani et al. applied to the timestep)."""
+    half = dim // 2
+    tau = 1000.0 * float(t)
+    f = max_period ** (-np.arange(half, dtype=np.float64) / half)
+    return np.concatenate([np.cos(tau * f), np.sin(tau * f)])
+
+
+def modulation_from_t(t_by_mode, w1, w2, w_mod, t_target=None, w1_tgt=None,
+                      w2_tgt=None, dtype=np.float64):
+    """Per-mode (shift, scale, gate) from timesteps.
+
+    The embedder is two bias-free layers 256 -> D -> D with silu between
+    [P4 "What step distillation removed"].  Noisy-image tokens use the
+    current t; text and reference tokens always use t = 0 [P1], so their
+    vectors never depend on the image timestep.  The distilled flow map adds
+    a second embedder's output for the target timestep to every mode
+    [P4 same section].  w_mod[mode] maps silu(embedding) to 3*D, split in
+    the order shift, scale, gate.  Returns {mode: [3][D]}.
+    """
+    w1, w2 = as_float(w1, dtype), as_float(w2, dtype)
+    extra = 0.0
+    if t_target is not None:
+        extra = as_float(w2_tgt, dtype) @ silu(as_float(w1_tgt, dtype) @ timestep_embedding(t_target))
+    out = {}
+    for mode, t in t_by_mode.items():
+        e = w2 @ silu(w1 @ timestep_embedding(t)) + extra
+        m = as_float(w_mod[mode], dtype) @ silu(e)
+        out[mode] = m.reshape(3, -1)
+    return out
+
+
+# --------------------------------------------------------------------------
+# sampler schedule (outside the block; pinned by printed values)
+#   [P4 "The denoise loop", "What step distillation removed"]
+# --------------------------------------------------------------------------
+def shifted_sigmas(steps, shift=6.93):
+    """steps noise levels evenly spaced from 1 down to 1/steps, each mapped
+    through sigma' = shift*sigma / (1 + (shift - 1)*sigma), then a final 0."""
+    sig = np.linspace(1.0, 1.0 / steps, steps)
+    sig = shift * sig / (1.0 + (shift - 1.0) * sig)
+    return np.concatenate([sig, [0.0]])
+
+
+def euler_step(sample, v, sigma, sigma_next):
+    """Flow-matching Euler update: sample + (sigma_next - sigma) * v."""
+    return sample + (sigma_next - sigma) * v

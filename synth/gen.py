@@ -1,0 +1,85 @@
+"""Seeded random draws for block inputs.
+
+Every tensor comes from its own NumPy PCG64 stream keyed by
+(seed, block_id, tensor_id), so any one block's weights can be regenerated
+without drawing the others.  Weights are drawn in fp32 from N(0, 0.02^2) and
+rounded once to bfloat16 (round to nearest, ties to even); both the GPU path
+and the oracle consume those same bf16 values.
+
+The modulation vectors (shift, scale, gate per token segment) are drawn
+directly as N(0, MOD_STD^2) stand-ins for the output of the timestep
+embedding path; computing them from a timestep is a separate step that the
+hot path takes as an input.
+"""
+import numpy as np
+
+WEIGHT_STD = 0.02
+MOD_STD = 0.07
+
+# tensor ids inside one block
+T_WQ, T_WK, T_WV, T_WO, T_WGATE, T_WUP, T_WDOWN, T_QNORM, T_KNORM = range(9)
+# stream ids for non-weight tensors (block_id slot)
+_X_STREAM = 1_000_000
+_MOD_STREAM = 2_000_000
+
+
+def _rng(*key):
+    return np.random.Generator(np.random.PCG64(np.random.SeedSequence(list(key))))
+
+
+def bf16_round_bits(a):
+    """fp32 array -> uint16 bfloat16 bit patterns, round to nearest even."""
+    a = np.ascontiguousarray(a, dtype=np.float32)
+    u = a.view(np.uint32).astype(np.uint64)
+    rounded = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    return rounded.astype(np.uint16)
+
+
+def bf16_bits_to_f32(bits):
+    """uint16 bfloat16 bit patterns -> fp32 (exact)."""
+    bits = np.ascontiguousarray(bits, dtype=np.uint16)
+    return (bits.astype(np.uint32) << 16).view(np.float32)
+
+
+def _normal_bf16(shape, std, *key):
+    a = _rng(*key).standard_normal(int(np.prod(shape)), dtype=np.float32)
+    a *= np.float32(std)
+    return bf16_round_bits(a).reshape(shape)
+
+
+def block_weights(seed, block_id, dims, norm_stress=False, std=WEIGHT_STD):
+    """One block's weights, torch-Linear layout [out][in], as bf16 bits.
+
+    Returns a dict with uint16 arrays wq, wk, wv, wo [D][D], w_gate, w_up
+    [F][D], w_down [D][F], and float32 q_norm, k_norm [head_dim] (all ones
+    unless norm_stress, which draws 1 + N(0, 0.1^2)).
+    """
+    D, F, hd = dims.width, dims.mlp_hidden, dims.head_dim
+    w = {
+        "wq": _normal_bf16((D, D), std, seed, block_id, T_WQ),
+        "wk": _normal_bf16((D, D), std, seed, block_id, T_WK),
+        "wv": _normal_bf16((D, D), std, seed, block_id, T_WV),
+        "wo": _normal_bf16((D, D), std, seed, block_id, T_WO),
+        "w_gate": _normal_bf16((F, D), std, seed, block_id, T_WGATE),
+        "w_up": _normal_bf16((F, D), std, seed, block_id, T_WUP),
+        "w_down": _normal_bf16((D, F), std, seed, block_id, T_WDOWN),
+    }
+    if norm_stress:
+        w["q_norm"] = (1.0 + 0.1 * _rng(seed, block_id, T_QNORM).standard_normal(hd)).astype(np.float32)
+        w["k_norm"] = (1.0 + 0.1 * _rng(seed, block_id, T_KNORM).standard_normal(hd)).astype(np.float32)
+    else:
+        w["q_norm"] = np.ones(hd, np.float32)
+        w["k_norm"] = np.ones(hd, np.float32)
+    return w
+
+
+def tokens(seed, n, width):
+    """Residual-stream input x ~ N(0, 1), fp32 [n][width]."""
+    return _rng(seed, _X_STREAM, n, width).standard_normal((n, width), dtype=np.float32)
+
+
+def modulation(seed, stream, n_segs, width, std=MOD_STD):
+    """(shift, scale, gate) per segment: fp32 [n_segs][3][width] ~ N(0, std^2)."""
+    a = _rng(seed, _MOD_STREAM, stream, n_segs, width).standard_normal(
+        (n_segs, 3, width), dtype=np.float32)
+    return a * np.float32(std)
