@@ -1,0 +1,203 @@
+/*
+ * flux3.h -- C ABI of libflux3, the MI355X (gfx950) forward path of the
+ * FLUX.3 Image Klein transformer block and its two-stage stack.
+ *
+ * Sources (release pages, cited by title and section):
+ *   [P1] "FLUX.3 Image Klein Is Now Available in Diffusers" (15jq.com),
+ *        section "Speed, architecture, and how the tokens move".
+ *   [P3] Chinese translation of the Diffusers release post (everytik.com):
+ *        the block listing `block(x, shift, scale, gate)` and the RoPE
+ *        position table; the modular pipeline's `prepare_rope_inputs` step.
+ *   [P4] "How to Run FLUX 3 Image Klein Locally" (rohitghumare.com),
+ *        sections "Inside the transformer", "The latent space and the VAE".
+ *   [P5] ifeeling.app summary, architecture paragraphs (reference tokens
+ *        are offset negatively along l).
+ *
+ * Conventions shared by every entry point
+ *   - Device pointers are caller-owned HIP device memory; the library never
+ *     allocates, frees or keeps any of them past the call.  Host pointers
+ *     (segment lists, weight-struct arrays, layout arrays, dims) are read
+ *     during the call only.
+ *   - `stream` is a hipStream_t passed as void*; NULL means the default
+ *     stream.  Calls only enqueue work and return; results are ready after
+ *     the caller synchronises that stream.
+ *   - All arguments are validated on the host before anything is enqueued;
+ *     a non-zero status means nothing was enqueued.  After enqueue, a HIP
+ *     launch error maps to FLUX3_E_HIP.  Device faults surface at the
+ *     caller's next synchronisation.  No C++ exception crosses the ABI.
+ *     flux3_last_error_detail() returns a per-thread message for the last
+ *     failing call.
+ *   - bf16 is bfloat16 (IEEE binary32 upper half); accumulation is fp32.
+ *   - Device pointers must be 16-byte aligned (FLUX3_E_ALIGN otherwise).
+ *   - Supported dims: head_dim == 128, heads a positive even number,
+ *     width == heads * 128, mlp_hidden a positive multiple of 128
+ *     (FLUX3_E_UNSUPPORTED otherwise); n_tokens at most 2^20.
+ *     The model's are width 3072, 24 heads, 128, SwiGLU hidden 9216 [P4].
+ */
+#ifndef FLUX3_H
+#define FLUX3_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t flux3_status;
+enum {
+  FLUX3_OK = 0,
+  FLUX3_E_INVALID = -1,     /* null pointer, bad mode or enum value          */
+  FLUX3_E_SHAPE = -2,       /* sizes or segments inconsistent                */
+  FLUX3_E_UNSUPPORTED = -3, /* dims outside what the kernels implement       */
+  FLUX3_E_ALIGN = -4,       /* device pointer not 16-byte aligned            */
+  FLUX3_E_WORKSPACE = -5,   /* workspace missing or smaller than required    */
+  FLUX3_E_HIP = -6          /* HIP runtime reported an error                 */
+};
+
+#define FLUX3_MAX_SEGMENTS 16
+#define FLUX3_MAX_REFS 15
+
+/* Token modes, in the order the joint sequence concatenates them [P1]. */
+enum { FLUX3_MODE_TEXT = 0, FLUX3_MODE_IMAGE = 1, FLUX3_MODE_REF = 2 };
+
+typedef struct {
+  int32_t width;      /* model width D (3072)                  */
+  int32_t heads;      /* attention heads (24)                  */
+  int32_t head_dim;   /* per-head dims, must be 128            */
+  int32_t mlp_hidden; /* SwiGLU hidden width F (9216)          */
+} flux3_dims;
+
+/* A contiguous run of tokens of one kind.  Segments passed to a call must
+ * tile [0, n_tokens) in order, each with count > 0, and with modes in the
+ * sequence order text, image, reference (non-decreasing mode) [P1]. */
+typedef struct {
+  int32_t start;
+  int32_t count;
+  int32_t mode; /* FLUX3_MODE_* */
+} flux3_segment;
+
+/* One block's weights, all device pointers.  Matrices are bf16 in torch
+ * Linear layout [out][in], row-major, no biases [P3 block listing; P4]:
+ *   wq, wk, wv, wo : [width][width]
+ *   w_gate, w_up   : [mlp_hidden][width]   (silu acts on the w_gate branch)
+ *   w_down         : [width][mlp_hidden]
+ *   q_norm, k_norm : fp32 [head_dim] RMSNorm scales for queries and keys. */
+typedef struct {
+  const void *wq, *wk, *wv, *wo;
+  const void *w_gate, *w_up, *w_down;
+  const float *q_norm, *k_norm;
+} flux3_block_weights;
+
+/* Token layout of one call: n_text text tokens, a grid_h x grid_w noisy
+ * image grid (raster order), then n_refs reference grids ref_h[k] x ref_w[k]
+ * (host arrays).  theta is the RoPE base (10000 in this build's reading);
+ * hw_scale multiplies a grid row/col to give its h/w position (0.5 is the
+ * row/2, col/2 of the page table). */
+typedef struct {
+  int32_t n_text, grid_h, grid_w, n_refs;
+  const int32_t *ref_h, *ref_w;
+  double theta;
+  double hw_scale;
+} flux3_rope_layout;
+
+/* Number of tokens a layout describes; -1 if the layout is invalid. */
+int64_t flux3_layout_tokens(const flux3_rope_layout *layout);
+
+/* Rotary tables for a layout: the pipeline's prepare_rope_inputs step,
+ * run once per layout outside the block loop [P3 modular pipeline].
+ * Positions follow the page table [P3 RoPE table; P5]:
+ *   text token i            -> (t, h, w, l) = (0, 0, 0, i)
+ *   image token (row, col)  -> (0, row*hw_scale, col*hw_scale, 0)
+ *   reference k (row, col)  -> (0, row*hw_scale, col*hw_scale, -(k+1))
+ * Each 128-dim head gives every axis (t, h, w, l) 32 dims [P1]: pair
+ * p = 16a + j rotates by angle pos[a] * theta^(-2j/32).
+ * Output rope: device fp32 [n_tokens][64][2] = (cos, sin), computed in fp64
+ * and rounded once to fp32.  n_tokens must equal flux3_layout_tokens().
+ * Errors: FLUX3_E_INVALID (null), FLUX3_E_SHAPE (token count mismatch,
+ * negative sizes, n_refs > FLUX3_MAX_REFS), FLUX3_E_ALIGN. */
+flux3_status flux3_rope_tables_build(const flux3_rope_layout *layout,
+                                     float *rope, int64_t n_tokens,
+                                     void *stream);
+
+/* Workspace bytes block_forward / stack_forward need for n_tokens tokens
+ * (about 48 KiB per token at the model dims); 0 if dims are unsupported. */
+size_t flux3_workspace_bytes(const flux3_dims *dims, int64_t n_tokens);
+
+/* Byte offsets of the intermediates a block leaves in the workspace, so a
+ * caller can inspect them after the call: h = modulated LayerNorm output
+ * bf16 [n_pad][width]; q, k = RMS-normalised, rotated queries/keys bf16
+ * [heads][n_pad][128]; vt = values bf16 [heads][128][n_pad] with keys
+ * permuted inside every 16 (groups of 4 in the order 0, 2, 1, 3); cat =
+ * bf16 [n_pad][width + mlp_hidden] holding the attention output in columns
+ * [0, width) and silu(gate)*up in [width, width + mlp_hidden).  n_pad is
+ * n_tokens rounded up to 256.  Returns FLUX3_E_UNSUPPORTED for bad dims. */
+typedef struct {
+  size_t h, q, k, vt, cat, total;
+  int64_t n_pad;
+} flux3_workspace_layout;
+flux3_status flux3_workspace_layout_get(const flux3_dims *dims, int64_t n_tokens,
+                                        flux3_workspace_layout *out);
+
+/* One transformer block, in place on the fp32 residual stream [P3 block
+ * listing; P1; P4 "Inside the transformer"]:
+ *   h   = (1 + scale_s) * LayerNorm(x) + shift_s     (no learned affine)
+ *   q,k = RoPE(RMSNorm(h Wq^T)), RoPE(RMSNorm(h Wk^T)); v = h Wv^T
+ *   out = Attention(q, k, v) Wo^T + (silu(h Wg^T) * (h Wu^T)) Wd^T
+ *   x  += gate_s * out
+ * where (shift_s, scale_s, gate_s) belong to the token's segment s; every
+ * token attends to all n_tokens tokens.  A per-mode (stage-1) block is this
+ * call on one stream's rows with a single segment.
+ *   x    : device fp32 [n_tokens][width], updated in place.
+ *   segs : host [n_segs], tiling [0, n_tokens) (see flux3_segment),
+ *          1 <= n_segs <= FLUX3_MAX_SEGMENTS.
+ *   mod  : device fp32 [n_segs][3][width] = shift, scale, gate per segment.
+ *   rope : device fp32 [n_tokens][64][2] from flux3_rope_tables_build (or a
+ *          row slice of one).
+ *   workspace: device, >= flux3_workspace_bytes(dims, n_tokens) bytes.
+ * n_tokens == 0 with n_segs == 0 is a no-op returning FLUX3_OK. */
+flux3_status flux3_block_forward(const flux3_dims *dims,
+                                 const flux3_block_weights *w, float *x,
+                                 int64_t n_tokens, const flux3_segment *segs,
+                                 int32_t n_segs, const float *mod,
+                                 const float *rope, void *workspace,
+                                 size_t workspace_bytes, void *stream);
+
+/* The two-stage stack [P1; P4 "Inside the transformer"]:
+ * stage 1 runs, for every segment s, the n_pm per-mode blocks of its mode
+ * on that segment's rows alone (each stream attends only to itself);
+ * stage 2 runs the n_joint joint blocks over all n_tokens with per-segment
+ * modulation.
+ *   per_mode : host array [3 * n_pm]; block b of mode m is
+ *              per_mode[m * n_pm + b] (entries of unused modes may be
+ *              zeroed; they are only checked if a segment uses that mode).
+ *   joint    : host array [n_joint].
+ *   mod_stage1, mod_stage2 : device fp32; block b of a stage reads
+ *              [n_segs][3][width] at offset b * mod_block_stride floats
+ *              (stride 0 shares one set of vectors across the stage;
+ *              a non-zero stride must be a multiple of 4).
+ *   Other arguments as in flux3_block_forward. */
+flux3_status flux3_stack_forward(const flux3_dims *dims,
+                                 const flux3_block_weights *per_mode,
+                                 int32_t n_pm,
+                                 const flux3_block_weights *joint,
+                                 int32_t n_joint, float *x, int64_t n_tokens,
+                                 const flux3_segment *segs, int32_t n_segs,
+                                 const float *mod_stage1,
+                                 const float *mod_stage2,
+                                 int64_t mod_block_stride, const float *rope,
+                                 void *workspace, size_t workspace_bytes,
+                                 void *stream);
+
+/* Debug switch: when non-zero every launch is followed by a stream
+ * synchronisation and an error check, so a faulting kernel is named in
+ * flux3_last_error_detail().  Off by default. */
+void flux3_set_debug_sync(int32_t on);
+
+const char *flux3_status_string(flux3_status s);
+const char *flux3_last_error_detail(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* FLUX3_H */

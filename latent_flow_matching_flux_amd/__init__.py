@@ -1,0 +1,15 @@
+"""MI355X (gfx950) forward path of the FLUX.3 Image Klein transformer block.
+
+The computation lives in libflux3.so (HIP kernels behind the C ABI in
+include/flux3.h); this package holds the build script and a thin ctypes
+binding with the same entry-point names.
+"""
+from ._lib import (Flux3Error, Dims, Segment, BlockWeights, RopeLayout, WorkspaceLayout,
+                   load, layout_tokens, rope_tables_build, workspace_bytes, workspace_layout,
+                   block_forward, stack_forward, set_debug_sync, status_string, EXPORTS,
+                   LIB_PATH)
+
+__all__ = ["Flux3Error", "Dims", "Segment", "BlockWeights", "RopeLayout", "WorkspaceLayout",
+           "load", "layout_tokens", "rope_tables_build", "workspace_bytes", "workspace_layout",
+           "block_forward", "stack_forward", "set_debug_sync", "status_string", "EXPORTS",
+           "LIB_PATH"]

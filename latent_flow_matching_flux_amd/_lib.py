@@ -1,0 +1,234 @@
+"""ctypes binding to libflux3.so: argument marshalling only.
+
+Every function here converts Python/torch arguments to the C ABI declared in
+include/flux3.h and calls it; all computation runs in the library's HIP
+kernels.  torch is used for device memory and streams.  If the library is
+missing the import-time loader raises: there is no fallback path.
+"""
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libflux3.so")
+
+FLUX3_OK = 0
+STATUS_NAMES = {0: "FLUX3_OK", -1: "FLUX3_E_INVALID", -2: "FLUX3_E_SHAPE",
+                -3: "FLUX3_E_UNSUPPORTED", -4: "FLUX3_E_ALIGN",
+                -5: "FLUX3_E_WORKSPACE", -6: "FLUX3_E_HIP"}
+MAX_SEGMENTS = 16
+MAX_REFS = 15
+
+# exported symbols, in the order include/flux3.h declares them
+EXPORTS = ("flux3_layout_tokens", "flux3_rope_tables_build", "flux3_workspace_bytes",
+           "flux3_workspace_layout_get", "flux3_block_forward", "flux3_stack_forward",
+           "flux3_set_debug_sync", "flux3_status_string", "flux3_last_error_detail")
+
+
+class Flux3Error(RuntimeError):
+    def __init__(self, status, detail):
+        self.status = status
+        self.detail = detail
+        super().__init__(f"{STATUS_NAMES.get(status, status)}: {detail}")
+
+
+class Dims(ctypes.Structure):
+    _fields_ = [("width", ctypes.c_int32), ("heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("mlp_hidden", ctypes.c_int32)]
+
+
+class Segment(ctypes.Structure):
+    _fields_ = [("start", ctypes.c_int32), ("count", ctypes.c_int32), ("mode", ctypes.c_int32)]
+
+
+class BlockWeights(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in
+                ("wq", "wk", "wv", "wo", "w_gate", "w_up", "w_down", "q_norm", "k_norm")]
+
+
+class RopeLayout(ctypes.Structure):
+    _fields_ = [("n_text", ctypes.c_int32), ("grid_h", ctypes.c_int32),
+                ("grid_w", ctypes.c_int32), ("n_refs", ctypes.c_int32),
+                ("ref_h", ctypes.POINTER(ctypes.c_int32)),
+                ("ref_w", ctypes.POINTER(ctypes.c_int32)),
+                ("theta", ctypes.c_double), ("hw_scale", ctypes.c_double)]
+
+
+class WorkspaceLayout(ctypes.Structure):
+    _fields_ = [("h", ctypes.c_size_t), ("q", ctypes.c_size_t), ("k", ctypes.c_size_t),
+                ("vt", ctypes.c_size_t), ("cat", ctypes.c_size_t), ("total", ctypes.c_size_t),
+                ("n_pad", ctypes.c_int64)]
+
+
+_lib = None
+
+
+def load(path=LIB_PATH):
+    """Load libflux3.so once and declare its signatures."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(f"libflux3.so not built at {path}; run __graft_entry__.build()")
+    lib = ctypes.CDLL(path)
+    P = ctypes.POINTER
+    i32, i64, sz, vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_void_p
+    lib.flux3_layout_tokens.argtypes = [P(RopeLayout)]
+    lib.flux3_layout_tokens.restype = i64
+    lib.flux3_rope_tables_build.argtypes = [P(RopeLayout), vp, i64, vp]
+    lib.flux3_rope_tables_build.restype = i32
+    lib.flux3_workspace_bytes.argtypes = [P(Dims), i64]
+    lib.flux3_workspace_bytes.restype = sz
+    lib.flux3_workspace_layout_get.argtypes = [P(Dims), i64, P(WorkspaceLayout)]
+    lib.flux3_workspace_layout_get.restype = i32
+    lib.flux3_block_forward.argtypes = [P(Dims), P(BlockWeights), vp, i64, P(Segment), i32,
+                                        vp, vp, vp, sz, vp]
+    lib.flux3_block_forward.restype = i32
+    lib.flux3_stack_forward.argtypes = [P(Dims), P(BlockWeights), i32, P(BlockWeights), i32,
+                                        vp, i64, P(Segment), i32, vp, vp, i64, vp, vp, sz, vp]
+    lib.flux3_stack_forward.restype = i32
+    lib.flux3_set_debug_sync.argtypes = [i32]
+    lib.flux3_set_debug_sync.restype = None
+    lib.flux3_status_string.argtypes = [i32]
+    lib.flux3_status_string.restype = ctypes.c_char_p
+    lib.flux3_last_error_detail.argtypes = []
+    lib.flux3_last_error_detail.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def _check(status):
+    if status != FLUX3_OK:
+        detail = load().flux3_last_error_detail().decode()
+        raise Flux3Error(status, detail)
+
+
+def _ptr(t):
+    """Device (or host) address of a tensor, an int address, or None -> NULL."""
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream_handle(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def make_dims(d):
+    """Dims from any object with width/heads/head_dim/mlp_hidden."""
+    if isinstance(d, Dims):
+        return d
+    return Dims(d.width, d.heads, d.head_dim, d.mlp_hidden)
+
+
+def make_segments(segs):
+    arr = (Segment * max(len(segs), 1))()
+    for i, s in enumerate(segs):
+        if hasattr(s, "start"):
+            arr[i] = Segment(s.start, s.count, s.mode)
+        else:
+            arr[i] = Segment(*s)
+    return arr, len(segs)
+
+
+def make_weights(w):
+    """BlockWeights from a dict of tensors (keys as in the header struct)."""
+    if isinstance(w, BlockWeights):
+        return w
+    return BlockWeights(*[_ptr(w.get(k)) for k in
+                          ("wq", "wk", "wv", "wo", "w_gate", "w_up", "w_down", "q_norm", "k_norm")])
+
+
+def make_layout(lay):
+    """RopeLayout from an object with n_text, grid_h, grid_w, refs, theta,
+    hw_scale.  Keeps the ref arrays alive on the returned struct."""
+    refs = list(getattr(lay, "refs", ()))
+    rh = (ctypes.c_int32 * max(len(refs), 1))(*[r[0] for r in refs])
+    rw = (ctypes.c_int32 * max(len(refs), 1))(*[r[1] for r in refs])
+    out = RopeLayout(lay.n_text, lay.grid_h, lay.grid_w, len(refs),
+                     ctypes.cast(rh, ctypes.POINTER(ctypes.c_int32)),
+                     ctypes.cast(rw, ctypes.POINTER(ctypes.c_int32)),
+                     float(lay.theta), float(lay.hw_scale))
+    out._keep = (rh, rw)
+    return out
+
+
+def layout_tokens(lay):
+    return load().flux3_layout_tokens(ctypes.byref(make_layout(lay)))
+
+
+def rope_tables_build(lay, rope, n_tokens=None, stream=None):
+    """flux3_rope_tables_build: fill rope [N][64][2] fp32 for a layout."""
+    L = make_layout(lay)
+    if n_tokens is None:
+        n_tokens = rope.shape[0] if rope is not None else 0
+    _check(load().flux3_rope_tables_build(ctypes.byref(L), _ptr(rope), n_tokens,
+                                          _stream_handle(stream)))
+
+
+def workspace_bytes(dims, n_tokens):
+    return load().flux3_workspace_bytes(ctypes.byref(make_dims(dims)), n_tokens)
+
+
+def workspace_layout(dims, n_tokens):
+    out = WorkspaceLayout()
+    _check(load().flux3_workspace_layout_get(ctypes.byref(make_dims(dims)), n_tokens,
+                                             ctypes.byref(out)))
+    return out
+
+
+def block_forward(dims, w, x, segs, mod, rope, workspace, n_tokens=None,
+                  workspace_nbytes=None, stream=None):
+    """flux3_block_forward: one block in place on x [N][D] fp32."""
+    seg_arr, n_segs = make_segments(segs)
+    W = make_weights(w)
+    if n_tokens is None:
+        n_tokens = x.shape[0]
+    if workspace_nbytes is None:
+        workspace_nbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(load().flux3_block_forward(ctypes.byref(make_dims(dims)), ctypes.byref(W), _ptr(x),
+                                      n_tokens, seg_arr, n_segs, _ptr(mod), _ptr(rope),
+                                      _ptr(workspace), workspace_nbytes, _stream_handle(stream)))
+
+
+def stack_forward(dims, per_mode, joint, x, segs, mod_stage1, mod_stage2, rope, workspace,
+                  mod_block_stride=0, n_tokens=None, workspace_nbytes=None, stream=None):
+    """flux3_stack_forward.  per_mode: {mode: [weights dict, ...]} (equal
+    lengths) or a flat list of 3*n_pm weights; joint: list of weights."""
+    if isinstance(per_mode, dict):
+        n_pm = max((len(v) for v in per_mode.values()), default=0)
+        flat = []
+        for m in range(3):
+            blocks = per_mode.get(m, [])
+            for b in range(n_pm):
+                flat.append(make_weights(blocks[b]) if b < len(blocks) else BlockWeights())
+    else:
+        flat = [make_weights(w) for w in per_mode]
+        n_pm = len(flat) // 3
+    pm_arr = (BlockWeights * max(len(flat), 1))(*flat)
+    jn = [make_weights(w) for w in joint]
+    j_arr = (BlockWeights * max(len(jn), 1))(*jn)
+    seg_arr, n_segs = make_segments(segs)
+    if n_tokens is None:
+        n_tokens = x.shape[0]
+    if workspace_nbytes is None:
+        workspace_nbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(load().flux3_stack_forward(ctypes.byref(make_dims(dims)), pm_arr, n_pm, j_arr,
+                                      len(jn), _ptr(x), n_tokens, seg_arr, n_segs,
+                                      _ptr(mod_stage1), _ptr(mod_stage2), mod_block_stride,
+                                      _ptr(rope), _ptr(workspace), workspace_nbytes,
+                                      _stream_handle(stream)))
+
+
+def set_debug_sync(on):
+    load().flux3_set_debug_sync(1 if on else 0)
+
+
+def status_string(status):
+    return load().flux3_status_string(status).decode()

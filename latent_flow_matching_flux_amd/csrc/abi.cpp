@@ -1,0 +1,352 @@
+// C ABI of libflux3: host-side validation, workspace carving and the
+// per-block launch sequence (K1 ln_modulate -> K2 projection GEMM -> K3
+// attention -> K4 output GEMM).  Every check runs before the first enqueue,
+// so a failing call enqueues nothing.
+#include <hip/hip_runtime.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "../../include/flux3.h"
+#include "kernels.hpp"
+
+namespace {
+
+thread_local char g_detail[512] = "";
+int g_debug_sync = 0;
+
+flux3_status fail(flux3_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_detail, sizeof g_detail, fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+flux3_status ok() {
+  g_detail[0] = '\0';
+  return FLUX3_OK;
+}
+
+constexpr float kEpsLN = 1e-6f;
+constexpr float kEpsRMS = 1e-6f;
+constexpr int64_t kRowAlign = 256;     // workspace rows are padded to this
+constexpr size_t kBufAlign = 256;      // byte alignment of each workspace buffer
+constexpr int64_t kMaxTokens = 1 << 20;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+flux3_status check_dims(const flux3_dims* d) {
+  if (!d) return fail(FLUX3_E_INVALID, "dims is NULL");
+  if (d->head_dim != 128)
+    return fail(FLUX3_E_UNSUPPORTED, "head_dim %d unsupported (must be 128)", d->head_dim);
+  if (d->heads < 2 || d->heads % 2 != 0)
+    return fail(FLUX3_E_UNSUPPORTED, "heads %d unsupported (must be a positive even number)", d->heads);
+  if (d->width != d->heads * 128)
+    return fail(FLUX3_E_UNSUPPORTED, "width %d != heads*128 (%d)", d->width, d->heads * 128);
+  if (d->mlp_hidden <= 0 || d->mlp_hidden % 128 != 0)
+    return fail(FLUX3_E_UNSUPPORTED, "mlp_hidden %d unsupported (positive multiple of 128)", d->mlp_hidden);
+  return FLUX3_OK;
+}
+
+bool layout_of(const flux3_dims* d, int64_t n, flux3_workspace_layout* L) {
+  const int64_t n_pad = (n + kRowAlign - 1) / kRowAlign * kRowAlign;
+  const size_t D = (size_t)d->width, F = (size_t)d->mlp_hidden, H = (size_t)d->heads;
+  size_t off = 0;
+  L->n_pad = n_pad;
+  L->h = off;   off = align_up(off + (size_t)n_pad * D * 2, kBufAlign);
+  L->q = off;   off = align_up(off + H * (size_t)n_pad * 128 * 2, kBufAlign);
+  L->k = off;   off = align_up(off + H * (size_t)n_pad * 128 * 2, kBufAlign);
+  L->vt = off;  off = align_up(off + H * 128 * (size_t)n_pad * 2, kBufAlign);
+  L->cat = off; off = align_up(off + (size_t)n_pad * (D + F) * 2, kBufAlign);
+  L->total = off;
+  return true;
+}
+
+flux3_status check_weights(const flux3_block_weights* w, const char* what, int idx) {
+  if (!w) return fail(FLUX3_E_INVALID, "%s[%d] weights struct is NULL", what, idx);
+  const void* ptrs[9] = {w->wq, w->wk, w->wv, w->wo, w->w_gate, w->w_up, w->w_down,
+                         w->q_norm, w->k_norm};
+  static const char* names[9] = {"wq", "wk", "wv", "wo", "w_gate", "w_up", "w_down",
+                                 "q_norm", "k_norm"};
+  for (int i = 0; i < 9; ++i) {
+    if (!ptrs[i]) return fail(FLUX3_E_INVALID, "%s[%d].%s is NULL", what, idx, names[i]);
+    if (!aligned16(ptrs[i]))
+      return fail(FLUX3_E_ALIGN, "%s[%d].%s is not 16-byte aligned", what, idx, names[i]);
+  }
+  return FLUX3_OK;
+}
+
+flux3_status check_segments(const flux3_segment* segs, int32_t n_segs, int64_t n,
+                            flux3::SegTableHost* st) {
+  if (n_segs < 1 || n_segs > FLUX3_MAX_SEGMENTS)
+    return fail(FLUX3_E_SHAPE, "n_segs %d outside [1, %d]", n_segs, FLUX3_MAX_SEGMENTS);
+  if (!segs) return fail(FLUX3_E_INVALID, "segs is NULL");
+  int64_t pos = 0;
+  int prev_mode = 0;
+  for (int i = 0; i < n_segs; ++i) {
+    const flux3_segment& s = segs[i];
+    if (s.mode < FLUX3_MODE_TEXT || s.mode > FLUX3_MODE_REF)
+      return fail(FLUX3_E_INVALID, "segment %d has mode %d", i, s.mode);
+    if (s.mode < prev_mode)
+      return fail(FLUX3_E_SHAPE, "segment %d mode %d after mode %d (order is text, image, reference)",
+                  i, s.mode, prev_mode);
+    if (s.count <= 0) return fail(FLUX3_E_SHAPE, "segment %d has count %d", i, s.count);
+    if (s.start != pos)
+      return fail(FLUX3_E_SHAPE, "segment %d starts at %d, expected %lld", i, s.start, (long long)pos);
+    pos += s.count;
+    prev_mode = s.mode;
+    st->start[i] = s.start;
+  }
+  for (int i = n_segs; i < 16; ++i) st->start[i] = 0;
+  st->n = n_segs;
+  if (pos != n)
+    return fail(FLUX3_E_SHAPE, "segments cover %lld tokens, n_tokens is %lld", (long long)pos,
+                (long long)n);
+  return FLUX3_OK;
+}
+
+flux3_status check_ws(const flux3_dims* d, int64_t n, void* ws, size_t ws_bytes,
+                      flux3_workspace_layout* L) {
+  layout_of(d, n, L);
+  if (!ws) return fail(FLUX3_E_WORKSPACE, "workspace is NULL");
+  if ((reinterpret_cast<uintptr_t>(ws) & (kBufAlign - 1)) != 0)
+    return fail(FLUX3_E_ALIGN, "workspace is not %zu-byte aligned", kBufAlign);
+  if (ws_bytes < L->total)
+    return fail(FLUX3_E_WORKSPACE, "workspace has %zu bytes, needs %zu", ws_bytes, L->total);
+  return FLUX3_OK;
+}
+
+flux3::WsPtrs carve(void* ws, const flux3_workspace_layout& L) {
+  char* b = static_cast<char*>(ws);
+  flux3::WsPtrs p;
+  p.h = b + L.h;
+  p.q = b + L.q;
+  p.k = b + L.k;
+  p.vt = b + L.vt;
+  p.cat = b + L.cat;
+  return p;
+}
+
+flux3::BlockWeightsDev dev_weights(const flux3_block_weights& w) {
+  flux3::BlockWeightsDev d;
+  d.wq = w.wq; d.wk = w.wk; d.wv = w.wv; d.wo = w.wo;
+  d.w_gate = w.w_gate; d.w_up = w.w_up; d.w_down = w.w_down;
+  d.q_norm = w.q_norm; d.k_norm = w.k_norm;
+  return d;
+}
+
+flux3_status after_launch(hipError_t e, const char* what, hipStream_t s) {
+  if (e != hipSuccess) return fail(FLUX3_E_HIP, "%s launch: %s", what, hipGetErrorString(e));
+  if (g_debug_sync) {
+    e = hipStreamSynchronize(s);
+    if (e != hipSuccess) return fail(FLUX3_E_HIP, "%s execution: %s", what, hipGetErrorString(e));
+  }
+  return FLUX3_OK;
+}
+
+// Enqueue one block on rows [0, n) of x (already validated).
+flux3_status run_block(const flux3_dims* d, const flux3_block_weights& w, float* x, int64_t n,
+                       const flux3::SegTableHost& st, const float* mod, const float* rope,
+                       void* ws, hipStream_t s) {
+  flux3_workspace_layout L;
+  layout_of(d, n, &L);
+  const flux3::WsPtrs wp = carve(ws, L);
+  flux3::BlockShape bs;
+  bs.M = (int32_t)n;
+  bs.n_pad = (int32_t)L.n_pad;
+  bs.D = d->width;
+  bs.H = d->heads;
+  bs.F = d->mlp_hidden;
+  const flux3::BlockWeightsDev wd = dev_weights(w);
+  flux3_status r;
+  if ((r = after_launch(flux3::launch_ln_modulate(bs, x, mod, st, wp.h, kEpsLN, s),
+                        "ln_modulate", s)) != FLUX3_OK)
+    return r;
+  if ((r = after_launch(flux3::launch_gemm_proj(bs, wd, rope, wp, kEpsRMS, s), "gemm_proj",
+                        s)) != FLUX3_OK)
+    return r;
+  if ((r = after_launch(flux3::launch_attention(bs, wp, s), "attention", s)) != FLUX3_OK)
+    return r;
+  if ((r = after_launch(flux3::launch_gemm_out(bs, wd, wp, x, mod, st, s), "gemm_out", s)) !=
+      FLUX3_OK)
+    return r;
+  return FLUX3_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int64_t flux3_layout_tokens(const flux3_rope_layout* L) {
+  if (!L) return -1;
+  if (L->n_text < 0 || L->grid_h < 0 || L->grid_w < 0 || L->n_refs < 0 ||
+      L->n_refs > FLUX3_MAX_REFS)
+    return -1;
+  if ((L->grid_h == 0) != (L->grid_w == 0)) return -1;
+  int64_t n = (int64_t)L->n_text + (int64_t)L->grid_h * L->grid_w;
+  if (L->n_refs > 0 && (!L->ref_h || !L->ref_w)) return -1;
+  for (int k = 0; k < L->n_refs; ++k) {
+    if (L->ref_h[k] <= 0 || L->ref_w[k] <= 0) return -1;
+    n += (int64_t)L->ref_h[k] * L->ref_w[k];
+  }
+  return n;
+}
+
+flux3_status flux3_rope_tables_build(const flux3_rope_layout* layout, float* rope,
+                                     int64_t n_tokens, void* stream) {
+  if (!layout) return fail(FLUX3_E_INVALID, "layout is NULL");
+  const int64_t n = flux3_layout_tokens(layout);
+  if (n < 0) return fail(FLUX3_E_SHAPE, "invalid layout (negative size, n_refs > %d or missing ref arrays)", FLUX3_MAX_REFS);
+  if (n != n_tokens)
+    return fail(FLUX3_E_SHAPE, "layout has %lld tokens, n_tokens is %lld", (long long)n,
+                (long long)n_tokens);
+  if (n > kMaxTokens) return fail(FLUX3_E_SHAPE, "n_tokens %lld above %lld", (long long)n, (long long)kMaxTokens);
+  if (n == 0) return ok();
+  if (!rope) return fail(FLUX3_E_INVALID, "rope is NULL");
+  if (!aligned16(rope)) return fail(FLUX3_E_ALIGN, "rope is not 16-byte aligned");
+  flux3::RopeLayoutDev dl;
+  memset(&dl, 0, sizeof dl);
+  dl.n_text = layout->n_text;
+  dl.grid_h = layout->grid_h;
+  dl.grid_w = layout->grid_w;
+  dl.n_refs = layout->n_refs;
+  for (int k = 0; k < layout->n_refs; ++k) {
+    dl.ref_h[k] = layout->ref_h[k];
+    dl.ref_w[k] = layout->ref_w[k];
+  }
+  dl.theta = layout->theta;
+  dl.hw_scale = layout->hw_scale;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  flux3_status r = after_launch(flux3::launch_rope_tables(dl, rope, n, s), "rope_tables", s);
+  return r == FLUX3_OK ? ok() : r;
+}
+
+size_t flux3_workspace_bytes(const flux3_dims* dims, int64_t n_tokens) {
+  if (check_dims(dims) != FLUX3_OK || n_tokens < 0 || n_tokens > kMaxTokens) return 0;
+  flux3_workspace_layout L;
+  layout_of(dims, n_tokens, &L);
+  return L.total;
+}
+
+flux3_status flux3_workspace_layout_get(const flux3_dims* dims, int64_t n_tokens,
+                                        flux3_workspace_layout* out) {
+  flux3_status r = check_dims(dims);
+  if (r != FLUX3_OK) return r;
+  if (!out) return fail(FLUX3_E_INVALID, "out is NULL");
+  if (n_tokens < 0 || n_tokens > kMaxTokens)
+    return fail(FLUX3_E_SHAPE, "n_tokens %lld outside [0, %lld]", (long long)n_tokens, (long long)kMaxTokens);
+  layout_of(dims, n_tokens, out);
+  return ok();
+}
+
+flux3_status flux3_block_forward(const flux3_dims* dims, const flux3_block_weights* w, float* x,
+                                 int64_t n_tokens, const flux3_segment* segs, int32_t n_segs,
+                                 const float* mod, const float* rope, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+  flux3_status r = check_dims(dims);
+  if (r != FLUX3_OK) return r;
+  if (n_tokens < 0 || n_tokens > kMaxTokens)
+    return fail(FLUX3_E_SHAPE, "n_tokens %lld outside [0, %lld]", (long long)n_tokens, (long long)kMaxTokens);
+  if (n_tokens == 0) {
+    if (n_segs != 0) return fail(FLUX3_E_SHAPE, "n_tokens is 0 but n_segs is %d", n_segs);
+    return ok();
+  }
+  if ((r = check_weights(w, "w", 0)) != FLUX3_OK) return r;
+  if (!x || !mod || !rope) return fail(FLUX3_E_INVALID, "x, mod or rope is NULL");
+  if (!aligned16(x) || !aligned16(mod) || !aligned16(rope))
+    return fail(FLUX3_E_ALIGN, "x, mod or rope is not 16-byte aligned");
+  flux3::SegTableHost st;
+  if ((r = check_segments(segs, n_segs, n_tokens, &st)) != FLUX3_OK) return r;
+  flux3_workspace_layout L;
+  if ((r = check_ws(dims, n_tokens, workspace, workspace_bytes, &L)) != FLUX3_OK) return r;
+  r = run_block(dims, *w, x, n_tokens, st, mod, rope, workspace, static_cast<hipStream_t>(stream));
+  return r == FLUX3_OK ? ok() : r;
+}
+
+flux3_status flux3_stack_forward(const flux3_dims* dims, const flux3_block_weights* per_mode,
+                                 int32_t n_pm, const flux3_block_weights* joint, int32_t n_joint,
+                                 float* x, int64_t n_tokens, const flux3_segment* segs,
+                                 int32_t n_segs, const float* mod_stage1, const float* mod_stage2,
+                                 int64_t mod_block_stride, const float* rope, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+  flux3_status r = check_dims(dims);
+  if (r != FLUX3_OK) return r;
+  if (n_tokens < 0 || n_tokens > kMaxTokens)
+    return fail(FLUX3_E_SHAPE, "n_tokens %lld outside [0, %lld]", (long long)n_tokens, (long long)kMaxTokens);
+  if (n_pm < 0 || n_joint < 0) return fail(FLUX3_E_SHAPE, "n_pm %d / n_joint %d negative", n_pm, n_joint);
+  if (mod_block_stride < 0) return fail(FLUX3_E_SHAPE, "mod_block_stride is negative");
+  if (n_tokens == 0) {
+    if (n_segs != 0) return fail(FLUX3_E_SHAPE, "n_tokens is 0 but n_segs is %d", n_segs);
+    return ok();
+  }
+  if (!x || !rope) return fail(FLUX3_E_INVALID, "x or rope is NULL");
+  if (!aligned16(x) || !aligned16(rope)) return fail(FLUX3_E_ALIGN, "x or rope is not 16-byte aligned");
+  flux3::SegTableHost st;
+  if ((r = check_segments(segs, n_segs, n_tokens, &st)) != FLUX3_OK) return r;
+  if (n_pm > 0) {
+    if (!per_mode) return fail(FLUX3_E_INVALID, "per_mode is NULL");
+    if (!mod_stage1) return fail(FLUX3_E_INVALID, "mod_stage1 is NULL");
+    if (!aligned16(mod_stage1)) return fail(FLUX3_E_ALIGN, "mod_stage1 is not 16-byte aligned");
+    for (int s = 0; s < n_segs; ++s)
+      for (int b = 0; b < n_pm; ++b)
+        if ((r = check_weights(&per_mode[segs[s].mode * n_pm + b], "per_mode",
+                               segs[s].mode * n_pm + b)) != FLUX3_OK)
+          return r;
+  }
+  if (n_joint > 0) {
+    if (!joint) return fail(FLUX3_E_INVALID, "joint is NULL");
+    if (!mod_stage2) return fail(FLUX3_E_INVALID, "mod_stage2 is NULL");
+    if (!aligned16(mod_stage2)) return fail(FLUX3_E_ALIGN, "mod_stage2 is not 16-byte aligned");
+    for (int b = 0; b < n_joint; ++b)
+      if ((r = check_weights(&joint[b], "joint", b)) != FLUX3_OK) return r;
+  }
+  if (mod_block_stride % 4 != 0)
+    return fail(FLUX3_E_ALIGN, "mod_block_stride must be a multiple of 4 floats");
+  flux3_workspace_layout L;
+  if ((r = check_ws(dims, n_tokens, workspace, workspace_bytes, &L)) != FLUX3_OK) return r;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const size_t D = (size_t)dims->width;
+  // stage 1: each segment runs its own mode's blocks on its rows alone
+  for (int sg = 0; sg < n_segs && n_pm > 0; ++sg) {
+    flux3::SegTableHost one;
+    memset(&one, 0, sizeof one);
+    one.n = 1;
+    const int64_t start = segs[sg].start, cnt = segs[sg].count;
+    for (int b = 0; b < n_pm; ++b) {
+      const float* m1 = mod_stage1 + (size_t)b * mod_block_stride + (size_t)sg * 3 * D;
+      r = run_block(dims, per_mode[segs[sg].mode * n_pm + b], x + start * D, cnt, one, m1,
+                    rope + start * 128, workspace, s);
+      if (r != FLUX3_OK) return r;
+    }
+  }
+  // stage 2: joint blocks over the whole sequence
+  for (int b = 0; b < n_joint; ++b) {
+    r = run_block(dims, joint[b], x, n_tokens, st, mod_stage2 + (size_t)b * mod_block_stride,
+                  rope, workspace, s);
+    if (r != FLUX3_OK) return r;
+  }
+  return ok();
+}
+
+void flux3_set_debug_sync(int32_t on) { g_debug_sync = on; }
+
+const char* flux3_status_string(flux3_status s) {
+  switch (s) {
+    case FLUX3_OK: return "ok";
+    case FLUX3_E_INVALID: return "invalid argument";
+    case FLUX3_E_SHAPE: return "inconsistent shape or segments";
+    case FLUX3_E_UNSUPPORTED: return "unsupported dims";
+    case FLUX3_E_ALIGN: return "misaligned pointer";
+    case FLUX3_E_WORKSPACE: return "workspace missing or too small";
+    case FLUX3_E_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+const char* flux3_last_error_detail(void) { return g_detail; }
+
+}  // extern "C"

@@ -1,0 +1,50 @@
+// Device-side helpers shared by the gfx950 kernels of libflux3.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace flux3 {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+// 16-byte raw chunk; a native vector type so arrays of it stay in registers
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+constexpr int kHeadDim = 128;
+constexpr int kRopePairs = 64;        // 128 dims -> 64 rotated pairs
+constexpr int kMaxSegs = 16;
+
+// Per-call segment table passed by value to kernels that need the token ->
+// segment map (modulation rows, gates).
+struct SegTable {
+  int32_t start[kMaxSegs];
+  int32_t n;
+};
+
+__device__ __forceinline__ int seg_of(const SegTable& st, int m) {
+  int s = 0;
+#pragma unroll
+  for (int i = 1; i < kMaxSegs; ++i)
+    if (i < st.n && m >= st.start[i]) s = i;
+  return s;
+}
+
+// 32x32x16 bf16 MFMA, fp32 accumulate.  Output layout (per lane l, reg r):
+// column l % 32, row 8*(r/4) + 4*(l/32) + r%4.
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float bf2f(bf16 v) { return (float)v; }
+__device__ __forceinline__ bf16 f2bf(float v) { return (bf16)v; }  // RNE
+
+// Cross-lane exchange inside a wave (ds_bpermute based).
+__device__ __forceinline__ float xor_lane(float v, int mask) {
+  return __shfl_xor(v, mask, kWave);
+}
+
+}  // namespace flux3

@@ -1,0 +1,55 @@
+// Host-side launch interface between the C ABI (abi.cpp) and the kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace flux3 {
+
+struct RopeLayoutDev {
+  int32_t n_text, grid_h, grid_w, n_refs;
+  int32_t ref_h[15], ref_w[15];
+  double theta, hw_scale;
+};
+
+struct BlockShape {
+  int32_t M;       // tokens in this call
+  int32_t n_pad;   // M rounded up to 256: row count of workspace buffers
+  int32_t D;       // width
+  int32_t H;       // heads
+  int32_t F;       // SwiGLU hidden
+};
+
+struct SegTableHost {
+  int32_t start[16];
+  int32_t n;
+};
+
+struct WsPtrs {
+  void* h;    // bf16 [n_pad][D]
+  void* q;    // bf16 [H][n_pad][128]
+  void* k;    // bf16 [H][n_pad][128]
+  void* vt;   // bf16 [H][128][n_pad]
+  void* cat;  // bf16 [n_pad][D + F]
+};
+
+struct BlockWeightsDev {
+  const void *wq, *wk, *wv, *wo, *w_gate, *w_up, *w_down;
+  const float *q_norm, *k_norm;
+};
+
+hipError_t launch_rope_tables(const RopeLayoutDev& lay, float* rope, int64_t n,
+                              hipStream_t s);
+hipError_t launch_ln_modulate(const BlockShape& bs, const float* x,
+                              const float* mod, const SegTableHost& segs,
+                              void* h, float eps, hipStream_t s);
+hipError_t launch_gemm_proj(const BlockShape& bs, const BlockWeightsDev& w,
+                            const float* rope, const WsPtrs& ws, float eps,
+                            hipStream_t s);
+hipError_t launch_attention(const BlockShape& bs, const WsPtrs& ws,
+                            hipStream_t s);
+hipError_t launch_gemm_out(const BlockShape& bs, const BlockWeightsDev& w,
+                           const WsPtrs& ws, float* x, const float* mod,
+                           const SegTableHost& segs, hipStream_t s);
+
+}  // namespace flux3

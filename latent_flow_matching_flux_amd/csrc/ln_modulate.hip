@@ -1,0 +1,110 @@
+// K1: parameter-free LayerNorm + per-segment adaLN modulation.
+//
+// Every block starts with a LayerNorm that has no learned affine; the scale
+// and shift come from the timestep embedding, per token type ("Speed,
+// architecture, and how the tokens move", 15jq.com post; block listing of
+// the Diffusers release post, everytik.com translation):
+//   h = (1 + scale_s) * (x - mean) / sqrt(var + eps) + shift_s
+// Statistics are fp32 over the row (biased variance, two passes over
+// registers); h is written as bf16, the GEMM operand type.
+//
+// One wave per row; each lane holds width/64 values.  HBM-bound: reads 4 B
+// and writes 2 B per element (the modulation vectors stay in cache).
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace flux3 {
+
+template <int D>
+__global__ __launch_bounds__(256) void k_ln_modulate(
+    const float* __restrict__ x, const float* __restrict__ mod, SegTable segs,
+    bf16* __restrict__ h, int M, float eps) {
+  constexpr int V = D / (kWave * 4);  // float4 per lane
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= M) return;
+  const float4* xr = reinterpret_cast<const float4*>(x + (size_t)row * D);
+  float4 v[V];
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < V; ++i) {
+    v[i] = xr[lane + 64 * i];
+    s += (v[i].x + v[i].y) + (v[i].z + v[i].w);
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) s += xor_lane(s, o);
+  const float mean = s * (1.0f / D);
+  float q = 0.f;
+#pragma unroll
+  for (int i = 0; i < V; ++i) {
+    const float a = v[i].x - mean, b = v[i].y - mean, c = v[i].z - mean,
+                d = v[i].w - mean;
+    q += (a * a + b * b) + (c * c + d * d);
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) q += xor_lane(q, o);
+  const float rstd = 1.0f / sqrtf(q * (1.0f / D) + eps);
+
+  const int sg = seg_of(segs, row);
+  const float4* shift = reinterpret_cast<const float4*>(mod + (size_t)sg * 3 * D);
+  const float4* scale = shift + D / 4;
+  bf16x4* hr = reinterpret_cast<bf16x4*>(h + (size_t)row * D);
+#pragma unroll
+  for (int i = 0; i < V; ++i) {
+    const int c = lane + 64 * i;
+    const float4 sh = shift[c], sc = scale[c];
+    bf16x4 o;
+    o[0] = f2bf((1.0f + sc.x) * ((v[i].x - mean) * rstd) + sh.x);
+    o[1] = f2bf((1.0f + sc.y) * ((v[i].y - mean) * rstd) + sh.y);
+    o[2] = f2bf((1.0f + sc.z) * ((v[i].z - mean) * rstd) + sh.z);
+    o[3] = f2bf((1.0f + sc.w) * ((v[i].w - mean) * rstd) + sh.w);
+    hr[c] = o;
+  }
+}
+
+// Generic width (any multiple of 256): loops instead of a register array.
+__global__ __launch_bounds__(256) void k_ln_modulate_any(
+    const float* __restrict__ x, const float* __restrict__ mod, SegTable segs,
+    bf16* __restrict__ h, int M, int D, float eps) {
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= M) return;
+  const float* xr = x + (size_t)row * D;
+  float s = 0.f;
+  for (int c = lane; c < D; c += 64) s += xr[c];
+  for (int o = 32; o >= 1; o >>= 1) s += xor_lane(s, o);
+  const float mean = s / (float)D;
+  float q = 0.f;
+  for (int c = lane; c < D; c += 64) {
+    const float a = xr[c] - mean;
+    q += a * a;
+  }
+  for (int o = 32; o >= 1; o >>= 1) q += xor_lane(q, o);
+  const float rstd = 1.0f / sqrtf(q / (float)D + eps);
+  const int sg = seg_of(segs, row);
+  const float* shift = mod + (size_t)sg * 3 * D;
+  const float* scale = shift + D;
+  for (int c = lane; c < D; c += 64)
+    h[(size_t)row * D + c] =
+        f2bf((1.0f + scale[c]) * ((xr[c] - mean) * rstd) + shift[c]);
+}
+
+hipError_t launch_ln_modulate(const BlockShape& bs, const float* x,
+                              const float* mod, const SegTableHost& segs,
+                              void* h, float eps, hipStream_t s) {
+  SegTable st;
+  for (int i = 0; i < kMaxSegs; ++i) st.start[i] = segs.start[i];
+  st.n = segs.n;
+  const unsigned blocks = (unsigned)((bs.M + 3) / 4);
+  if (blocks == 0) return hipSuccess;
+  if (bs.D == 3072) {
+    hipLaunchKernelGGL(k_ln_modulate<3072>, dim3(blocks), dim3(256), 0, s, x,
+                       mod, st, reinterpret_cast<bf16*>(h), bs.M, eps);
+  } else {
+    hipLaunchKernelGGL(k_ln_modulate_any, dim3(blocks), dim3(256), 0, s, x,
+                       mod, st, reinterpret_cast<bf16*>(h), bs.M, bs.D, eps);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace flux3

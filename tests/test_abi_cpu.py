@@ -1,0 +1,189 @@
+"""Host-side checks of the C ABI that need no GPU: the library loads, exports
+every function include/flux3.h declares, sizes its workspace as documented,
+and rejects bad arguments with the documented status before any HIP call.
+
+Only failing calls are made here (validation runs before anything is
+enqueued); no valid compute call is issued without a GPU.
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import latent_flow_matching_flux_amd as F
+from latent_flow_matching_flux_amd import _lib as L
+import synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "flux3.h")
+
+OK, E_INVALID, E_SHAPE, E_UNSUPPORTED, E_ALIGN, E_WORKSPACE = 0, -1, -2, -3, -4, -5
+FAKE = 0x7F0000000000          # a 256-byte aligned address that is never dereferenced
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(flux3_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    lib = F.load()
+    declared = header_functions()
+    assert declared == sorted(L.EXPORTS)
+    for name in declared:
+        assert hasattr(lib, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", F.LIB_PATH], capture_output=True,
+                         text=True).stdout
+    exported = set(re.findall(r" T (flux3_\w+)", out))
+    assert set(declared) <= exported
+
+
+def _dims(width=3072, heads=24, head_dim=128, hidden=9216):
+    return L.Dims(width, heads, head_dim, hidden)
+
+
+def _w(addr=FAKE):
+    return L.BlockWeights(*[addr + 4096 * i for i in range(9)])
+
+
+def _call_block(dims=None, w=None, x=FAKE, n=336, segs=((0, 80, 0), (80, 256, 1)),
+                mod=FAKE, rope=FAKE, ws=FAKE, ws_bytes=None):
+    lib = F.load()
+    d = dims if dims is not None else _dims()
+    seg_arr, n_segs = L.make_segments(list(segs))
+    if ws_bytes is None:
+        ws_bytes = lib.flux3_workspace_bytes(ctypes.byref(d), n) if d.head_dim == 128 else 1 << 30
+    wp = ctypes.byref(w if w is not None else _w())
+    return lib.flux3_block_forward(ctypes.byref(d), wp, x, n, seg_arr, n_segs, mod, rope, ws,
+                                   ws_bytes, 0)
+
+
+def test_workspace_bytes_formula():
+    d = synth.DIMS
+    per_tok = (d.width + 3 * d.width + d.width + d.mlp_hidden) * 2   # h, q, k, vt, cat in bf16
+    for n in (1, 7, 256, 336, 8432, 65776):
+        n_pad = (n + 255) // 256 * 256
+        assert F.workspace_bytes(d, n) == n_pad * per_tok
+    assert F.workspace_bytes(synth.Dims(3072, 24, 64, 9216), 10) == 0
+    lay = F.workspace_layout(d, 8432)
+    assert lay.n_pad == 8448 and lay.total == F.workspace_bytes(d, 8432)
+    assert lay.h == 0 and lay.q < lay.k < lay.vt < lay.cat < lay.total
+    assert all(off % 256 == 0 for off in (lay.q, lay.k, lay.vt, lay.cat))
+
+
+def test_layout_tokens():
+    for wl in synth.WORKLOADS.values():
+        assert F.layout_tokens(wl.layout) == wl.n_tokens
+    assert F.layout_tokens(synth.RopeLayout(-1, 2, 2)) == -1
+    assert F.layout_tokens(synth.RopeLayout(0, 2, 0)) == -1
+    assert F.layout_tokens(synth.RopeLayout(0, 1, 1, tuple((1, 1) for _ in range(16)))) == -1
+
+
+@pytest.mark.parametrize("dims,status", [
+    (_dims(head_dim=64), E_UNSUPPORTED),
+    (_dims(width=3072, heads=23), E_UNSUPPORTED),
+    (_dims(width=3000), E_UNSUPPORTED),
+    (_dims(hidden=9200), E_UNSUPPORTED),
+    (_dims(hidden=0), E_UNSUPPORTED),
+])
+def test_block_rejects_unsupported_dims(dims, status):
+    assert _call_block(dims=dims) == status
+
+
+def test_block_rejects_null_and_misaligned():
+    assert F.load().flux3_block_forward(None, ctypes.byref(_w()), FAKE, 336, None, 0, FAKE, FAKE,
+                                        FAKE, 1 << 40, 0) == E_INVALID
+    assert _call_block(x=None) == E_INVALID
+    assert _call_block(mod=None) == E_INVALID
+    assert _call_block(rope=None) == E_INVALID
+    w = _w()
+    w.w_down = None
+    assert _call_block(w=w) == E_INVALID
+    assert b"w_down" in F.load().flux3_last_error_detail()
+    assert _call_block(x=FAKE + 4) == E_ALIGN
+    w = _w()
+    w.wk = FAKE + 2
+    assert _call_block(w=w) == E_ALIGN
+    assert _call_block(ws=FAKE + 16) == E_ALIGN
+
+
+def test_block_rejects_bad_segments():
+    assert _call_block(segs=()) == E_SHAPE                                  # no segments
+    assert _call_block(segs=((0, 80, 0), (80, 255, 1))) == E_SHAPE         # short
+    assert _call_block(segs=((0, 80, 0), (81, 255, 1))) == E_SHAPE         # gap
+    assert _call_block(segs=((0, 80, 1), (80, 256, 0))) == E_SHAPE         # order
+    assert _call_block(segs=((0, 80, 0), (80, 256, 3))) == E_INVALID       # mode
+    assert _call_block(segs=((0, 0, 0), (0, 336, 1))) == E_SHAPE          # empty
+    assert _call_block(segs=tuple((i, 1, 0) for i in range(17)), n=17) == E_SHAPE
+
+
+def test_block_sizes_and_workspace():
+    assert _call_block(n=-1) == E_SHAPE
+    assert _call_block(n=(1 << 20) + 1, segs=((0, (1 << 20) + 1, 0),)) == E_SHAPE
+    assert _call_block(ws=None) == E_WORKSPACE
+    need = F.workspace_bytes(synth.DIMS, 336)
+    assert _call_block(ws_bytes=need - 1) == E_WORKSPACE
+    # empty call is a no-op
+    assert _call_block(n=0, segs=()) == OK
+    assert _call_block(n=0, segs=((0, 1, 0),)) == E_SHAPE
+
+
+def test_rope_build_validation():
+    lib = F.load()
+    lay = L.make_layout(synth.workload("block336").layout)
+    assert lib.flux3_rope_tables_build(None, FAKE, 336, 0) == E_INVALID
+    assert lib.flux3_rope_tables_build(ctypes.byref(lay), FAKE, 335, 0) == E_SHAPE
+    assert lib.flux3_rope_tables_build(ctypes.byref(lay), None, 336, 0) == E_INVALID
+    assert lib.flux3_rope_tables_build(ctypes.byref(lay), FAKE + 8, 336, 0) == E_ALIGN
+    many = L.make_layout(synth.RopeLayout(0, 1, 1, tuple((1, 1) for _ in range(16))))
+    assert lib.flux3_rope_tables_build(ctypes.byref(many), FAKE, 17, 0) == E_SHAPE
+    empty = L.make_layout(synth.RopeLayout(0, 0, 0))
+    assert lib.flux3_rope_tables_build(ctypes.byref(empty), None, 0, 0) == OK
+
+
+def _call_stack(n_pm=5, n_joint=28, per_mode=True, joint=True, m1=FAKE, m2=FAKE, stride=0,
+                segs=((0, 80, 0), (80, 256, 1)), ws_bytes=None):
+    lib = F.load()
+    d = _dims()
+    pm = (L.BlockWeights * (3 * max(n_pm, 1)))(*[_w() for _ in range(3 * max(n_pm, 1))])
+    jt = (L.BlockWeights * max(n_joint, 1))(*[_w() for _ in range(max(n_joint, 1))])
+    seg_arr, n_segs = L.make_segments(list(segs))
+    n = sum(s[1] for s in segs)
+    if ws_bytes is None:
+        ws_bytes = lib.flux3_workspace_bytes(ctypes.byref(d), n)
+    return lib.flux3_stack_forward(ctypes.byref(d), pm if per_mode else None, n_pm,
+                                   jt if joint else None, n_joint, FAKE, n, seg_arr, n_segs,
+                                   m1, m2, stride, FAKE, FAKE, ws_bytes, 0)
+
+
+def test_stack_validation():
+    assert _call_stack(per_mode=False) == E_INVALID
+    assert _call_stack(joint=False) == E_INVALID
+    assert _call_stack(m1=None) == E_INVALID
+    assert _call_stack(m2=None) == E_INVALID
+    assert _call_stack(m2=FAKE + 4) == E_ALIGN
+    assert _call_stack(stride=-4) == E_SHAPE
+    assert _call_stack(stride=6) == E_ALIGN
+    assert _call_stack(n_pm=-1) == E_SHAPE
+    assert _call_stack(ws_bytes=100) == E_WORKSPACE
+    assert _call_stack(segs=((0, 80, 2), (80, 256, 1))) == E_SHAPE
+
+
+def test_status_strings():
+    for s in (0, -1, -2, -3, -4, -5, -6):
+        assert F.status_string(s) and F.status_string(s) != "unknown status"
+    assert F.status_string(-99) == "unknown status"
+
+
+def test_binding_has_no_cpu_fallback(tmp_path):
+    """Loading from a path without the library raises instead of falling back."""
+    saved = L._lib
+    L._lib = None
+    try:
+        with pytest.raises(ImportError):
+            L.load(str(tmp_path / "missing.so"))
+    finally:
+        L._lib = saved
