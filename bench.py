@@ -1,0 +1,234 @@
+#!/usr/bin/env python3
+"""Throughput of the FLUX.3 Image Klein block stack on one MI355X.
+
+One step is the whole hot path over one batch: the rotary tables for the
+token layout, then the two-stage stack -- 5 per-mode blocks on each stream
+(text, noisy image, reference; each stream attends only to itself) and 28
+joint blocks over the concatenated sequence -- on the single-reference edit
+workload [240 text | 64x64 image | 64x64 reference] = 8432 tokens at width
+3072, 24 heads x 128, SwiGLU hidden 9216, bf16 operands with fp32
+accumulation and an fp32 residual stream.  Weights (43 distinct blocks) are
+seeded random N(0, 0.02^2) in bf16, tokens N(0, 1), modulation vectors
+N(0, 0.07^2); everything is resident in HBM before timing starts.
+
+value = block-token passes per second = (5 + 28) * 8432 / step time, the
+rate at which tokens go through transformer blocks.  Per-kernel durations
+come from HIP events the library records around each of its launches on the
+launch stream, inside the timed region.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6      # 256 CU x 2.4 GHz x 4096 dense bf16 FLOP/clk/CU
+PEAK_HBM_GBS = 8000.0
+N_PM, N_JOINT = 5, 28
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_proj_edit8432_traffic.json")
+KERNEL_SOURCES = ("gemm.hip", "common.hpp")
+
+
+def gemm_flops_per_token(d):
+    proj = 2 * d.width * (3 * d.width + 2 * d.mlp_hidden)
+    out = 2 * (d.width + d.mlp_hidden) * d.width
+    return proj, out
+
+
+def source_hash():
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "latent_flow_matching_flux_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(launch_tokens):
+    """HBM bytes per gemm_proj launch from the committed rocprofv3 counter
+    summary, or None if absent or taken on a different kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("source_hash") != source_hash() or t.get("tokens") != launch_tokens:
+        return None
+    return t.get("bytes_per_launch")
+
+
+def cpu_baseline(workload_name):
+    """The oracle, as it stands (NumPy float64), on one joint block of the
+    same workload; value in block tokens/s."""
+    import numpy as np
+    import synth
+    from oracle import flux3_oracle as O
+    wl = synth.workload(workload_name)
+    lay = wl.layout
+    n = lay.n_tokens
+    segs = [(s.start, s.count, s.mode) for s in lay.segments()]
+    w = synth.block_weights(0, 0, synth.DIMS)
+    x = synth.tokens(0, n, synth.DIMS.width)
+    mod = synth.modulation(0, 0, len(segs), synth.DIMS.width)
+    rope = O.rope_tables(O.token_positions(lay.n_text, lay.grid_h, lay.grid_w, lay.refs))
+    t0 = time.perf_counter()
+    y = O.block_forward(x, w, segs, mod, rope)
+    dt = time.perf_counter() - t0
+    assert np.isfinite(y).all()
+    cores = len(os.sched_getaffinity(0))
+    return {"value": n / dt, "unit": "block tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"one joint block over the {n}-token {workload_name} sequence, "
+                      f"NumPy float64, {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default="edit8432")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path; run with --gpus 1",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import latent_flow_matching_flux_amd as F
+    import synth
+
+    F.load()
+    dev = torch.device("cuda:0")
+    dims = synth.DIMS
+    wl = synth.workload(args.workload)
+    lay = wl.layout
+    segs = lay.segments()
+    n = lay.n_tokens
+    D, Fh = dims.width, dims.mlp_hidden
+
+    g = torch.Generator(device=dev)
+    g.manual_seed(0)
+
+    def rand(*shape, std=1.0, dtype=torch.bfloat16):
+        return (torch.randn(*shape, generator=g, device=dev, dtype=torch.float32) * std).to(dtype)
+
+    def rand_block():
+        return {"wq": rand(D, D, std=0.02), "wk": rand(D, D, std=0.02), "wv": rand(D, D, std=0.02),
+                "wo": rand(D, D, std=0.02), "w_gate": rand(Fh, D, std=0.02),
+                "w_up": rand(Fh, D, std=0.02), "w_down": rand(D, Fh, std=0.02),
+                "q_norm": torch.ones(128, device=dev), "k_norm": torch.ones(128, device=dev)}
+
+    modes = sorted({s.mode for s in segs})
+    per_mode = {m: [rand_block() for _ in range(N_PM)] for m in modes}
+    joint = [rand_block() for _ in range(N_JOINT)]
+    x0 = rand(n, D, dtype=torch.float32)
+    x = torch.empty_like(x0)
+    m1 = rand(len(segs), 3, D, std=0.07, dtype=torch.float32)
+    m2 = rand(len(segs), 3, D, std=0.07, dtype=torch.float32)
+    rope = torch.empty((n, 64, 2), dtype=torch.float32, device=dev)
+    ws = torch.empty(F.workspace_bytes(dims, n), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        F.rope_tables_build(lay, rope, stream=stream)
+        x.copy_(x0)
+        F.stack_forward(dims, per_mode, joint, x, segs, m1, m2, rope, ws, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    assert torch.isfinite(x).all(), "non-finite stack output"
+
+    F.profile_reset()
+    F.profile_enable(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    F.profile_enable(False)
+    stats = {k: F.profile_read(k) for k in F.KERNELS}
+    F.profile_reset()
+
+    ms_per_step = (t1 - t0) / args.steps * 1e3
+    passes = (N_PM + N_JOINT) * n
+    value = passes / (ms_per_step / 1e3)
+    proj_fpt, out_fpt = gemm_flops_per_token(dims)
+
+    def tflops(flops, ms):
+        return flops / (ms * 1e-3) / 1e12 if ms > 0 else 0.0
+
+    kern = {}
+    for k, st in stats.items():
+        ms = st["total_ms"]
+        entry = {"launches": st["launches"], "ms_per_step": ms / args.steps,
+                 "avg_us": 1e3 * ms / max(st["launches"], 1)}
+        if k == "gemm_proj":
+            entry["tflops"] = tflops(proj_fpt * st["tokens"], ms)
+        elif k == "gemm_out":
+            entry["tflops"] = tflops(out_fpt * st["tokens"], ms)
+        elif k == "attention":
+            entry["tflops"] = tflops(4.0 * D * st["tokens_sq"], ms)
+        elif k == "ln_modulate":
+            entry["gbs"] = 6.0 * D * st["tokens"] / (ms * 1e-3) / 1e9 if ms > 0 else 0.0
+        elif k == "rope_tables":
+            entry["gbs"] = 512.0 * st["tokens"] / (ms * 1e-3) / 1e9 if ms > 0 else 0.0
+        if "tflops" in entry:
+            entry["frac_peak"] = entry["tflops"] / PEAK_BF16_TFLOPS
+        kern[k] = entry
+
+    step_flops = 0.0
+    step_flops += proj_fpt * stats["gemm_proj"]["tokens"] + out_fpt * stats["gemm_out"]["tokens"]
+    step_flops += 4.0 * D * stats["attention"]["tokens_sq"]
+    step_flops /= args.steps
+
+    # dominant kernel: the projection GEMM (the largest FLOP share)
+    gp = stats["gemm_proj"]
+    avg_ms = gp["total_ms"] / max(gp["launches"], 1)
+    flops_per_launch = proj_fpt * gp["tokens"] / max(gp["launches"], 1)
+    achieved = flops_per_launch / (avg_ms * 1e-3) / 1e12
+    roofline = {"bound": "mfma", "kernel": "gemm_proj", "achieved": achieved,
+                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
+                "traffic": measured_traffic(n),
+                "work_per_launch": f"{proj_fpt / 1e6:.2f} MFLOP/token x {gp['tokens'] / max(gp['launches'], 1):.0f} tokens (mean over stage-1 and stage-2 launches)"}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(args.workload)
+
+    out = {
+        "metric": "block tokens/s + attn/GEMM TFLOP/s (% bf16 MFMA peak) at 8432 tokens",
+        "value": value,
+        "unit": "block tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{args.workload}: {wl.description}; rope tables + "
+                               f"{N_PM} per-mode blocks per stream + {N_JOINT} joint blocks",
+                   "tokens": n, "width": D, "heads": dims.heads, "head_dim": dims.head_dim,
+                   "mlp_hidden": Fh, "segments": [[s.start, s.count, s.mode] for s in segs]},
+        "step_tflops": step_flops / (ms_per_step * 1e-3) / 1e12,
+        "step_frac_peak": step_flops / (ms_per_step * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+        "stack_tokens_per_s": n / (ms_per_step / 1e3),
+        "kernels": kern,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

@@ -189,6 +189,35 @@ flux3_status flux3_stack_forward(const flux3_dims *dims,
                                  void *workspace, size_t workspace_bytes,
                                  void *stream);
 
+/* Kernel timing, for benchmarks and profiling.  While enabled, every kernel
+ * launch is bracketed by a pair of HIP events recorded on the launch stream,
+ * so the durations are those of the kernels themselves on the stream they
+ * run on.  flux3_profile_read waits for the recorded events and returns, for
+ * one kernel kind, the number of launches, their summed duration in
+ * milliseconds, and the summed token count M and M^2 of those launches (the
+ * units the kernels' algorithmic work is counted in).  flux3_profile_reset
+ * drops all records.  Recording allocates HIP events on the host side; the
+ * facility is not thread-safe and is off by default. */
+enum {
+  FLUX3_K_ROPE_TABLES = 0,
+  FLUX3_K_LN_MODULATE = 1,
+  FLUX3_K_GEMM_PROJ = 2,
+  FLUX3_K_ATTENTION = 3,
+  FLUX3_K_GEMM_OUT = 4,
+  FLUX3_K_COUNT = 5
+};
+typedef struct {
+  int64_t launches;
+  double total_ms;
+  double tokens;     /* sum of M over launches   */
+  double tokens_sq;  /* sum of M*M over launches */
+} flux3_kernel_stats;
+void flux3_profile_enable(int32_t on);
+void flux3_profile_reset(void);
+/* FLUX3_E_INVALID for a bad kind or NULL out; FLUX3_E_HIP if an event
+ * cannot be read. */
+flux3_status flux3_profile_read(int32_t kernel, flux3_kernel_stats *out);
+
 /* Debug switch: when non-zero every launch is followed by a stream
  * synchronisation and an error check, so a faulting kernel is named in
  * flux3_last_error_detail().  Off by default. */

@@ -21,7 +21,9 @@ MAX_REFS = 15
 # exported symbols, in the order include/flux3.h declares them
 EXPORTS = ("flux3_layout_tokens", "flux3_rope_tables_build", "flux3_workspace_bytes",
            "flux3_workspace_layout_get", "flux3_block_forward", "flux3_stack_forward",
+           "flux3_profile_enable", "flux3_profile_reset", "flux3_profile_read",
            "flux3_set_debug_sync", "flux3_status_string", "flux3_last_error_detail")
+KERNELS = ("rope_tables", "ln_modulate", "gemm_proj", "attention", "gemm_out")
 
 
 class Flux3Error(RuntimeError):
@@ -51,6 +53,11 @@ class RopeLayout(ctypes.Structure):
                 ("ref_h", ctypes.POINTER(ctypes.c_int32)),
                 ("ref_w", ctypes.POINTER(ctypes.c_int32)),
                 ("theta", ctypes.c_double), ("hw_scale", ctypes.c_double)]
+
+
+class KernelStats(ctypes.Structure):
+    _fields_ = [("launches", ctypes.c_int64), ("total_ms", ctypes.c_double),
+                ("tokens", ctypes.c_double), ("tokens_sq", ctypes.c_double)]
 
 
 class WorkspaceLayout(ctypes.Structure):
@@ -86,6 +93,12 @@ def load(path=LIB_PATH):
     lib.flux3_stack_forward.argtypes = [P(Dims), P(BlockWeights), i32, P(BlockWeights), i32,
                                         vp, i64, P(Segment), i32, vp, vp, i64, vp, vp, sz, vp]
     lib.flux3_stack_forward.restype = i32
+    lib.flux3_profile_enable.argtypes = [i32]
+    lib.flux3_profile_enable.restype = None
+    lib.flux3_profile_reset.argtypes = []
+    lib.flux3_profile_reset.restype = None
+    lib.flux3_profile_read.argtypes = [i32, P(KernelStats)]
+    lib.flux3_profile_read.restype = i32
     lib.flux3_set_debug_sync.argtypes = [i32]
     lib.flux3_set_debug_sync.restype = None
     lib.flux3_status_string.argtypes = [i32]
@@ -224,6 +237,24 @@ def stack_forward(dims, per_mode, joint, x, segs, mod_stage1, mod_stage2, rope, 
                                       _ptr(mod_stage1), _ptr(mod_stage2), mod_block_stride,
                                       _ptr(rope), _ptr(workspace), workspace_nbytes,
                                       _stream_handle(stream)))
+
+
+def profile_enable(on):
+    load().flux3_profile_enable(1 if on else 0)
+
+
+def profile_reset():
+    load().flux3_profile_reset()
+
+
+def profile_read(kernel):
+    """Stats for one kernel kind (name from KERNELS or its index): dict with
+    launches, total_ms, tokens (sum of M), tokens_sq (sum of M^2)."""
+    idx = KERNELS.index(kernel) if isinstance(kernel, str) else int(kernel)
+    out = KernelStats()
+    _check(load().flux3_profile_read(idx, ctypes.byref(out)))
+    return {"launches": out.launches, "total_ms": out.total_ms, "tokens": out.tokens,
+            "tokens_sq": out.tokens_sq}
 
 
 def set_debug_sync(on):

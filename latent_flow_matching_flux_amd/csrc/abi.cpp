@@ -7,6 +7,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <vector>
+
 #include "../../include/flux3.h"
 #include "kernels.hpp"
 
@@ -14,6 +16,41 @@ namespace {
 
 thread_local char g_detail[512] = "";
 int g_debug_sync = 0;
+
+// kernel timing records (flux3_profile_*)
+struct ProfRec {
+  int kind;
+  hipEvent_t a, b;
+  double m;
+};
+bool g_prof_on = false;
+std::vector<ProfRec> g_prof;
+std::vector<hipEvent_t> g_event_pool;
+
+hipEvent_t pool_event() {
+  if (!g_event_pool.empty()) {
+    hipEvent_t e = g_event_pool.back();
+    g_event_pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+// Records the start event of a launch when profiling; returns its index.
+int prof_begin(int kind, double m, hipStream_t s) {
+  if (!g_prof_on) return -1;
+  ProfRec r{kind, pool_event(), pool_event(), m};
+  if (!r.a || !r.b) return -1;
+  if (hipEventRecord(r.a, s) != hipSuccess) return -1;
+  g_prof.push_back(r);
+  return (int)g_prof.size() - 1;
+}
+
+void prof_end(int idx, hipStream_t s) {
+  if (idx >= 0) (void)hipEventRecord(g_prof[idx].b, s);
+}
 
 flux3_status fail(flux3_status s, const char* fmt, ...) {
   va_list ap;
@@ -162,17 +199,23 @@ flux3_status run_block(const flux3_dims* d, const flux3_block_weights& w, float*
   bs.F = d->mlp_hidden;
   const flux3::BlockWeightsDev wd = dev_weights(w);
   flux3_status r;
-  if ((r = after_launch(flux3::launch_ln_modulate(bs, x, mod, st, wp.h, kEpsLN, s),
-                        "ln_modulate", s)) != FLUX3_OK)
-    return r;
-  if ((r = after_launch(flux3::launch_gemm_proj(bs, wd, rope, wp, kEpsRMS, s), "gemm_proj",
-                        s)) != FLUX3_OK)
-    return r;
-  if ((r = after_launch(flux3::launch_attention(bs, wp, s), "attention", s)) != FLUX3_OK)
-    return r;
-  if ((r = after_launch(flux3::launch_gemm_out(bs, wd, wp, x, mod, st, s), "gemm_out", s)) !=
-      FLUX3_OK)
-    return r;
+  const double m = (double)n;
+  int pi = prof_begin(FLUX3_K_LN_MODULATE, m, s);
+  hipError_t e = flux3::launch_ln_modulate(bs, x, mod, st, wp.h, kEpsLN, s);
+  prof_end(pi, s);
+  if ((r = after_launch(e, "ln_modulate", s)) != FLUX3_OK) return r;
+  pi = prof_begin(FLUX3_K_GEMM_PROJ, m, s);
+  e = flux3::launch_gemm_proj(bs, wd, rope, wp, kEpsRMS, s);
+  prof_end(pi, s);
+  if ((r = after_launch(e, "gemm_proj", s)) != FLUX3_OK) return r;
+  pi = prof_begin(FLUX3_K_ATTENTION, m, s);
+  e = flux3::launch_attention(bs, wp, s);
+  prof_end(pi, s);
+  if ((r = after_launch(e, "attention", s)) != FLUX3_OK) return r;
+  pi = prof_begin(FLUX3_K_GEMM_OUT, m, s);
+  e = flux3::launch_gemm_out(bs, wd, wp, x, mod, st, s);
+  prof_end(pi, s);
+  if ((r = after_launch(e, "gemm_out", s)) != FLUX3_OK) return r;
   return FLUX3_OK;
 }
 
@@ -220,7 +263,10 @@ flux3_status flux3_rope_tables_build(const flux3_rope_layout* layout, float* rop
   dl.theta = layout->theta;
   dl.hw_scale = layout->hw_scale;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  flux3_status r = after_launch(flux3::launch_rope_tables(dl, rope, n, s), "rope_tables", s);
+  const int pi = prof_begin(FLUX3_K_ROPE_TABLES, (double)n, s);
+  const hipError_t e = flux3::launch_rope_tables(dl, rope, n, s);
+  prof_end(pi, s);
+  flux3_status r = after_launch(e, "rope_tables", s);
   return r == FLUX3_OK ? ok() : r;
 }
 
@@ -333,6 +379,36 @@ flux3_status flux3_stack_forward(const flux3_dims* dims, const flux3_block_weigh
 }
 
 void flux3_set_debug_sync(int32_t on) { g_debug_sync = on; }
+
+void flux3_profile_enable(int32_t on) { g_prof_on = on != 0; }
+
+void flux3_profile_reset(void) {
+  for (const ProfRec& r : g_prof) {
+    (void)hipEventSynchronize(r.b);
+    g_event_pool.push_back(r.a);
+    g_event_pool.push_back(r.b);
+  }
+  g_prof.clear();
+}
+
+flux3_status flux3_profile_read(int32_t kernel, flux3_kernel_stats* out) {
+  if (!out) return fail(FLUX3_E_INVALID, "out is NULL");
+  if (kernel < 0 || kernel >= FLUX3_K_COUNT) return fail(FLUX3_E_INVALID, "kernel kind %d", kernel);
+  flux3_kernel_stats st = {0, 0.0, 0.0, 0.0};
+  for (const ProfRec& r : g_prof) {
+    if (r.kind != kernel) continue;
+    hipError_t e = hipEventSynchronize(r.b);
+    float ms = 0.f;
+    if (e == hipSuccess) e = hipEventElapsedTime(&ms, r.a, r.b);
+    if (e != hipSuccess) return fail(FLUX3_E_HIP, "event read: %s", hipGetErrorString(e));
+    st.launches += 1;
+    st.total_ms += ms;
+    st.tokens += r.m;
+    st.tokens_sq += r.m * r.m;
+  }
+  *out = st;
+  return ok();
+}
 
 const char* flux3_status_string(flux3_status s) {
   switch (s) {

@@ -49,11 +49,42 @@ def metrics(got, want):
 
 
 def assert_close(got, want, what, maxabs_tol=MAXABS_TOL, cos_tol=COS_TOL):
+    """One block's fp32 output against the oracle: max-abs and cosine."""
     maxabs, cos = metrics(got, want)
+    print(f"[parity] {what}: max-abs {maxabs:.3e} (tol {maxabs_tol:.3e}) cosine {cos:.8f}")
     assert np.all(np.isfinite(got)), f"{what}: non-finite output"
     assert maxabs <= maxabs_tol and cos >= cos_tol, \
         f"{what}: max-abs {maxabs:.3e} (tol {maxabs_tol}), cosine {cos:.7f} (tol {cos_tol})"
     return maxabs, cos
+
+
+# A bf16-stored intermediate carries its own rounding (half an ulp, 2^-9
+# relative) on top of the operand rounding upstream of it; elementwise bound
+# |got - want| <= 3e-2 + 2^-7 |want| (two bf16 ulps relative).
+BF16_REL = 2.0 ** -7
+
+
+def assert_close_bf16(got, want, what, cos_tol=COS_TOL):
+    got = np.asarray(got, np.float64)
+    want = np.asarray(want, np.float64)
+    err = np.abs(got - want)
+    bound = MAXABS_TOL + BF16_REL * np.abs(want)
+    worst = float(np.max(err / bound)) if err.size else 0.0
+    _, cos = metrics(got, want)
+    print(f"[parity] {what}: max-abs {err.max():.3e}, worst err/bound {worst:.3f}, cosine {cos:.8f}")
+    assert np.all(np.isfinite(got)), f"{what}: non-finite output"
+    assert worst <= 1.0 and cos >= cos_tol, f"{what}: err/bound {worst:.3f}, cosine {cos:.7f}"
+
+
+def assert_close_stack(got, want, x_in, what):
+    """Stack output: bf16 rounding is relative, so over many blocks the
+    absolute bound scales with the residual stream: max-abs <= 3e-2 * max(1,
+    rms(want)); cosine >= 0.9995 on x_out and on x_out - x_in."""
+    rms = float(np.sqrt(np.mean(np.asarray(want, np.float64) ** 2)))
+    tol = MAXABS_TOL * max(1.0, rms)
+    assert_close(got, want, what + " x_out", maxabs_tol=tol)
+    dw = np.asarray(want, np.float64) - x_in
+    assert_close(np.asarray(got, np.float64) - x_in, dw, what + " delta", maxabs_tol=tol)
 
 
 def seg_tuples(segs):
