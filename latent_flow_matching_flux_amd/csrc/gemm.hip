@@ -15,11 +15,13 @@
 // Both operands are K-contiguous ("NT"): C[m][n] = sum_k A[m][k] * B[n][k],
 // with B in torch Linear layout [out][in].  Tile 256 x 256 x 64, 4 waves in
 // a 2 x 2 arrangement, each wave 128 x 128 = 4 x 4 blocks of the 32x32x16
-// bf16 MFMA, fp32 accumulators.  A and B k-slices go global -> registers ->
-// LDS (rows padded to 144 B so 16-byte fragment reads hit distinct banks),
-// double-buffered with one barrier per k-step.  Workgroups are remapped so
-// that the workgroups resident on one XCD (every 8th id) cover a compact
-// group of C tiles and share A and B slices in that XCD's L2.
+// bf16 MFMA, fp32 accumulators.  A and B k-slices stream from global memory
+// straight into LDS (gfx950 global_load_lds_dwordx4, no staging registers),
+// XOR-swizzled instead of padded, double-buffered with one barrier per
+// k-step; fragment reads and the next slice's loads are interleaved with
+// the MFMAs.  Workgroups are remapped so that the workgroups resident on one
+// XCD (every 8th id) cover a compact group of C tiles and share A and B
+// slices in that XCD's L2.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -28,10 +30,16 @@ namespace flux3 {
 namespace {
 
 constexpr int BM = 256, BN = 256, BK = 64;
-constexpr int LDK = BK + 8;               // padded LDS row, elements
-constexpr int TILE_ELEMS = BM * LDK;      // one operand, one stage
+constexpr int ROW_BYTES = BK * 2;             // one tile row of a k-slice
+constexpr int OP_BYTES = BM * ROW_BYTES;      // one operand, one stage: 32 KiB
+constexpr int STAGE_BYTES = 2 * OP_BYTES;     // A then B
+constexpr int LDS_BYTES = 2 * STAGE_BYTES;    // double-buffered: 128 KiB
 constexpr int NTHREADS = 256;
 constexpr int GROUP_M = 8;
+
+typedef __attribute__((address_space(3))) unsigned char lds_u8;
+typedef __attribute__((address_space(3))) void lds_void;
+typedef const __attribute__((address_space(1))) void gvoid;
 
 struct Acc {
   f32x16 c[4][4];
@@ -53,62 +61,110 @@ __device__ __forceinline__ void tile_coords(int b, int n_m, int n_n, int& mt,
   nt = in / gm;
 }
 
-__device__ __forceinline__ void load_slices(u32x4 (&ra)[8], u32x4 (&rb)[8],
-                                            const bf16* ap, size_t a_run,
-                                            const bf16* const (&bp)[8], int ka,
-                                            int kb) {
-#pragma unroll
-  for (int i = 0; i < 8; ++i)
-    ra[i] = *reinterpret_cast<const u32x4*>(ap + i * a_run + ka);
-#pragma unroll
-  for (int i = 0; i < 8; ++i)
-    rb[i] = *reinterpret_cast<const u32x4*>(bp[i] + kb);
-}
+// Where this wave's share of one operand tile comes from: wave w loads tile
+// rows [64w, 64w + 64), i.e. the 32-row runs 2w (lo) and 2w + 1 (hi); each
+// run has a wave-uniform base pointer (its first row at k = 0) and all rows
+// share the stride ld.
+struct Src {
+  const bf16* lo;
+  const bf16* hi;
+  int ld;
+};
 
-__device__ __forceinline__ void store_slices(bf16* As, bf16* Bs,
-                                             const u32x4 (&ra)[8],
-                                             const u32x4 (&rb)[8], int t) {
-  const int row = t >> 3, ch = t & 7;
+// LDS layout of a k-slice: row r of the tile occupies 128 contiguous bytes
+// (no padding); its 16-byte chunk c sits in slot c ^ ((r / 2) % 8).  With
+// 64 banks this keeps the MFMA fragment reads (32 consecutive rows, one
+// chunk, per half-wave) conflict-free, and it lets each wave fill whole
+// 1-KiB blocks with direct global->LDS loads: lane l of a block writes slot
+// l % 8 of row l / 8 and therefore fetches chunk (l % 8) ^ swizzle(row).
+__device__ __forceinline__ void issue_operand(const Src& S, int k, lds_u8* dst,
+                                              int wave, int lane) {
+  const int rsub = lane >> 3, slot = lane & 7;
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
-    *reinterpret_cast<u32x4*>(As + (row + 32 * i) * LDK + ch * 8) = ra[i];
-#pragma unroll
-  for (int i = 0; i < 8; ++i)
-    *reinterpret_cast<u32x4*>(Bs + (row + 32 * i) * LDK + ch * 8) = rb[i];
-}
-
-__device__ __forceinline__ void mma_slice(const bf16* As, const bf16* Bs,
-                                          Acc& acc, int wm, int wn,
-                                          int lane) {
-  const int r = lane & 31, kh = (lane >> 5) * 8;
-#pragma unroll
-  for (int kk = 0; kk < BK / 16; ++kk) {
-    bf16x8 a[4], b[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      a[i] = *reinterpret_cast<const bf16x8*>(
-          As + (wm * 128 + i * 32 + r) * LDK + kk * 16 + kh);
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      b[j] = *reinterpret_cast<const bf16x8*>(
-          Bs + (wn * 128 + j * 32 + r) * LDK + kk * 16 + kh);
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) acc.c[i][j] = mfma32(a[i], b[j], acc.c[i][j]);
+  for (int i = 0; i < 8; ++i) {
+    const int c = slot ^ ((4 * (i & 1) + (lane >> 4)) & 7);   // (row/2)%8 of this row
+    const bf16* g = (i < 4 ? S.lo : S.hi) + (8 * (i & 3) + rsub) * S.ld + k + c * 8;
+    __builtin_amdgcn_global_load_lds((gvoid*)g, (lds_void*)(dst + (64 * wave + 8 * i) * ROW_BYTES),
+                                     16, 0, 0);
   }
 }
 
-// Main loop over k.  Phase 0 covers k tiles [0, nk0) with B pointers bp0,
-// phase 1 (if nk1 > 0) the next nk1 tiles with bp1; A runs straight through.
-__device__ __forceinline__ void gemm_mainloop(
-    bf16* smem, Acc& acc, const bf16* ap, size_t a_run,
-    const bf16* const (&bp0)[8], int nk0, const bf16* const (&bp1)[8],
-    int nk1, int t) {
-  const int wave = t >> 6, lane = t & 63;
+__device__ __forceinline__ void wait_loads() {
+  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+}
+
+struct Frags {
+  bf16x8 a[4], b[4];
+};
+
+__device__ __forceinline__ void read_frags(Frags& f, const lds_u8* As, const lds_u8* Bs,
+                                           int wm, int wn, int lane, int kk) {
+  const int r = lane & 31;
+  const int chunk = ((2 * kk + (lane >> 5)) ^ ((lane >> 1) & 7)) << 4;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    f.a[i] = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(
+        As + (wm * 128 + i * 32 + r) * ROW_BYTES + chunk);
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    f.b[j] = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(
+        Bs + (wn * 128 + j * 32 + r) * ROW_BYTES + chunk);
+}
+
+__device__ __forceinline__ void mma_frags(const Frags& f, Acc& acc) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc.c[i][j] = mfma32(f.a[i], f.b[j], acc.c[i][j]);
+}
+
+// Scheduling-group masks for __builtin_amdgcn_sched_group_barrier.
+constexpr int kSchedMFMA = 0x008;
+constexpr int kSchedVMEMRead = 0x020;
+constexpr int kSchedDSRead = 0x100;
+
+// One BK slice.  The 8 fragment reads of k-step kk+1 are interleaved one by
+// one with the MFMAs of k-step kk; with_loads also spreads the next slice's
+// 16 direct loads over the second half of k-steps 0 and 1.
+template <bool with_loads>
+__device__ __forceinline__ void mma_slice(const lds_u8* As, const lds_u8* Bs,
+                                          Acc& acc, int wm, int wn, int lane) {
+  Frags f0, f1;
+  read_frags(f0, As, Bs, wm, wn, lane, 0);
+#pragma unroll
+  for (int kk = 0; kk < BK / 16; ++kk) {
+    Frags& cur = (kk & 1) ? f1 : f0;
+    Frags& nxt = (kk & 1) ? f0 : f1;
+    if (kk + 1 < BK / 16) read_frags(nxt, As, Bs, wm, wn, lane, kk + 1);
+    mma_frags(cur, acc);
+    if (kk + 1 < BK / 16) {
+#pragma unroll
+      for (int g = 0; g < 8; ++g) {
+        __builtin_amdgcn_sched_group_barrier(kSchedMFMA, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 1, 0);
+      }
+      if (with_loads && kk < 2) {
+#pragma unroll
+        for (int g = 0; g < 8; ++g) {
+          __builtin_amdgcn_sched_group_barrier(kSchedMFMA, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(kSchedVMEMRead, 1, 0);
+        }
+      } else {
+        __builtin_amdgcn_sched_group_barrier(kSchedMFMA, 8, 0);
+      }
+    }
+  }
+}
+
+// Main loop over k.  Phase 0 covers k tiles [0, nk0) with B rows from B0,
+// phase 1 (if nk1 > 0) the next nk1 tiles from B1; A runs straight through.
+// Slice kt+1 streams into the other LDS buffer while slice kt is consumed.
+__device__ __forceinline__ void gemm_mainloop(lds_u8* smem, Acc& acc, const Src& A,
+                                              const Src& B0, int nk0, const Src& B1,
+                                              int nk1) {
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
   const int wm = wave >> 1, wn = wave & 1;
-  bf16* As[2] = {smem, smem + TILE_ELEMS};
-  bf16* Bs[2] = {smem + 2 * TILE_ELEMS, smem + 3 * TILE_ELEMS};
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -117,23 +173,24 @@ __device__ __forceinline__ void gemm_mainloop(
       for (int e = 0; e < 16; ++e) acc.c[i][j][e] = 0.f;
 
   const int nk = nk0 + nk1;
-  u32x4 ra[8], rb[8];
-  load_slices(ra, rb, ap, a_run, bp0, 0, 0);
-  store_slices(As[0], Bs[0], ra, rb, t);
+  issue_operand(A, 0, smem, wave, lane);
+  issue_operand(B0, 0, smem + OP_BYTES, wave, lane);
+  wait_loads();
   __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    const int nx = kt + 1;
-    if (nx < nk) {
-      if (nx < nk0)
-        load_slices(ra, rb, ap, a_run, bp0, nx * BK, nx * BK);
-      else
-        load_slices(ra, rb, ap, a_run, bp1, nx * BK, (nx - nk0) * BK);
-    }
-    mma_slice(As[cur], Bs[cur], acc, wm, wn, lane);
-    if (nx < nk) store_slices(As[cur ^ 1], Bs[cur ^ 1], ra, rb, t);
+  for (int kt = 0; kt + 1 < nk; ++kt) {
+    const int cur = (kt & 1) * STAGE_BYTES;
+    const int nxt = STAGE_BYTES - cur;
+    const int kn = kt + 1;
+    const bool ph0 = kn < nk0;
+    issue_operand(A, kn * BK, smem + nxt, wave, lane);
+    issue_operand(ph0 ? B0 : B1, ph0 ? kn * BK : (kn - nk0) * BK, smem + nxt + OP_BYTES, wave,
+                  lane);
+    mma_slice<true>(smem + cur, smem + cur + OP_BYTES, acc, wm, wn, lane);
+    wait_loads();
     __syncthreads();
   }
+  const int last = ((nk - 1) & 1) * STAGE_BYTES;
+  mma_slice<false>(smem + last, smem + last + OP_BYTES, acc, wm, wn, lane);
 }
 
 struct ProjArgs {
@@ -156,9 +213,10 @@ __device__ __forceinline__ int vt_pos(int m) {
 }
 
 __global__ __launch_bounds__(NTHREADS, 1) void k_gemm_proj(ProjArgs p) {
-  __shared__ bf16 smem[4 * TILE_ELEMS];
+  __shared__ __attribute__((aligned(1024))) unsigned char smem_raw[LDS_BYTES];
+  lds_u8* smem = (lds_u8*)smem_raw;
   const int t = threadIdx.x;
-  const int wave = t >> 6, lane = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6), lane = t & 63;
   const int wm = wave >> 1, wn = wave & 1;
   const int qkv_tiles = p.H / 2;
   const int n_n = 3 * qkv_tiles + p.F / 128;
@@ -176,25 +234,25 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_gemm_proj(ProjArgs p) {
     hid0 = (nt - 3 * qkv_tiles) * 128;
   }
   const int D = p.D;
-  const int row = t >> 3, ch = t & 7;
-  const bf16* bp[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const bf16* W;
-    int brow;
+  // first row of 32-row run i of the B tile
+  auto b_run = [&](int i) -> const bf16* {
     if (kind < 3) {
-      W = kind == 0 ? p.wq : (kind == 1 ? p.wk : p.wv);
-      brow = head0 * 128 + 32 * i + row;
-    } else {
-      const int half = i >> 2, blk = i & 3;
-      W = blk < 2 ? p.wg : p.wu;
-      brow = hid0 + 64 * half + 32 * (blk & 1) + row;
+      const bf16* W = kind == 0 ? p.wq : (kind == 1 ? p.wk : p.wv);
+      return W + (size_t)(head0 * 128 + 32 * i) * D;
     }
-    bp[i] = W + (size_t)brow * D + ch * 8;
-  }
-  const bf16* ap = p.h + (size_t)(m0 + row) * D + ch * 8;
+    const int half = i >> 2, blk = i & 3;
+    const bf16* W = blk < 2 ? p.wg : p.wu;
+    return W + (size_t)(hid0 + 64 * half + 32 * (blk & 1)) * D;
+  };
+  Src A, B;
+  A.lo = p.h + (size_t)(m0 + 64 * wave) * D;
+  A.hi = A.lo + (size_t)32 * D;
+  A.ld = D;
+  B.lo = b_run(2 * wave);
+  B.hi = b_run(2 * wave + 1);
+  B.ld = D;
   Acc acc;
-  gemm_mainloop(smem, acc, ap, (size_t)32 * D, bp, D / BK, bp, 0, t);
+  gemm_mainloop(smem, acc, A, B, D / BK, B, 0);
 
   const int r32 = lane & 31, hi = lane >> 5;
   if (kind < 2) {
@@ -280,9 +338,10 @@ struct OutArgs {
 };
 
 __global__ __launch_bounds__(NTHREADS, 1) void k_gemm_out(OutArgs p) {
-  __shared__ bf16 smem[4 * TILE_ELEMS];
+  __shared__ __attribute__((aligned(1024))) unsigned char smem_raw[LDS_BYTES];
+  lds_u8* smem = (lds_u8*)smem_raw;
   const int t = threadIdx.x;
-  const int wave = t >> 6, lane = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6), lane = t & 63;
   const int wm = wave >> 1, wn = wave & 1;
   const int D = p.D, F = p.F;
   const int n_n = D / BN;
@@ -290,17 +349,19 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_gemm_out(OutArgs p) {
   int mt, nt;
   tile_coords(blockIdx.x, n_m, n_n, mt, nt);
   const int m0 = mt * BM, n0 = nt * BN;
-  const int row = t >> 3, ch = t & 7;
-  const bf16 *bp0[8], *bp1[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    bp0[i] = p.wo + (size_t)(n0 + 32 * i + row) * D + ch * 8;
-    bp1[i] = p.wd + (size_t)(n0 + 32 * i + row) * F + ch * 8;
-  }
   const int ldc = D + F;
-  const bf16* ap = p.cat + (size_t)(m0 + row) * ldc + ch * 8;
+  Src A, B0, B1;
+  A.lo = p.cat + (size_t)(m0 + 64 * wave) * ldc;
+  A.hi = A.lo + (size_t)32 * ldc;
+  A.ld = ldc;
+  B0.lo = p.wo + (size_t)(n0 + 64 * wave) * D;
+  B0.hi = B0.lo + (size_t)32 * D;
+  B0.ld = D;
+  B1.lo = p.wd + (size_t)(n0 + 64 * wave) * F;
+  B1.hi = B1.lo + (size_t)32 * F;
+  B1.ld = F;
   Acc acc;
-  gemm_mainloop(smem, acc, ap, (size_t)32 * ldc, bp0, D / BK, bp1, F / BK, t);
+  gemm_mainloop(smem, acc, A, B0, D / BK, B1, F / BK);
 
   const int r32 = lane & 31, hi = lane >> 5;
 #pragma unroll
