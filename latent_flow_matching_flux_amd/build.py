@@ -21,32 +21,36 @@ COMMON = [
 SOURCES = ["rope.hip", "ln_modulate.hip", "gemm.hip", "attention.hip", "abi.cpp"]
 
 
-def _compile(src):
-    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
+def _compile(src, defines=(), build_dir=BUILD):
+    obj = os.path.join(build_dir, os.path.splitext(src)[0] + ".o")
     lang = ["-x", "hip"] if src.endswith(".hip") else []
-    cmd = [HIPCC, *COMMON, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *COMMON, *[f"-D{d}" for d in defines], *lang, "-c", os.path.join(CSRC, src),
+           "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
     return obj, r.stderr
 
 
-def build(verbose=False):
-    os.makedirs(BUILD, exist_ok=True)
+def build(verbose=False, defines=(), out=LIB, build_dir=BUILD):
+    """Compile every source and link libflux3.so.  `defines` (NAME=VALUE
+    strings) select compile-time kernel parameters; `out`/`build_dir` place
+    the result elsewhere than the package directory."""
+    os.makedirs(build_dir, exist_ok=True)
     with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
-        results = list(ex.map(_compile, SOURCES))
+        results = list(ex.map(lambda src: _compile(src, defines, build_dir), SOURCES))
     objs = [o for o, _ in results]
     if verbose:
         for _, err in results:
             if err.strip():
                 print(err, file=sys.stderr)
-    tmp = LIB + ".tmp"
+    tmp = out + ".tmp"
     cmd = [HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":

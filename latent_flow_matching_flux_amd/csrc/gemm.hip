@@ -17,11 +17,13 @@
 // a 2 x 2 arrangement, each wave 128 x 128 = 4 x 4 blocks of the 32x32x16
 // bf16 MFMA, fp32 accumulators.  A and B k-slices stream from global memory
 // straight into LDS (gfx950 global_load_lds_dwordx4, no staging registers),
-// XOR-swizzled instead of padded, double-buffered with one barrier per
-// k-step; fragment reads and the next slice's loads are interleaved with
-// the MFMAs.  Workgroups are remapped so that the workgroups resident on one
+// XOR-swizzled instead of padded, through a ring of LDS buffers that keeps
+// several slices in flight (one barrier per slice); fragment reads and the
+// loads are interleaved with the MFMAs.  Workgroups are remapped so that the workgroups resident on one
 // XCD (every 8th id) cover a compact group of C tiles and share A and B
 // slices in that XCD's L2.
+#include <utility>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -29,17 +31,44 @@ namespace flux3 {
 
 namespace {
 
-constexpr int BM = 256, BN = 256, BK = 64;
-constexpr int ROW_BYTES = BK * 2;             // one tile row of a k-slice
-constexpr int OP_BYTES = BM * ROW_BYTES;      // one operand, one stage: 32 KiB
-constexpr int STAGE_BYTES = 2 * OP_BYTES;     // A then B
-constexpr int LDS_BYTES = 2 * STAGE_BYTES;    // double-buffered: 128 KiB
+constexpr int BM = 256, BN = 256;
 constexpr int NTHREADS = 256;
 constexpr int GROUP_M = 8;
+
+#ifndef FLUX3_GEMM_BK
+#define FLUX3_GEMM_BK 64
+#endif
+#ifndef FLUX3_GEMM_STAGES
+#define FLUX3_GEMM_STAGES 2
+#endif
+constexpr int BK = FLUX3_GEMM_BK;        // k depth of one LDS slice
+constexpr int STAGES = FLUX3_GEMM_STAGES;  // LDS ring: STAGES - 1 slices in flight
 
 typedef __attribute__((address_space(3))) unsigned char lds_u8;
 typedef __attribute__((address_space(3))) void lds_void;
 typedef const __attribute__((address_space(1))) void gvoid;
+
+// Geometry of one k-slice in LDS.  Tile row r (256 rows per operand)
+// occupies ROW_BYTES contiguous bytes, no padding; its 16-byte chunk c sits
+// in slot c ^ ((r / SWZ_DIV) % CPR), where SWZ_DIV rows span one 256-byte
+// bank cycle.  With 64 banks this keeps the MFMA fragment reads (32
+// consecutive rows, one chunk, per half-wave) conflict-free, and lets each
+// wave fill whole 1-KiB blocks with direct global->LDS loads: lane l of a
+// block writes slot l % CPR of row l / CPR, so it fetches chunk
+// (l % CPR) ^ swizzle(row).
+constexpr int ROW_BYTES = BK * 2;
+constexpr int CPR = ROW_BYTES / 16;
+constexpr int ROWS_PER_KB = 1024 / ROW_BYTES;
+constexpr int SWZ_DIV = 256 / ROW_BYTES;
+constexpr int OP_BYTES = BM * ROW_BYTES;
+constexpr int STAGE_BYTES = 2 * OP_BYTES;              // A then B
+constexpr int LDS_BYTES = STAGES * STAGE_BYTES;
+constexpr int LOADS_PER_OP = 64 / ROWS_PER_KB;         // 1-KiB blocks per wave per operand
+constexpr int LOADS_PER_SLICE = 2 * LOADS_PER_OP;      // per wave
+constexpr int KSTEPS = BK / 16;
+static_assert(LDS_BYTES <= 160 * 1024, "LDS ring too large");
+static_assert(CPR >= 4 && ROWS_PER_KB <= 16, "slice geometry");
+static_assert((STAGES - 1) * LOADS_PER_SLICE <= 63, "vmcnt range");
 
 struct Acc {
   f32x16 c[4][4];
@@ -71,100 +100,168 @@ struct Src {
   int ld;
 };
 
-// LDS layout of a k-slice: row r of the tile occupies 128 contiguous bytes
-// (no padding); its 16-byte chunk c sits in slot c ^ ((r / 2) % 8).  With
-// 64 banks this keeps the MFMA fragment reads (32 consecutive rows, one
-// chunk, per half-wave) conflict-free, and it lets each wave fill whole
-// 1-KiB blocks with direct global->LDS loads: lane l of a block writes slot
-// l % 8 of row l / 8 and therefore fetches chunk (l % 8) ^ swizzle(row).
-__device__ __forceinline__ void issue_operand(const Src& S, int k, lds_u8* dst,
-                                              int wave, int lane) {
-  const int rsub = lane >> 3, slot = lane & 7;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int c = slot ^ ((4 * (i & 1) + (lane >> 4)) & 7);   // (row/2)%8 of this row
-    const bf16* g = (i < 4 ? S.lo : S.hi) + (8 * (i & 3) + rsub) * S.ld + k + c * 8;
-    __builtin_amdgcn_global_load_lds((gvoid*)g, (lds_void*)(dst + (64 * wave + 8 * i) * ROW_BYTES),
-                                     16, 0, 0);
-  }
+// One direct global->LDS load of 16 bytes per lane: lane l's data lands at
+// LDS byte lds_off + 16 l.  Written as a two-instruction asm statement (M0
+// set, one wait state for the M0 -> LDS-DMA hazard, then the load) so that
+// the compiler does not track it: it would otherwise wait for every such
+// load in flight before any LDS read, collapsing the multi-slice pipeline.
+// The statement has no register outputs; the address is consumed at issue.
+// Completion is awaited explicitly with wait_vm<>.
+__device__ __forceinline__ void dma16(const bf16* g, uint32_t lds_off) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(g), "s"(lds_off)
+               : "m0");
 }
 
-__device__ __forceinline__ void wait_loads() {
-  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
+}
+
+// The i-th of this wave's direct loads for one slice (A blocks first, then
+// B): LOADS_PER_OP 1-KiB blocks per operand, rows [64w, 64w + 64) of the tile.
+template <int I>
+__device__ __forceinline__ void issue_load(const Src& S, int k, uint32_t dst, int wave,
+                                           int lane) {
+  constexpr int i = I % LOADS_PER_OP;
+  const int rsub = lane / CPR, slot = lane % CPR;
+  const int rr = i * ROWS_PER_KB + rsub;                 // row within this wave's 64
+  const int c = slot ^ ((rr / SWZ_DIV) % CPR);
+  const bf16* g = (i * ROWS_PER_KB < 32 ? S.lo : S.hi) + (rr & 31) * S.ld + k + c * 8;
+  dma16(g, dst + (uint32_t)((64 * wave + i * ROWS_PER_KB) * ROW_BYTES));
 }
 
 struct Frags {
   bf16x8 a[4], b[4];
 };
 
-__device__ __forceinline__ void read_frags(Frags& f, const lds_u8* As, const lds_u8* Bs,
-                                           int wm, int wn, int lane, int kk) {
+// One 16-byte fragment read (Q < 4: A block Q, else B block Q - 4) of k-step kk.
+template <int Q>
+__device__ __forceinline__ void read_frag(Frags& f, const lds_u8* As, const lds_u8* Bs, int wm,
+                                          int wn, int lane, int kk) {
   const int r = lane & 31;
-  const int chunk = ((2 * kk + (lane >> 5)) ^ ((lane >> 1) & 7)) << 4;
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-    f.a[i] = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(
-        As + (wm * 128 + i * 32 + r) * ROW_BYTES + chunk);
-#pragma unroll
-  for (int j = 0; j < 4; ++j)
-    f.b[j] = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(
-        Bs + (wn * 128 + j * 32 + r) * ROW_BYTES + chunk);
+  const int chunk = ((2 * kk + (lane >> 5)) ^ ((r / SWZ_DIV) % CPR)) << 4;
+  typedef const __attribute__((address_space(3))) bf16x8 lds_frag;
+  if constexpr (Q < 4)
+    f.a[Q] = *reinterpret_cast<lds_frag*>(As + (wm * 128 + Q * 32 + r) * ROW_BYTES + chunk);
+  else
+    f.b[Q - 4] = *reinterpret_cast<lds_frag*>(Bs + (wn * 128 + (Q - 4) * 32 + r) * ROW_BYTES + chunk);
 }
 
-__device__ __forceinline__ void mma_frags(const Frags& f, Acc& acc) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc.c[i][j] = mfma32(f.a[i], f.b[j], acc.c[i][j]);
+// Per-workgroup stream state.
+// Everything is held by value (wave-uniform values in scalar registers): a
+// pointer to a stack copy would be spilled and re-read from scratch, and
+// that read's wait would also wait for every direct load in flight.
+struct Stream {
+  lds_u8* smem;
+  Src A, B0, B1;
+  int nk0, nk;
+  int wave, lane, wm, wn;
+  // the slice whose loads are spread over the current slice's MFMAs
+  int ld_k_a;
+  Src ld_b;            // B source of that slice, offset to its k
+  uint32_t ld_dst;
+
+  __device__ __forceinline__ void set_load(int s, int buf) {
+    s = min(s, nk - 1);   // past the end: re-fetch the last slice into a free buffer
+    ld_dst = (uint32_t)(uintptr_t)(smem + buf * STAGE_BYTES);
+    const bool ph0 = s < nk0;
+    ld_k_a = s * BK;
+    const int kb = ph0 ? s * BK : (s - nk0) * BK;
+    ld_b.lo = (ph0 ? B0.lo : B1.lo) + kb;
+    ld_b.hi = (ph0 ? B0.hi : B1.hi) + kb;
+    ld_b.ld = ph0 ? B0.ld : B1.ld;
+  }
+  template <int I>
+  __device__ __forceinline__ void load() const {
+    if constexpr (I < LOADS_PER_OP)
+      issue_load<I>(A, ld_k_a, ld_dst, wave, lane);
+    else
+      issue_load<I>(ld_b, 0, ld_dst + OP_BYTES, wave, lane);
+  }
+  template <int... I>
+  __device__ __forceinline__ void load_all(std::integer_sequence<int, I...>) const {
+    (load<I>(), ...);
+  }
+  __device__ __forceinline__ const lds_u8* a_buf(int buf) const { return smem + buf * STAGE_BYTES; }
+  __device__ __forceinline__ const lds_u8* b_buf(int buf) const {
+    return smem + buf * STAGE_BYTES + OP_BYTES;
+  }
+};
+
+// MFMA number IDX (block i = IDX/4, j = IDX%4) of a k-step, followed by at
+// most one memory instruction, then a scheduling barrier so that the exact
+// order (one memory op issued in the shadow of each MFMA) is kept.
+template <int KK, int IDX>
+__device__ __forceinline__ void kstep_op(const Stream& st, const Frags& cur, Frags& nxt, Acc& acc,
+                                         const lds_u8* As, const lds_u8* Bs, int kk_next) {
+  constexpr int i = IDX / 4, j = IDX % 4;
+  acc.c[i][j] = mfma32(cur.a[i], cur.b[j], acc.c[i][j]);
+  constexpr bool last = KK == KSTEPS - 1;
+  if constexpr (!last) {
+    if constexpr (IDX < 8) read_frag<IDX>(nxt, As, Bs, st.wm, st.wn, st.lane, kk_next);
+    constexpr int dma = (IDX - 8) + 8 * KK;      // MFMAs 8..15 of early k-steps carry loads
+    if constexpr (IDX >= 8 && dma < LOADS_PER_SLICE) st.template load<dma>();
+  } else {
+    if constexpr (IDX >= 8) read_frag<IDX - 8>(nxt, As, Bs, st.wm, st.wn, st.lane, 0);
+  }
+  __builtin_amdgcn_sched_barrier(0);
 }
 
-// Scheduling-group masks for __builtin_amdgcn_sched_group_barrier.
-constexpr int kSchedMFMA = 0x008;
-constexpr int kSchedVMEMRead = 0x020;
-constexpr int kSchedDSRead = 0x100;
+template <int KK, int... IDX>
+__device__ __forceinline__ void kstep_ops(const Stream& st, const Frags& cur, Frags& nxt,
+                                          Acc& acc, const lds_u8* As, const lds_u8* Bs,
+                                          int kk_next, std::integer_sequence<int, IDX...>) {
+  (kstep_op<KK, IDX>(st, cur, nxt, acc, As, Bs, kk_next), ...);
+}
 
-// One BK slice.  The 8 fragment reads of k-step kk+1 are interleaved one by
-// one with the MFMAs of k-step kk; with_loads also spreads the next slice's
-// 16 direct loads over the second half of k-steps 0 and 1.
-template <bool with_loads>
-__device__ __forceinline__ void mma_slice(const lds_u8* As, const lds_u8* Bs,
-                                          Acc& acc, int wm, int wn, int lane) {
-  Frags f0, f1;
-  read_frags(f0, As, Bs, wm, wn, lane, 0);
-#pragma unroll
-  for (int kk = 0; kk < BK / 16; ++kk) {
-    Frags& cur = (kk & 1) ? f1 : f0;
-    Frags& nxt = (kk & 1) ? f0 : f1;
-    if (kk + 1 < BK / 16) read_frags(nxt, As, Bs, wm, wn, lane, kk + 1);
-    mma_frags(cur, acc);
-    if (kk + 1 < BK / 16) {
-#pragma unroll
-      for (int g = 0; g < 8; ++g) {
-        __builtin_amdgcn_sched_group_barrier(kSchedMFMA, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 1, 0);
-      }
-      if (with_loads && kk < 2) {
-#pragma unroll
-        for (int g = 0; g < 8; ++g) {
-          __builtin_amdgcn_sched_group_barrier(kSchedMFMA, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(kSchedVMEMRead, 1, 0);
-        }
-      } else {
-        __builtin_amdgcn_sched_group_barrier(kSchedMFMA, 8, 0);
-      }
-    }
+// k-step KK of slice kt (LDS buffer buf).  Early k-steps read the next
+// k-step's fragments during their first 8 MFMAs and carry the direct loads
+// of slice kt + STAGES - 1 during the other 8.  The last k-step runs 8
+// MFMAs, waits for slice kt + 1 to have landed (for this wave) and meets the
+// other waves at the workgroup barrier -- after which slice kt's buffer is
+// free and slice kt + 1 is complete -- then reads slice kt + 1's first
+// fragments during its last 8 MFMAs.
+template <int KK>
+__device__ __forceinline__ void mma_kstep(Stream& st, Frags& cur, Frags& nxt, Acc& acc, int kt,
+                                          int buf, int buf_next) {
+  if constexpr (KK + 1 < KSTEPS) {
+    kstep_ops<KK>(st, cur, nxt, acc, st.a_buf(buf), st.b_buf(buf), KK + 1,
+                  std::make_integer_sequence<int, 16>{});
+    mma_kstep<KK + 1>(st, nxt, cur, acc, kt, buf, buf_next);
+  } else {
+    kstep_ops<KK>(st, cur, nxt, acc, st.a_buf(buf), st.b_buf(buf), 0,
+                  std::integer_sequence<int, 0, 1, 2, 3, 4, 5, 6, 7>{});
+    wait_vm<(STAGES - 2) * LOADS_PER_SLICE>();
+    __syncthreads();
+    // slice kt's buffer is free from here on: it takes slice kt + STAGES
+    st.set_load(kt + STAGES, buf);
+    kstep_ops<KK>(st, cur, nxt, acc, st.a_buf(buf_next), st.b_buf(buf_next), 0,
+                  std::integer_sequence<int, 8, 9, 10, 11, 12, 13, 14, 15>{});
   }
 }
 
-// Main loop over k.  Phase 0 covers k tiles [0, nk0) with B rows from B0,
-// phase 1 (if nk1 > 0) the next nk1 tiles from B1; A runs straight through.
-// Slice kt+1 streams into the other LDS buffer while slice kt is consumed.
+// Main loop over k.  Phase 0 covers k slices [0, nk0) with B rows from B0,
+// phase 1 (if nk1 > 0) the next nk1 slices from B1; A runs straight through.
+// A ring of STAGES LDS buffers: while slice kt is consumed, slices up to
+// kt + STAGES - 1 are loading or loaded.
 __device__ __forceinline__ void gemm_mainloop(lds_u8* smem, Acc& acc, const Src& A,
                                               const Src& B0, int nk0, const Src& B1,
                                               int nk1) {
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
-  const int wm = wave >> 1, wn = wave & 1;
+  static_assert(KSTEPS % 2 == 0, "slices start in the first fragment set");
+  static_assert(LOADS_PER_SLICE <= 8 * (KSTEPS - 1), "loads must fit the early k-steps");
+  Stream st;
+  st.smem = smem;
+  st.A = A;
+  st.B0 = B0;
+  st.B1 = B1;
+  st.nk0 = nk0;
+  st.nk = nk0 + nk1;
+  st.wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  st.lane = threadIdx.x & 63;
+  st.wm = st.wave >> 1;
+  st.wn = st.wave & 1;
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -172,25 +269,33 @@ __device__ __forceinline__ void gemm_mainloop(lds_u8* smem, Acc& acc, const Src&
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc.c[i][j][e] = 0.f;
 
-  const int nk = nk0 + nk1;
-  issue_operand(A, 0, smem, wave, lane);
-  issue_operand(B0, 0, smem + OP_BYTES, wave, lane);
-  wait_loads();
-  __syncthreads();
-  for (int kt = 0; kt + 1 < nk; ++kt) {
-    const int cur = (kt & 1) * STAGE_BYTES;
-    const int nxt = STAGE_BYTES - cur;
-    const int kn = kt + 1;
-    const bool ph0 = kn < nk0;
-    issue_operand(A, kn * BK, smem + nxt, wave, lane);
-    issue_operand(ph0 ? B0 : B1, ph0 ? kn * BK : (kn - nk0) * BK, smem + nxt + OP_BYTES, wave,
-                  lane);
-    mma_slice<true>(smem + cur, smem + cur + OP_BYTES, acc, wm, wn, lane);
-    wait_loads();
-    __syncthreads();
+  // prologue: slices 0 .. STAGES-2 in flight, slice STAGES-1 rides on slice 0
+#pragma unroll
+  for (int s = 0; s < STAGES - 1; ++s) {
+    st.set_load(s, s);
+    st.load_all(std::make_integer_sequence<int, LOADS_PER_SLICE>{});
   }
-  const int last = ((nk - 1) & 1) * STAGE_BYTES;
-  mma_slice<false>(smem + last, smem + last + OP_BYTES, acc, wm, wn, lane);
+  st.set_load(STAGES - 1, STAGES - 1);
+  wait_vm<(STAGES - 2) * LOADS_PER_SLICE>();
+  __syncthreads();
+  Frags f0, f1;
+  read_frag<0>(f0, st.a_buf(0), st.b_buf(0), st.wm, st.wn, st.lane, 0);
+  read_frag<1>(f0, st.a_buf(0), st.b_buf(0), st.wm, st.wn, st.lane, 0);
+  read_frag<2>(f0, st.a_buf(0), st.b_buf(0), st.wm, st.wn, st.lane, 0);
+  read_frag<3>(f0, st.a_buf(0), st.b_buf(0), st.wm, st.wn, st.lane, 0);
+  read_frag<4>(f0, st.a_buf(0), st.b_buf(0), st.wm, st.wn, st.lane, 0);
+  read_frag<5>(f0, st.a_buf(0), st.b_buf(0), st.wm, st.wn, st.lane, 0);
+  read_frag<6>(f0, st.a_buf(0), st.b_buf(0), st.wm, st.wn, st.lane, 0);
+  read_frag<7>(f0, st.a_buf(0), st.b_buf(0), st.wm, st.wn, st.lane, 0);
+  int buf = 0;
+  for (int kt = 0; kt < st.nk; ++kt) {
+    const int buf_next = buf + 1 == STAGES ? 0 : buf + 1;
+    mma_kstep<0>(st, f0, f1, acc, kt, buf, buf_next);
+    buf = buf_next;
+  }
+  // the re-fetches issued by the last iterations must land before the
+  // workgroup can release its LDS
+  wait_vm<0>();
 }
 
 struct ProjArgs {
@@ -234,58 +339,72 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_gemm_proj(ProjArgs p) {
     hid0 = (nt - 3 * qkv_tiles) * 128;
   }
   const int D = p.D;
-  // first row of 32-row run i of the B tile
-  auto b_run = [&](int i) -> const bf16* {
+  // first row of 32-row run i of the weight tile (256 output features)
+  auto w_run = [&](int i) -> const bf16* {
     if (kind < 3) {
       const bf16* W = kind == 0 ? p.wq : (kind == 1 ? p.wk : p.wv);
       return W + (size_t)(head0 * 128 + 32 * i) * D;
     }
+    // SwiGLU tiles: each 128-row half holds 64 gate rows then the 64 up rows
+    // of the same hidden units, so gate and up land in one lane's registers
     const int half = i >> 2, blk = i & 3;
     const bf16* W = blk < 2 ? p.wg : p.wu;
     return W + (size_t)(hid0 + 64 * half + 32 * (blk & 1)) * D;
   };
-  Src A, B;
-  A.lo = p.h + (size_t)(m0 + 64 * wave) * D;
-  A.hi = A.lo + (size_t)32 * D;
-  A.ld = D;
-  B.lo = b_run(2 * wave);
-  B.hi = b_run(2 * wave + 1);
-  B.ld = D;
+  Src H, W;
+  H.lo = p.h + (size_t)(m0 + 64 * wave) * D;
+  H.hi = H.lo + (size_t)32 * D;
+  H.ld = D;
+  W.lo = w_run(2 * wave);
+  W.hi = w_run(2 * wave + 1);
+  W.ld = D;
+  // Values use C = h . Wv^T (a lane then holds 4 consecutive tokens of one
+  // dim, the order of the transposed store).  Queries, keys and SwiGLU use
+  // C^T = W . h^T: a lane holds one token and 4 consecutive features per
+  // register group, so RoPE pairs are lane-local, the per-head RMS needs one
+  // exchange with lane ^ 32, and stores are 8 bytes wide.
   Acc acc;
-  gemm_mainloop(smem, acc, A, B, D / BK, B, 0);
+  if (kind == 2)
+    gemm_mainloop(smem, acc, H, W, D / BK, W, 0);
+  else
+    gemm_mainloop(smem, acc, W, H, D / BK, H, 0);
 
   const int r32 = lane & 31, hi = lane >> 5;
   if (kind < 2) {
-    // per-head RMSNorm + RoPE; this wave holds one full head of 128 tokens
-    const int head = head0 + wn;
+    // per-head RMSNorm + RoPE: this wave holds head head0 + wm for 128 tokens
+    const int head = head0 + wm;
     const float* nw = kind == 0 ? p.qn : p.kn;
     bf16* dst = (kind == 0 ? p.q : p.k) + (size_t)head * p.n_pad * kHeadDim;
-    float w[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) w[j] = nw[j * 32 + r32];
+    for (int j = 0; j < 4; ++j) {
+      const int m = m0 + wn * 128 + j * 32 + r32;
+      const bool live = m < p.M;
+      float ss = 0.f;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+      for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int m = m0 + wm * 128 + i * 32 + 8 * (e >> 2) + 4 * hi + (e & 3);
-        float ss = 0.f;
+        for (int e = 0; e < 16; ++e) ss += acc.c[i][j][e] * acc.c[i][j][e];
+      ss += xor_lane(ss, 32);
+      const float rs = 1.0f / sqrtf(ss * (1.0f / kHeadDim) + p.eps);
+      const float* rr = reinterpret_cast<const float*>(p.rope) + (size_t)(live ? m : 0) * 2 * kRopePairs;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) ss += acc.c[i][j][e] * acc.c[i][j][e];
+      for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int o = 1; o < 32; o <<= 1) ss += xor_lane(ss, o);
-        const float rs = 1.0f / sqrtf(ss * (1.0f / kHeadDim) + p.eps);
-        const bool live = m < p.M;
-        const float2* rr = p.rope + (size_t)(live ? m : 0) * kRopePairs;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int d = j * 32 + r32;
-          const float v = acc.c[i][j][e] * rs * w[j];
-          const float vp = xor_lane(v, 1);
-          const float2 cs = rr[d >> 1];
-          const float o = (d & 1) ? (vp * cs.y + v * cs.x) : (v * cs.x - vp * cs.y);
-          dst[(size_t)m * kHeadDim + d] = f2bf(live ? o : 0.f);
+        for (int g = 0; g < 4; ++g) {
+          const int d0 = i * 32 + 8 * g + 4 * hi;          // 4 consecutive dims = 2 pairs
+          const float4 wv = *reinterpret_cast<const float4*>(nw + d0);
+          const float4 cs = *reinterpret_cast<const float4*>(rr + d0);   // cos0 sin0 cos1 sin1
+          const float x0 = acc.c[i][j][4 * g + 0] * rs * wv.x;
+          const float x1 = acc.c[i][j][4 * g + 1] * rs * wv.y;
+          const float x2 = acc.c[i][j][4 * g + 2] * rs * wv.z;
+          const float x3 = acc.c[i][j][4 * g + 3] * rs * wv.w;
+          bf16x4 o;
+          o[0] = f2bf(live ? x0 * cs.x - x1 * cs.y : 0.f);
+          o[1] = f2bf(live ? x0 * cs.y + x1 * cs.x : 0.f);
+          o[2] = f2bf(live ? x2 * cs.z - x3 * cs.w : 0.f);
+          o[3] = f2bf(live ? x2 * cs.w + x3 * cs.z : 0.f);
+          *reinterpret_cast<bf16x4*>(dst + (size_t)m * kHeadDim + d0) = o;
         }
-      }
     }
   } else if (kind == 2) {
     // values, transposed: vt[head][d][pos(m)], 4 consecutive tokens per store
@@ -308,22 +427,26 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_gemm_proj(ProjArgs p) {
       }
     }
   } else {
-    // SwiGLU: blocks 0,1 are gate columns, blocks 2,3 the matching up columns
+    // SwiGLU: register blocks 0,1 are gate rows, 2,3 the matching up rows
     const int ldc = D + p.F;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int j = 0; j < 4; ++j) {
+      const int m = m0 + wn * 128 + j * 32 + r32;
+      const bool live = m < p.M;
+      bf16* dst = p.cat + (size_t)m * ldc + D + hid0 + 64 * wm;
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int m = m0 + wm * 128 + i * 32 + 8 * (e >> 2) + 4 * hi + (e & 3);
-        const bool live = m < p.M;
+      for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const int hc = hid0 + 64 * wn + 32 * j + r32;
-          const float g = acc.c[i][j][e], u = acc.c[i][j + 2][e];
-          const float a = g / (1.0f + __expf(-g)) * u;
-          p.cat[(size_t)m * ldc + D + hc] = f2bf(live ? a : 0.f);
+        for (int g = 0; g < 4; ++g) {
+          bf16x4 o;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float gt = acc.c[i][j][4 * g + e], up = acc.c[i + 2][j][4 * g + e];
+            const float a = gt * __builtin_amdgcn_rcpf(1.0f + __expf(-gt)) * up;
+            o[e] = f2bf(live ? a : 0.f);
+          }
+          *reinterpret_cast<bf16x4*>(dst + 32 * i + 8 * g + 4 * hi) = o;
         }
-      }
     }
   }
 }
