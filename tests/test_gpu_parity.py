@@ -282,3 +282,49 @@ def test_per_mode_block_equals_single_segment_block():
                         rope[s.start:s.start + s.count].contiguous(), workspace(dims, s.count))
         torch.cuda.synchronize()
         np.testing.assert_array_equal(got[s.start:s.start + s.count], xs.cpu().numpy())
+
+
+# --------------------------------------------------------------------------
+# the other workloads: 1024^2 text-to-image block, 4K block, per-mode stage
+# --------------------------------------------------------------------------
+def test_block_t2i4336_all_rows():
+    """One joint block over 240 text + 64x64 image tokens, every row."""
+    dims = synth.DIMS
+    layout, segs, w, x, mod = _case(name="t2i4336", seed=2)
+    got, _, _ = run_block(dims, w, x, segs, mod, layout)
+    want = O.block_forward(x, w, seg_tuples(segs), mod, oracle_rope(layout), dtype=np.float32)
+    assert_close(got, want, "x_out t2i4336")
+    assert_close(got - x, want - x, "delta t2i4336")
+
+
+def test_block_4k_sampled_rows():
+    """One joint block over 240 text + 256x256 image tokens (4096x4096 px):
+    the long-sequence attention shape, checked on sampled rows."""
+    dims = synth.DIMS
+    layout, segs, w, x, mod = _case(name="t2i4k65776", seed=4)
+    got, _, _ = run_block(dims, w, x, segs, mod, layout)
+    rng = np.random.default_rng(4)
+    n = layout.n_tokens
+    rows = np.unique(np.concatenate([[0, 239, 240, 241, n - 2, n - 1],
+                                     rng.choice(n, 42, replace=False)]))
+    want = O.block_forward_rows(x, w, seg_tuples(segs), mod, oracle_rope(layout), rows,
+                                dtype=np.float32, attn_chunk=16)
+    assert_close(got[rows], want, "x_out rows 4k")
+    assert_close(got[rows] - x[rows], want - x[rows], "delta rows 4k")
+
+
+@pytest.mark.parametrize("name,mode", [("permode_text240", 0), ("permode_image4096", 1)])
+def test_per_mode_stage_streams(name, mode):
+    """The per-mode stage alone: a stream's 5 blocks with its own weights
+    (self-attention within the stream), against the oracle's stack."""
+    dims = synth.DIMS
+    layout = synth.workload(name).layout
+    segs = layout.segments()
+    assert len(segs) == 1 and segs[0].mode == mode
+    pm = {mode: [weights(7, 300 + b, dims) for b in range(5)]}
+    x = synth.tokens(7, layout.n_tokens, dims.width)
+    m1 = synth.modulation(7, 3, 1, dims.width)
+    got = _run_stack(dims, layout, segs, pm, [], x, m1, m1, False)
+    want = O.stack_forward(x, pm, [], seg_tuples(segs), m1, m1, oracle_rope(layout),
+                           dtype=np.float32)
+    assert_close_stack(got, want, x, f"per-mode {name}")
