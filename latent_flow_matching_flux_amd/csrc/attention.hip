@@ -7,25 +7,29 @@
 // Queries and keys arrive RMS-normalised and rotated; the scale is
 // 1/sqrt(128).
 //
-// Work split: a workgroup is 4 waves x 64 queries of one head (one wave per
-// SIMD).  A wave keeps its 64 queries in registers and computes
-// S^T = K . Q^T with the 32x32x16 bf16 MFMA, so every lane owns one query of
-// each 32-query block and 16 of each 32 keys; O^T = V^T . P^T then takes the
+// Work split: a workgroup is 8 waves x 32 queries of one head, two waves per
+// SIMD.  A wave keeps its 32 queries in registers and computes
+// S^T = K . Q^T with the 32x32x16 bf16 MFMA, so every lane owns one query
+// (lane % 32) and 16 of each 32 keys; O^T = V^T . P^T then takes the
 // probabilities straight from those registers as the B operand (V arrives
-// transposed, keys permuted inside each group of 16 to match).  Every K or
-// V^T fragment read from LDS feeds two MFMAs (one per 32-query block).
+// transposed, keys permuted inside each group of 16 to match).
 //
-// K and V^T tiles of 64 keys stream from global memory straight into a
-// 4-deep LDS ring (gfx950 direct loads, XOR-swizzled rows), two tiles ahead.
-// Keys are processed in blocks of 32: the QK^T MFMAs of the next block are
-// issued before the softmax of the current one.
+// Software pipeline over 64-key tiles: while the softmax of tile t runs on
+// the VALU, the same wave issues the QK^T MFMAs of tile t+1 and the PV MFMAs
+// of tile t-1, one of each per slot, with LDS fragments fetched four slots
+// ahead; the order inside a tile is pinned with scheduling barriers.  K and
+// V^T stream from global memory straight into two 4-deep LDS rings (gfx950
+// direct loads, XOR-swizzled rows), K four tiles and V^T two tiles ahead of
+// their use, one workgroup barrier per tile.
 //
 // Online softmax with lazy rescaling: scores are kept in the log2 domain
-// (log2(e)/sqrt(128) folded into the scale); the running reference max of a
-// query only moves -- and O and the running sum are only rescaled -- when a
-// tile's max exceeds it by more than TAU, so exp2(s - m) <= 2^TAU and fp32 /
-// bf16 never overflow.  Keys past the sequence end are masked to -inf (the
-// workspace pads them with zeros).
+// (log2(e)/sqrt(128) folded into one FMA with the max); the reference max of
+// a query only moves -- and O and the running sum are only rescaled -- when
+// a tile's max exceeds it by more than TAU, so exp2(s - m) <= 2^TAU and fp32
+// / bf16 never overflow.  Keys past the sequence end are masked in the last
+// tile (the workspace pads them with zeros).
+#include <type_traits>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -33,18 +37,20 @@ namespace flux3 {
 
 namespace {
 
-constexpr int QW = 64;                 // queries per wave
-constexpr int WAVES = 4;
+constexpr int QW = 32;                 // queries per wave
+constexpr int WAVES = 8;
+constexpr int NTHREADS = 64 * WAVES;
 constexpr int AQ = QW * WAVES;         // queries per workgroup
 constexpr int AKV = 64;                // keys per tile
-constexpr int NSTAGE = 4;              // LDS ring depth (tiles)
+constexpr int NSTAGE = 4;              // depth of each LDS ring (tiles)
 constexpr int K_ROW = kHeadDim * 2;    // 256 B: one key of K
 constexpr int V_ROW = AKV * 2;         // 128 B: one dim of V^T for the tile
 constexpr int K_BYTES = AKV * K_ROW;   // 16 KiB
 constexpr int V_BYTES = kHeadDim * V_ROW;  // 16 KiB
-constexpr int STAGE_BYTES = K_BYTES + V_BYTES;
-constexpr int LDS_BYTES = NSTAGE * STAGE_BYTES;  // 128 KiB
-constexpr int DMA_PER_TILE = 8;        // per wave: 4 for K, 4 for V^T
+constexpr int V_RING = NSTAGE * K_BYTES;   // byte offset of the V^T ring
+constexpr int LDS_BYTES = NSTAGE * (K_BYTES + V_BYTES);  // 128 KiB
+constexpr int DMA_PER_GROUP = 4;       // per wave: 2 for a K tile, 2 for a V^T tile
+constexpr int PREFETCH = 4;            // fragment reads run this many slots ahead
 constexpr float TAU = 8.0f;
 
 typedef __attribute__((address_space(3))) unsigned char lds_u8;
@@ -57,12 +63,23 @@ struct AttnArgs {
   float scale_log2;  // log2(e) / sqrt(head_dim)
 };
 
-// Direct global->LDS load, 16 bytes per lane to LDS byte lds_off + 16 * lane
-// (see the projection GEMM for why it is an asm statement).
-__device__ __forceinline__ void dma16(const bf16* g, uint32_t lds_off) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+template <int B, int E, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
+}
+
+// Direct global->LDS load of 16 bytes per lane from base + voff (a uniform
+// base in SGPRs, a per-lane byte offset) to LDS byte lds_off + 16 * lane.
+// An asm statement (M0 set, one wait state for the M0 -> LDS-DMA hazard,
+// the load) so that the compiler does not wait for it before every LDS
+// read; completion is awaited explicitly with wait_vm<>.
+__device__ __forceinline__ void dma16(const void* base, uint32_t voff, uint32_t lds_off) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
                :
-               : "v"(g), "s"(lds_off)
+               : "v"(voff), "s"(base), "s"(lds_off)
                : "m0");
 }
 
@@ -73,127 +90,174 @@ __device__ __forceinline__ void wait_vm() {
 
 // LDS layouts.  K tile: key r's 256 bytes, 16-byte chunk c in slot
 // c ^ (r % 16).  V^T tile: dim r's 128 bytes, chunk c in slot c ^ ((r/2) % 8).
-// Both keep 16 consecutive rows of a fragment read on distinct banks.
-__device__ __forceinline__ void issue_tile(const bf16* kh, const bf16* vh, int n_pad, int kv0,
-                                           uint32_t stage, int wave, int lane) {
-  // K: this wave loads keys [16 wave, 16 wave + 16): 4 blocks of 4 rows x 256 B
+// Both keep the 16 consecutive rows of a fragment read on distinct banks.
+// A wave loads keys [8 wave, 8 wave + 8) of a K tile (2 blocks of 4 rows x
+// 256 B) and dims [16 wave, 16 wave + 16) of a V^T tile (2 blocks of 8 rows
+// x 128 B); the per-lane source offsets inside a tile are fixed.
+struct DmaLanes {
+  uint32_t k[2], v[2];   // byte offsets from the tile's first key / column
+};
+
+__device__ __forceinline__ DmaLanes dma_lanes(int n_pad, int wave, int lane) {
+  DmaLanes d;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int row = 16 * wave + 4 * i + (lane >> 4);
-    const int c = (lane & 15) ^ (row & 15);
-    dma16(kh + (size_t)(kv0 + row) * kHeadDim + c * 8, stage + (16 * wave + 4 * i) * K_ROW);
+  for (int i = 0; i < 2; ++i) {
+    const int kr = 8 * wave + 4 * i + (lane >> 4);
+    d.k[i] = (uint32_t)(kr * kHeadDim + ((lane & 15) ^ (kr & 15)) * 8) * 2;
+    const int vr = 16 * wave + 8 * i + (lane >> 3);
+    d.v[i] = (uint32_t)(vr * n_pad + ((lane & 7) ^ ((vr >> 1) & 7)) * 8) * 2;
   }
-  // V^T: this wave loads dims [32 wave, 32 wave + 32): 4 blocks of 8 rows x 128 B
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int row = 32 * wave + 8 * i + (lane >> 3);
-    const int c = (lane & 7) ^ ((row >> 1) & 7);
-    dma16(vh + (size_t)row * n_pad + kv0 + c * 8, stage + K_BYTES + (32 * wave + 8 * i) * V_ROW);
-  }
+  return d;
 }
 
-typedef f32x16 SHalf[2];        // S^T for 32 keys x 2 query blocks
-typedef bf16x8 PHalf[2][2];     // P^T fragments: [16-key half][query block]
-
-// S^T for key block kb (32 keys) of a tile: 8 head-dim steps x 2 query blocks.
-__device__ __forceinline__ void qk_half(SHalf& S, const lds_u8* Ks, int kb,
-                                        const bf16x8 (&qf)[2][8], int lane) {
-  const int r = lane & 31, hh = lane >> 5;
+__device__ __forceinline__ void issue_k(const bf16* kh, int kv0, uint32_t dst, const DmaLanes& dl,
+                                        int wave) {
+  const bf16* base = kh + (size_t)kv0 * kHeadDim;
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb)
+  for (int i = 0; i < 2; ++i) dma16(base, dl.k[i], dst + (8 * wave + 4 * i) * K_ROW);
+}
+__device__ __forceinline__ void issue_v(const bf16* vh, int kv0, uint32_t dst, const DmaLanes& dl,
+                                        int wave) {
+  const bf16* base = vh + kv0;
 #pragma unroll
-    for (int e = 0; e < 16; ++e) S[qb][e] = 0.f;
-  const int row = kb * 32 + r;
-#pragma unroll
-  for (int ks = 0; ks < 8; ++ks) {
-    const int c = (2 * ks + hh) ^ (row & 15);
-    const bf16x8 a = *reinterpret_cast<lds_frag*>(Ks + row * K_ROW + c * 16);
-    S[0] = mfma32(a, qf[0][ks], S[0]);
-    S[1] = mfma32(a, qf[1][ks], S[1]);
-  }
+  for (int i = 0; i < 2; ++i) dma16(base, dl.v[i], dst + (16 * wave + 8 * i) * V_ROW);
 }
 
-// O^T += V^T . P^T for key block kb (32 keys) of a tile.
-__device__ __forceinline__ void pv_half(f32x16 (&o)[4][2], const lds_u8* Vs, int kb,
-                                        const PHalf& pf, int lane) {
+typedef f32x16 STile[2];        // S^T of one tile: [32-key block]
+// P^T fragments as packed bf16 pairs: [32-key block][16-key half][pair]
+typedef uint32_t PTile[2][2][4];
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ bf16x8 pfrag(const uint32_t (&w)[4]) {
+  const u32x4 v = {w[0], w[1], w[2], w[3]};
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+// Keeps a value computed where it stands: earlier passes may otherwise sink
+// it past the scheduling barriers into a later block.
+template <class T>
+__device__ __forceinline__ void pin(T& v) {
+  asm volatile("" : "+v"(v));
+}
+
+// Per-query online softmax state of one lane.
+struct SoftState {
+  float m_ref;   // reference max, log2 domain
+  float l_sum;   // running sum of exp2(s - m_ref) over this lane's keys
+  float alpha;   // factor O must take before the next PV (1 if m_ref held)
+  bool moved;    // wave-uniform: m_ref moved in the last softmax
+};
+
+// One tile's worth of pipelined work, in 32 slots.  Even slot 2j: QK^T
+// MFMA j of tile t+1 (k-step j/2, key block j%2) into Sn; odd slot 2j+1: PV
+// MFMA j of tile t-1 (key block j/8, 16-key half (j/4)%2, dim block j%4)
+// with probabilities Pp.  Softmax of tile t (scores Sc -> Pc) rides along:
+// slots 0-7 take the max, slot 8 moves the reference, slots 9-24 take two
+// exponentials each, slot 25 closes the sum.
+template <bool QK, bool PV, bool SM, bool MASK>
+__device__ __forceinline__ void region(STile& Sn, uint32_t k_off, f32x16 (&o)[4], uint32_t v_off,
+                                       const PTile& Pp, const STile& Sc, PTile& Pc, SoftState& st,
+                                       const bf16x8 (&qf)[8], const lds_u8* smem, float scale,
+                                       int key0, int M, int lane) {
   const int r = lane & 31, hh = lane >> 5;
-#pragma unroll
-  for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-    for (int d = 0; d < 4; ++d) {
-      const int row = d * 32 + r;
-      const int c = (4 * kb + 2 * tt + hh) ^ ((row >> 1) & 7);
-      const bf16x8 a = *reinterpret_cast<lds_frag*>(Vs + row * V_ROW + c * 16);
-      o[d][0] = mfma32(a, pf[tt][0], o[d][0]);
-      o[d][1] = mfma32(a, pf[tt][1], o[d][1]);
+  // fragment addresses: row base with the lane's swizzle term, the k-step
+  // part of the chunk index is xor-ed in per slot
+  const uint32_t ka = k_off + r * K_ROW + 16 * (hh ^ (r & 15));
+  const uint32_t va = v_off + r * V_ROW + 16 * (hh ^ ((r >> 1) & 7));
+  bf16x8 fr[32];
+  auto load = [&](auto ic) {
+    constexpr int i = decltype(ic)::value;
+    if constexpr ((i & 1) ? PV : QK) {
+      constexpr int j = i / 2;
+      uint32_t a;
+      if constexpr ((i & 1) == 0)
+        a = (ka ^ (32 * (j / 2))) + (j % 2) * 32 * K_ROW;
+      else
+        a = (va ^ (64 * (j / 8) + 32 * ((j / 4) % 2))) + (j % 4) * 32 * V_ROW;
+      fr[i] = *reinterpret_cast<lds_frag*>(smem + a);
     }
-}
+  };
+  static_for<0, PREFETCH>(load);
 
-// Softmax of one 32-key block: raw scores S (in units of q.k), masking keys
-// past the end when MASK.  The reference max moves only when the block's
-// max (log2 domain) exceeds it by more than TAU; then `alpha` is the factor
-// that O must be multiplied by once the PV MFMAs issued so far have landed,
-// and the function returns true.  P = exp2(scale * S - m) goes to bf16.
-template <bool MASK>
-__device__ __forceinline__ bool softmax_half(const SHalf& S, PHalf& pf, float (&m_ref)[2],
-                                             float (&l_sum)[2], float (&alpha)[2], float scale,
-                                             int key0, int M, int hh) {
-  float mx[2];
-  float v[2][16];
+  float vals[32];
+  float m = -INFINITY, l = 0.f;
+  auto val = [&](int idx) -> float {
+    const int kb = idx >> 4, e = idx & 15;
+    float s = Sc[kb][e];
+    if constexpr (MASK) {
+      const int jk = key0 + kb * 32 + 8 * (e >> 2) + 4 * hh + (e & 3);
+      s = jk < M ? s : -INFINITY;
+    }
+    return s;
+  };
+
+  static_for<0, 32>([&](auto ic) {
+    constexpr int i = decltype(ic)::value;
+    constexpr int j = i / 2;
+    if constexpr ((i & 1) == 0 && QK) {
+      constexpr int ks = j / 2, kb = j % 2;
+      if constexpr (ks == 0)
+        Sn[kb] = mfma32(fr[i], qf[0], f32x16{});
+      else
+        Sn[kb] = mfma32(fr[i], qf[ks], Sn[kb]);
+    }
+    if constexpr ((i & 1) == 1 && PV) {
+      constexpr int kb = j / 8, tt = (j / 4) % 2, d = j % 4;
+      o[d] = mfma32(fr[i], pfrag(Pp[kb][tt]), o[d]);
+    }
+    if constexpr (i + PREFETCH < 32) load(std::integral_constant<int, i + PREFETCH>{});
+    if constexpr (SM) {
+      if constexpr (i < 8) {
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
+        for (int u = 0; u < 4; ++u) {
+          vals[4 * i + u] = val(4 * i + u);
+          m = fmaxf(m, vals[4 * i + u]);
+        }
+      } else if constexpr (i == 8) {
+        m *= scale;
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m),
+                                                         false, false);
+        const float mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+        st.moved = __any(mx > st.m_ref + TAU);
+        const float m_new = st.moved ? fmaxf(st.m_ref, mx) : st.m_ref;
+        st.alpha = __builtin_amdgcn_exp2f(st.m_ref - m_new);
+        st.m_ref = m_new;
+        st.l_sum *= st.alpha;
+      } else if constexpr (i >= 9 && i <= 24) {
+        constexpr int idx = 2 * (i - 9);
+        f32x2 pp;
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      v[qb][e] = S[qb][e];
-      if constexpr (MASK) {
-        const int j = key0 + 8 * (e >> 2) + 4 * hh + (e & 3);
-        v[qb][e] = j < M ? v[qb][e] : -INFINITY;
+        for (int u = 0; u < 2; ++u) {
+          pp[u] = __builtin_amdgcn_exp2f(__builtin_fmaf(vals[idx + u], scale, -st.m_ref));
+          l += pp[u];
+        }
+        const bf16x2 pb = __builtin_convertvector(pp, bf16x2);
+        uint32_t w = __builtin_bit_cast(uint32_t, pb);
+        pin(w);
+        Pc[idx >> 4][(idx >> 3) & 1][(idx & 7) >> 1] = w;
+      } else if constexpr (i == 25) {
+        st.l_sum += l;
+        pin(st.l_sum);
       }
     }
-    float m = v[qb][0];
-#pragma unroll
-    for (int e = 1; e < 16; ++e) m = fmaxf(m, v[qb][e]);
-    m *= scale;
-    mx[qb] = fmaxf(m, xor_lane(m, 32));
-  }
-  // branch-free so the whole softmax stays one scheduling region with the
-  // MFMAs it hides behind; alpha is 1 when nothing moved
-  const bool grow = (mx[0] > m_ref[0] + TAU) || (mx[1] > m_ref[1] + TAU);
-  const bool any = __any(grow);
-#pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
-    const float m_new = any ? fmaxf(m_ref[qb], mx[qb]) : m_ref[qb];
-    alpha[qb] = __builtin_amdgcn_exp2f(m_ref[qb] - m_new);
-    m_ref[qb] = m_new;
-    l_sum[qb] *= alpha[qb];
-  }
-#pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
-    float l = 0.f;
-#pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(v[qb][e], scale, -m_ref[qb]));
-      l += pv;
-      pf[e >> 3][qb][e & 7] = f2bf(pv);
-    }
-    l_sum[qb] += l;
-  }
-  return any;
+    __builtin_amdgcn_sched_barrier(0);
+  });
 }
 
-__device__ __forceinline__ void rescale_o(f32x16 (&o)[4][2], const float (&alpha)[2]) {
-#pragma unroll
-  for (int qb = 0; qb < 2; ++qb)
+__device__ __forceinline__ void rescale(f32x16 (&o)[4], const SoftState& st) {
+  if (st.moved) {
 #pragma unroll
     for (int d = 0; d < 4; ++d)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) o[d][qb][e] *= alpha[qb];
+      for (int e = 0; e < 16; ++e) o[d][e] *= st.alpha;
+  }
 }
 
-__global__ __launch_bounds__(256, 1) void k_attention(AttnArgs p) {
+__global__ __launch_bounds__(NTHREADS, 1) void k_attention(AttnArgs p) {
   __shared__ __attribute__((aligned(1024))) unsigned char smem_raw[LDS_BYTES];
-  lds_u8* smem = (lds_u8*)smem_raw;
-  const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
+  const lds_u8* smem = (const lds_u8*)smem_raw;
+  const uint32_t lds0 = (uint32_t)(uintptr_t)smem_raw;
   const int t = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6), lane = t & 63;
   const int r32 = lane & 31, hh = lane >> 5;
@@ -216,95 +280,121 @@ __global__ __launch_bounds__(256, 1) void k_attention(AttnArgs p) {
   const bf16* kh = p.k + (size_t)head * p.n_pad * kHeadDim;
   const bf16* vh = p.vt + (size_t)head * kHeadDim * p.n_pad;
   const int nkv = (p.M + AKV - 1) / AKV;
+  const int M = p.M;
+  const float sc = p.scale_log2;
 
-  // stream the first tiles while the queries load
+  bf16x8 qf[8];
 #pragma unroll
-  for (int s = 0; s < NSTAGE - 1; ++s)
-    issue_tile(kh, vh, p.n_pad, min(s, nkv - 1) * AKV, lds0 + s * STAGE_BYTES, wave, lane);
+  for (int ks = 0; ks < 8; ++ks)
+    qf[ks] = *reinterpret_cast<const bf16x8*>(qh + (size_t)(q0 + r32) * kHeadDim + ks * 16 + hh * 8);
 
-  bf16x8 qf[2][8];
+  // DMA group g (issued at the top of tile g): K tile g+4 and V^T tile g+2,
+  // indices clamped to the last tile; the prologue issues groups -4..-1.
+  const DmaLanes dl = dma_lanes(p.n_pad, wave, lane);
+  auto k_stage = [](int tile) { return (uint32_t)((tile & (NSTAGE - 1)) * K_BYTES); };
+  auto v_stage = [](int tile) { return (uint32_t)(V_RING + (tile & (NSTAGE - 1)) * V_BYTES); };
+  auto issue_group = [&](int g) {
+    const int kt = g + 4, vt = g + 2;
+    issue_k(kh, min(kt, nkv - 1) * AKV, lds0 + k_stage(kt), dl, wave);
+    issue_v(vh, max(0, min(vt, nkv - 1)) * AKV, lds0 + v_stage(vt), dl, wave);
+  };
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks)
-      qf[qb][ks] = *reinterpret_cast<const bf16x8*>(
-          qh + (size_t)(q0 + qb * 32 + r32) * kHeadDim + ks * 16 + hh * 8);
+  for (int g = -4; g < 0; ++g) issue_group(g);
 
-  f32x16 o[4][2];
+  f32x16 o[4];
 #pragma unroll
   for (int d = 0; d < 4; ++d)
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) o[d][qb][e] = 0.f;
-  float m_ref[2] = {-INFINITY, -INFINITY}, l_sum[2] = {0.f, 0.f};
-  const float sc = p.scale_log2;
-  const int M = p.M;
-  auto stage_ptr = [&](int tile) -> const lds_u8* { return smem + (tile % NSTAGE) * STAGE_BYTES; };
-  // tile it+1 must be in LDS; past this barrier tile it-1's stage is free
-  auto advance = [&](int it) {
-    wait_vm<(NSTAGE - 3) * DMA_PER_TILE>();
+    for (int e = 0; e < 16; ++e) o[d][e] = 0.f;
+  SoftState st{-INFINITY, 0.f, 1.f, false};
+  STile S0, S1;
+  PTile P0, P1;
+
+  // top of tile it: K tile it+1 and V^T tile it-1 (group it-3) resident in
+  // every wave's part; past the barrier K tile it and V^T tile it-2 are no
+  // longer read, and group it refills those stages
+  auto top = [&](int it) {
+    wait_vm<2 * DMA_PER_GROUP>();
     __syncthreads();
-    issue_tile(kh, vh, p.n_pad, min(it + NSTAGE - 1, nkv - 1) * AKV,
-               lds0 + ((it + NSTAGE - 1) % NSTAGE) * STAGE_BYTES, wave, lane);
+    issue_group(it);
   };
 
-  wait_vm<(NSTAGE - 2) * DMA_PER_TILE>();
+  // scores of tile 0 (group -4 landed: the later 3 groups may be in flight)
+  wait_vm<3 * DMA_PER_GROUP>();
   __syncthreads();
-  // 32-key blocks: the scores of the next block are computed before the
-  // softmax of the current one, then the current block's PV.
-  SHalf Sa, Sb;
-  PHalf pf;
-  float alpha[2];
-  qk_half(Sa, smem, 0, qf, lane);
-  for (int it = 0; it + 1 < nkv; ++it) {
-    const lds_u8* cur = stage_ptr(it);
-    const int kv0 = it * AKV;
-    qk_half(Sb, cur, 1, qf, lane);
-    if (softmax_half<false>(Sa, pf, m_ref, l_sum, alpha, sc, kv0, M, hh)) rescale_o(o, alpha);
-    pv_half(o, cur + K_BYTES, 0, pf, lane);
-    advance(it);
-    qk_half(Sa, stage_ptr(it + 1), 0, qf, lane);
-    if (softmax_half<false>(Sb, pf, m_ref, l_sum, alpha, sc, kv0 + 32, M, hh)) rescale_o(o, alpha);
-    pv_half(o, cur + K_BYTES, 1, pf, lane);
-  }
-  {
-    // last tile, keys past the sequence end masked
-    const int it = nkv - 1;
-    const lds_u8* cur = stage_ptr(it);
-    const int kv0 = it * AKV;
-    qk_half(Sb, cur, 1, qf, lane);
-    if (softmax_half<true>(Sa, pf, m_ref, l_sum, alpha, sc, kv0, M, hh)) rescale_o(o, alpha);
-    pv_half(o, cur + K_BYTES, 0, pf, lane);
-    if (softmax_half<true>(Sb, pf, m_ref, l_sum, alpha, sc, kv0 + 32, M, hh)) rescale_o(o, alpha);
-    pv_half(o, cur + K_BYTES, 1, pf, lane);
-  }
-  wait_vm<0>();
+  region<true, false, false, false>(S0, k_stage(0), o, 0, P1, S1, P1, st, qf, smem, sc, 0, M, lane);
 
-#pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
-    const float l_tot = l_sum[qb] + xor_lane(l_sum[qb], 32);
-    const float inv = 1.0f / l_tot;
-    const int qi = q0 + qb * 32 + r32;
-    if (qi < p.M) {
-      bf16* dst = p.out + (size_t)qi * p.ldo + head * kHeadDim;
-#pragma unroll
-      for (int d = 0; d < 4; ++d)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          bf16x4 v;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) v[e] = f2bf(o[d][qb][4 * g + e] * inv);
-          *reinterpret_cast<bf16x4*>(dst + d * 32 + 8 * g + 4 * hh) = v;
-        }
+  top(0);
+  if (nkv == 1) {
+    region<false, false, true, true>(S1, 0, o, 0, P1, S0, P0, st, qf, smem, sc, 0, M, lane);
+    rescale(o, st);
+    wait_vm<0>();
+    __syncthreads();
+    region<false, true, false, false>(S1, 0, o, v_stage(0), P0, S0, P1, st, qf, smem, sc, 0, M, lane);
+  } else {
+    region<true, false, true, false>(S1, k_stage(1), o, 0, P1, S0, P0, st, qf, smem, sc, 0, M, lane);
+    rescale(o, st);
+    int it = 1;
+    for (; it + 1 < nkv - 1; it += 2) {
+      // it odd: scores in S1, probabilities to P1; then it+1 even
+      top(it);
+      region<true, true, true, false>(S0, k_stage(it + 1), o, v_stage(it - 1), P0, S1, P1, st, qf,
+                                      smem, sc, it * AKV, M, lane);
+      rescale(o, st);
+      top(it + 1);
+      region<true, true, true, false>(S1, k_stage(it + 2), o, v_stage(it), P1, S0, P0, st, qf,
+                                      smem, sc, (it + 1) * AKV, M, lane);
+      rescale(o, st);
     }
+    if (it < nkv - 1) {
+      // it = nkv-2 (odd), then the last tile nkv-1 (even)
+      top(it);
+      region<true, true, true, false>(S0, k_stage(it + 1), o, v_stage(it - 1), P0, S1, P1, st, qf,
+                                      smem, sc, it * AKV, M, lane);
+      rescale(o, st);
+      top(it + 1);
+      region<false, true, true, true>(S1, 0, o, v_stage(it), P1, S0, P0, st, qf, smem, sc,
+                                      (it + 1) * AKV, M, lane);
+      rescale(o, st);
+      wait_vm<0>();
+      __syncthreads();
+      region<false, true, false, false>(S1, 0, o, v_stage(it + 1), P0, S0, P1, st, qf, smem, sc, 0,
+                                        M, lane);
+    } else {
+      // it = nkv-1 (odd) is the last tile
+      top(it);
+      region<false, true, true, true>(S0, 0, o, v_stage(it - 1), P0, S1, P1, st, qf, smem, sc,
+                                      it * AKV, M, lane);
+      rescale(o, st);
+      wait_vm<0>();
+      __syncthreads();
+      region<false, true, false, false>(S0, 0, o, v_stage(it), P1, S1, P0, st, qf, smem, sc, 0, M,
+                                        lane);
+    }
+  }
+
+  const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(st.l_sum),
+                                                   __float_as_uint(st.l_sum), false, false);
+  const float l_tot = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+  const float inv = 1.0f / l_tot;
+  const int qi = q0 + r32;
+  if (qi < M) {
+    bf16* dst = p.out + (size_t)qi * p.ldo + head * kHeadDim;
+#pragma unroll
+    for (int d = 0; d < 4; ++d)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        bf16x4 v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = f2bf(o[d][4 * g + e] * inv);
+        *reinterpret_cast<bf16x4*>(dst + d * 32 + 8 * g + 4 * hh) = v;
+      }
   }
 }
 
 }  // namespace
 
-hipError_t launch_attention(const BlockShape& bs, const WsPtrs& ws,
-                            hipStream_t s) {
+hipError_t launch_attention(const BlockShape& bs, const WsPtrs& ws, hipStream_t s) {
   AttnArgs p;
   p.q = static_cast<const bf16*>(ws.q);
   p.k = static_cast<const bf16*>(ws.k);
@@ -316,7 +406,7 @@ hipError_t launch_attention(const BlockShape& bs, const WsPtrs& ws,
   p.ldo = bs.D + bs.F;
   p.scale_log2 = 1.4426950408889634f / sqrtf((float)kHeadDim);
   const int nqb = (bs.M + AQ - 1) / AQ;
-  hipLaunchKernelGGL(k_attention, dim3(nqb * bs.H), dim3(256), 0, s, p);
+  hipLaunchKernelGGL(k_attention, dim3(nqb * bs.H), dim3(NTHREADS), 0, s, p);
   return hipGetLastError();
 }
 
