@@ -121,7 +121,8 @@ flux3_status flux3_rope_tables_build(const flux3_rope_layout *layout,
                                      void *stream);
 
 /* Workspace bytes block_forward / stack_forward need for n_tokens tokens
- * (about 48 KiB per token at the model dims); 0 if dims are unsupported. */
+ * (about 48 KiB per token at the model dims, plus a fixed 128 MiB of
+ * split-tile partial sums); 0 if dims are unsupported. */
 size_t flux3_workspace_bytes(const flux3_dims *dims, int64_t n_tokens);
 
 /* Byte offsets of the intermediates a block leaves in the workspace, so a
@@ -130,10 +131,12 @@ size_t flux3_workspace_bytes(const flux3_dims *dims, int64_t n_tokens);
  * [heads][n_pad][128]; vt = values bf16 [heads][128][n_pad] with keys
  * permuted inside every 16 (groups of 4 in the order 0, 2, 1, 3); cat =
  * bf16 [n_pad][width + mlp_hidden] holding the attention output in columns
- * [0, width) and silu(gate)*up in [width, width + mlp_hidden).  n_pad is
- * n_tokens rounded up to 256.  Returns FLUX3_E_UNSUPPORTED for bad dims. */
+ * [0, width) and silu(gate)*up in [width, width + mlp_hidden); part =
+ * scratch of the output projection (fp32 partial tiles, 512 x 256 KiB; its
+ * contents after a call are unspecified).  n_pad is n_tokens rounded up to
+ * 256.  Returns FLUX3_E_UNSUPPORTED for bad dims. */
 typedef struct {
-  size_t h, q, k, vt, cat, total;
+  size_t h, q, k, vt, cat, part, total;
   int64_t n_pad;
 } flux3_workspace_layout;
 flux3_status flux3_workspace_layout_get(const flux3_dims *dims, int64_t n_tokens,

@@ -62,8 +62,8 @@ class KernelStats(ctypes.Structure):
 
 class WorkspaceLayout(ctypes.Structure):
     _fields_ = [("h", ctypes.c_size_t), ("q", ctypes.c_size_t), ("k", ctypes.c_size_t),
-                ("vt", ctypes.c_size_t), ("cat", ctypes.c_size_t), ("total", ctypes.c_size_t),
-                ("n_pad", ctypes.c_int64)]
+                ("vt", ctypes.c_size_t), ("cat", ctypes.c_size_t), ("part", ctypes.c_size_t),
+                ("total", ctypes.c_size_t), ("n_pad", ctypes.c_int64)]
 
 
 _lib = None

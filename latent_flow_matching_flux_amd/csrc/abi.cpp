@@ -98,6 +98,8 @@ bool layout_of(const flux3_dims* d, int64_t n, flux3_workspace_layout* L) {
   L->k = off;   off = align_up(off + H * (size_t)n_pad * 128 * 2, kBufAlign);
   L->vt = off;  off = align_up(off + H * 128 * (size_t)n_pad * 2, kBufAlign);
   L->cat = off; off = align_up(off + (size_t)n_pad * (D + F) * 2, kBufAlign);
+  L->part = off; off = align_up(off + 2 * (size_t)flux3::kMaxSplitGroups * flux3::kSplitSlotBytes,
+                                kBufAlign);
   L->total = off;
   return true;
 }
@@ -164,6 +166,7 @@ flux3::WsPtrs carve(void* ws, const flux3_workspace_layout& L) {
   p.k = b + L.k;
   p.vt = b + L.vt;
   p.cat = b + L.cat;
+  p.part = b + L.part;
   return p;
 }
 

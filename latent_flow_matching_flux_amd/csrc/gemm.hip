@@ -156,15 +156,17 @@ __device__ __forceinline__ void read_frag(Frags& f, const lds_u8* As, const lds_
 struct Stream {
   lds_u8* smem;
   Src A, B0, B1;
-  int nk0, nk;
+  int nk0;             // slices [0, nk0) take B rows from B0, later ones from B1
+  int k_begin, nk;     // this call covers slices [k_begin, k_begin + nk)
   int wave, lane, wm, wn;
   // the slice whose loads are spread over the current slice's MFMAs
   int ld_k_a;
   Src ld_b;            // B source of that slice, offset to its k
   uint32_t ld_dst;
 
+  // s counts slices from k_begin
   __device__ __forceinline__ void set_load(int s, int buf) {
-    s = min(s, nk - 1);   // past the end: re-fetch the last slice into a free buffer
+    s = k_begin + min(s, nk - 1);   // past the end: re-fetch the last slice into a free buffer
     ld_dst = (uint32_t)(uintptr_t)(smem + buf * STAGE_BYTES);
     const bool ph0 = s < nk0;
     ld_k_a = s * BK;
@@ -242,13 +244,14 @@ __device__ __forceinline__ void mma_kstep(Stream& st, Frags& cur, Frags& nxt, Ac
   }
 }
 
-// Main loop over k.  Phase 0 covers k slices [0, nk0) with B rows from B0,
-// phase 1 (if nk1 > 0) the next nk1 slices from B1; A runs straight through.
-// A ring of STAGES LDS buffers: while slice kt is consumed, slices up to
-// kt + STAGES - 1 are loading or loaded.
+// Main loop over the k slices [k_begin, k_end) of one tile.  Slices below
+// nk0 take their B rows from B0, the others (from slice nk0 on) from B1; A
+// runs straight through.  A ring of STAGES LDS buffers: while slice kt is
+// consumed, slices up to kt + STAGES - 1 are loading or loaded.  The caller
+// separates two calls on the same LDS with a workgroup barrier.
 __device__ __forceinline__ void gemm_mainloop(lds_u8* smem, Acc& acc, const Src& A,
                                               const Src& B0, int nk0, const Src& B1,
-                                              int nk1) {
+                                              int k_begin, int k_end) {
   static_assert(KSTEPS % 2 == 0, "slices start in the first fragment set");
   static_assert(LOADS_PER_SLICE <= 8 * (KSTEPS - 1), "loads must fit the early k-steps");
   Stream st;
@@ -257,7 +260,8 @@ __device__ __forceinline__ void gemm_mainloop(lds_u8* smem, Acc& acc, const Src&
   st.B0 = B0;
   st.B1 = B1;
   st.nk0 = nk0;
-  st.nk = nk0 + nk1;
+  st.k_begin = k_begin;
+  st.nk = k_end - k_begin;
   st.wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   st.lane = threadIdx.x & 63;
   st.wm = st.wave >> 1;
@@ -365,9 +369,9 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_gemm_proj(ProjArgs p) {
   // exchange with lane ^ 32, and stores are 8 bytes wide.
   Acc acc;
   if (kind == 2)
-    gemm_mainloop(smem, acc, H, W, D / BK, W, 0);
+    gemm_mainloop(smem, acc, H, W, D / BK, W, 0, D / BK);
   else
-    gemm_mainloop(smem, acc, W, H, D / BK, H, 0);
+    gemm_mainloop(smem, acc, W, H, D / BK, H, 0, D / BK);
 
   const int r32 = lane & 31, hi = lane >> 5;
   if (kind < 2) {
@@ -456,36 +460,55 @@ struct OutArgs {
   const bf16 *wo, *wd;
   float* x;
   const float* mod;
+  float* part;       // split-tile partial sums: 2 slots of BM x BN fp32 per workgroup
   SegTable segs;
   int M, n_pad, D, F;
+  int groups;        // persistent workgroups G
+  int dp_rounds;     // whole-tile rounds before the split tail
+  int tail;          // tiles left to the stream-K split (0: none)
 };
 
-__global__ __launch_bounds__(NTHREADS, 1) void k_gemm_out(OutArgs p) {
-  __shared__ __attribute__((aligned(1024))) unsigned char smem_raw[LDS_BYTES];
-  lds_u8* smem = (lds_u8*)smem_raw;
-  const int t = threadIdx.x;
-  const int wave = __builtin_amdgcn_readfirstlane(t >> 6), lane = t & 63;
-  const int wm = wave >> 1, wn = wave & 1;
-  const int D = p.D, F = p.F;
-  const int n_n = D / BN;
-  const int n_m = p.n_pad / BM;
-  int mt, nt;
-  tile_coords(blockIdx.x, n_m, n_n, mt, nt);
-  const int m0 = mt * BM, n0 = nt * BN;
-  const int ldc = D + F;
-  Src A, B0, B1;
-  A.lo = p.cat + (size_t)(m0 + 64 * wave) * ldc;
-  A.hi = A.lo + (size_t)32 * ldc;
-  A.ld = ldc;
-  B0.lo = p.wo + (size_t)(n0 + 64 * wave) * D;
-  B0.hi = B0.lo + (size_t)32 * D;
-  B0.ld = D;
-  B1.lo = p.wd + (size_t)(n0 + 64 * wave) * F;
-  B1.hi = B1.lo + (size_t)32 * F;
-  B1.ld = F;
-  Acc acc;
-  gemm_mainloop(smem, acc, A, B0, D / BK, B1, F / BK);
+// Work split of K4 over G persistent workgroups.  Tiles are numbered in the
+// XCD-grouped order of tile_coords.  The first dp_rounds * G of them go
+// whole, G at a time (the workgroups of one XCD then walk the same k
+// slices of neighbouring tiles together and share them in L2).  The last
+// `tail` tiles, when they would leave most of a round idle, are split
+// stream-K fashion: their k slices, laid end to end (tail tile t owns
+// slices [t nk, (t + 1) nk)), are cut into G equal ranges, range v from
+// start(v) = floor(v total / G).  A tail tile one range covers whole gets
+// its epilogue at once; a tile cut by range boundaries is summed afterwards
+// by the fixup kernel from the partials of its ranges, in k order.  A
+// range's first segment writes slot 2v, its last (when it is another tile)
+// slot 2v + 1.
+struct SplitK {
+  int64_t total;   // tail * nk
+  int G, nk;
+  __device__ __forceinline__ int64_t start(int v) const { return total * v / G; }
+  // range holding slice s
+  __device__ __forceinline__ int range_of(int64_t s) const {
+    return (int)(((s + 1) * G - 1) / total);
+  }
+  __device__ __forceinline__ int slot(int v, int t) const {
+    return 2 * v + (t == (int)(start(v) / nk) ? 0 : 1);
+  }
+};
 
+// Physical workgroup id -> range: the workgroups one XCD runs (every 8th id)
+// take consecutive ranges, so they work on neighbouring tiles.
+__device__ __forceinline__ int range_of_block(int b, int G) {
+  return (G % 8 == 0) ? (b % 8) * (G / 8) + b / 8 : b;
+}
+
+// x[m][n] += gate_s[n] * v for one accumulator value.
+__device__ __forceinline__ void out_update(const OutArgs& p, int m, int n, float v) {
+  const float* gate = p.mod + (size_t)seg_of(p.segs, m) * 3 * p.D + 2 * p.D;
+  p.x[(size_t)m * p.D + n] += gate[n] * v;
+}
+
+// x += gate_s * acc for the tile's live rows.
+__device__ __forceinline__ void out_epilogue(const OutArgs& p, const Acc& acc, int m0, int n0,
+                                             int wm, int wn, int lane) {
+  const int D = p.D;
   const int r32 = lane & 31, hi = lane >> 5;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -501,6 +524,148 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_gemm_out(OutArgs p) {
         xr[n] += gate[n] * acc.c[i][j][e];
       }
     }
+  }
+}
+
+// Partial slot layout: float4 q = 4 (4 i + j) + g of a lane holds
+// acc.c[i][j][4g .. 4g + 3] (4 consecutive rows of one column); lane l of
+// wave w keeps it at float4 index (64 w + q) 64 + l, so each store or load
+// instruction moves 1 KiB contiguously.
+__device__ __forceinline__ float4* slot_base(const OutArgs& p, int slot) {
+  return reinterpret_cast<float4*>(p.part + (size_t)slot * BM * BN);
+}
+
+__device__ __forceinline__ void out_tile_ptrs(const OutArgs& p, int m0, int n0, int wave, Src& A,
+                                              Src& B0, Src& B1) {
+  const int D = p.D, F = p.F, ldc = D + F;
+  A.lo = p.cat + (size_t)(m0 + 64 * wave) * ldc;
+  A.hi = A.lo + (size_t)32 * ldc;
+  A.ld = ldc;
+  B0.lo = p.wo + (size_t)(n0 + 64 * wave) * D;
+  B0.hi = B0.lo + (size_t)32 * D;
+  B0.ld = D;
+  B1.lo = p.wd + (size_t)(n0 + 64 * wave) * F;
+  B1.hi = B1.lo + (size_t)32 * F;
+  B1.ld = F;
+}
+
+__global__ __launch_bounds__(NTHREADS, 1) void k_gemm_out(OutArgs p) {
+  __shared__ __attribute__((aligned(1024))) unsigned char smem_raw[LDS_BYTES];
+  lds_u8* smem = (lds_u8*)smem_raw;
+  const int t = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6), lane = t & 63;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int n_n = p.D / BN;
+  const int n_m = p.n_pad / BM;
+  const int n_tiles = n_m * n_n;
+  const int nk = (p.D + p.F) / BK;
+  const int G = p.groups;
+  bool first = true;
+
+  for (int r = 0; r < p.dp_rounds; ++r) {
+    const int L = r * G + blockIdx.x;
+    if (L >= n_tiles) break;
+    int mt, nt;
+    tile_coords(L, n_m, n_n, mt, nt);
+    Src A, B0, B1;
+    out_tile_ptrs(p, mt * BM, nt * BN, wave, A, B0, B1);
+    if (!first) __syncthreads();   // the previous tile's LDS reads are done
+    first = false;
+    Acc acc;
+    gemm_mainloop(smem, acc, A, B0, p.D / BK, B1, 0, nk);
+    out_epilogue(p, acc, mt * BM, nt * BN, wm, wn, lane);
+  }
+  if (p.tail == 0) return;
+
+  SplitK sk;
+  sk.nk = nk;
+  sk.G = G;
+  sk.total = (int64_t)p.tail * nk;
+  const int tile0 = p.dp_rounds * G;
+  const int v = range_of_block(blockIdx.x, G);
+  const int64_t s_end = sk.start(v + 1);
+  for (int64_t s = sk.start(v); s < s_end;) {
+    const int tt = (int)(s / nk);
+    const int kb = (int)(s - (int64_t)tt * nk);
+    const int ke = (int)min<int64_t>(nk, kb + (s_end - s));
+    int mt, nt;
+    tile_coords(tile0 + tt, n_m, n_n, mt, nt);
+    Src A, B0, B1;
+    out_tile_ptrs(p, mt * BM, nt * BN, wave, A, B0, B1);
+    if (!first) __syncthreads();
+    first = false;
+    Acc acc;
+    gemm_mainloop(smem, acc, A, B0, p.D / BK, B1, kb, ke);
+    if (kb == 0 && ke == nk) {
+      out_epilogue(p, acc, mt * BM, nt * BN, wm, wn, lane);
+    } else {
+      float4* dst = slot_base(p, sk.slot(v, tt)) + (size_t)wave * 64 * 64 + lane;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const f32x16& c = acc.c[i][j];
+            dst[(size_t)(4 * (4 * i + j) + g) * 64] =
+                make_float4(c[4 * g], c[4 * g + 1], c[4 * g + 2], c[4 * g + 3]);
+          }
+    }
+    s += ke - kb;
+  }
+}
+
+constexpr int FIX_SPLIT = 16;   // fixup workgroups per split tile
+
+// Sums the partials of every tail tile cut by a range boundary, in k order,
+// and applies the epilogue.  Workgroups (i, c) look at the boundary between
+// ranges i and i + 1 and take part c of its tile if no earlier boundary
+// falls inside the tile; a thread handles one float4 of the slot layout.
+__global__ __launch_bounds__(NTHREADS) void k_gemm_out_fixup(OutArgs p) {
+  const int n_n = p.D / BN;
+  const int n_m = p.n_pad / BM;
+  SplitK sk;
+  sk.nk = (p.D + p.F) / BK;
+  sk.G = p.groups;
+  sk.total = (int64_t)p.tail * sk.nk;
+  const int i = blockIdx.x / FIX_SPLIT, chunk = blockIdx.x % FIX_SPLIT;
+  const int64_t b = sk.start(i + 1);
+  if (b % sk.nk == 0) return;                       // boundary on a tile edge
+  const int tt = (int)(b / sk.nk);
+  if (sk.start(i) > (int64_t)tt * sk.nk) return;    // an earlier boundary owns the tile
+  const int v_first = sk.range_of((int64_t)tt * sk.nk);
+  const int v_last = sk.range_of((int64_t)(tt + 1) * sk.nk - 1);
+
+  // float4 index inside the slot: (64 w + q) 64 + l
+  const int f = chunk * (BM * BN / 4 / FIX_SPLIT) + threadIdx.x;
+  float4 sum[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) sum[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int v = v_first; v <= v_last; ++v) {
+    if (sk.start(v + 1) == sk.start(v)) continue;   // empty range (fewer slices than ranges)
+    const float4* src = slot_base(p, sk.slot(v, tt)) + f;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const float4 x = src[u * NTHREADS];
+      sum[u].x += x.x;
+      sum[u].y += x.y;
+      sum[u].z += x.z;
+      sum[u].w += x.w;
+    }
+  }
+  int mt, nt;
+  tile_coords(p.dp_rounds * p.groups + tt, n_m, n_n, mt, nt);
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int idx = f + u * NTHREADS;
+    const int l = idx & 63, q = (idx >> 6) & 63, w = idx >> 12;
+    const int ij = q >> 2, g = q & 3, ii = ij >> 2, jj = ij & 3;
+    const int m = mt * BM + (w >> 1) * 128 + ii * 32 + 8 * g + 4 * (l >> 5);
+    const int n = nt * BN + (w & 1) * 128 + jj * 32 + (l & 31);
+    const float vals[4] = {sum[u].x, sum[u].y, sum[u].z, sum[u].w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (m + e < p.M) out_update(p, m + e, n, vals[e]);
   }
 }
 
@@ -535,6 +700,20 @@ hipError_t launch_gemm_proj(const BlockShape& bs, const BlockWeightsDev& w,
   return hipGetLastError();
 }
 
+int stream_k_groups() {
+  static int groups[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return kMaxSplitGroups;
+  if (groups[dev] == 0) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus <= 0)
+      cus = kMaxSplitGroups;
+    groups[dev] = cus < kMaxSplitGroups ? cus : kMaxSplitGroups;
+  }
+  return groups[dev];
+}
+
 hipError_t launch_gemm_out(const BlockShape& bs, const BlockWeightsDev& w,
                            const WsPtrs& ws, float* x, const float* mod,
                            const SegTableHost& segs, hipStream_t s) {
@@ -544,15 +723,28 @@ hipError_t launch_gemm_out(const BlockShape& bs, const BlockWeightsDev& w,
   p.wd = static_cast<const bf16*>(w.w_down);
   p.x = x;
   p.mod = mod;
+  p.part = static_cast<float*>(ws.part);
   for (int i = 0; i < kMaxSegs; ++i) p.segs.start[i] = segs.start[i];
   p.segs.n = segs.n;
   p.M = bs.M;
   p.n_pad = bs.n_pad;
   p.D = bs.D;
   p.F = bs.F;
-  const int n_n = bs.D / BN;
-  const int n_m = bs.n_pad / BM;
-  hipLaunchKernelGGL(k_gemm_out, dim3(n_m * n_n), dim3(NTHREADS), 0, s, p);
+  p.groups = stream_k_groups();
+  const int n_tiles = (bs.n_pad / BM) * (bs.D / BN);
+  const int G = p.groups;
+  p.dp_rounds = n_tiles / G;
+  p.tail = n_tiles % G;
+  // a tail filling most of a round runs whole (its tiles keep sharing L2);
+  // a thin one is spread over all workgroups
+  if (p.tail * 10 > G * 7) {
+    p.dp_rounds += 1;
+    p.tail = 0;
+  }
+  hipLaunchKernelGGL(k_gemm_out, dim3(G), dim3(NTHREADS), 0, s, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || p.tail == 0 || G < 2) return e;
+  hipLaunchKernelGGL(k_gemm_out_fixup, dim3((G - 1) * FIX_SPLIT), dim3(NTHREADS), 0, s, p);
   return hipGetLastError();
 }
 

@@ -31,7 +31,13 @@ struct WsPtrs {
   void* k;    // bf16 [H][n_pad][128]
   void* vt;   // bf16 [H][128][n_pad]
   void* cat;  // bf16 [n_pad][D + F]
+  void* part; // fp32 [2 kMaxSplitGroups][256 * 256]: split-tile partials of K4
 };
+
+// Upper bound on the persistent workgroups of the stream-K output GEMM (one
+// per CU, at most this many); the workspace holds two partial tiles for each.
+constexpr int kMaxSplitGroups = 256;
+constexpr size_t kSplitSlotBytes = 256 * 256 * 4;
 
 struct BlockWeightsDev {
   const void *wq, *wk, *wv, *wo, *w_gate, *w_up, *w_down;
@@ -48,6 +54,7 @@ hipError_t launch_gemm_proj(const BlockShape& bs, const BlockWeightsDev& w,
                             hipStream_t s);
 hipError_t launch_attention(const BlockShape& bs, const WsPtrs& ws,
                             hipStream_t s);
+int stream_k_groups();
 hipError_t launch_gemm_out(const BlockShape& bs, const BlockWeightsDev& w,
                            const WsPtrs& ws, float* x, const float* mod,
                            const SegTableHost& segs, hipStream_t s);

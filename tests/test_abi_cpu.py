@@ -64,14 +64,16 @@ def _call_block(dims=None, w=None, x=FAKE, n=336, segs=((0, 80, 0), (80, 256, 1)
 def test_workspace_bytes_formula():
     d = synth.DIMS
     per_tok = (d.width + 3 * d.width + d.width + d.mlp_hidden) * 2   # h, q, k, vt, cat in bf16
+    part = 2 * 256 * 256 * 256 * 4        # two fp32 256x256 partial tiles per stream-K group
     for n in (1, 7, 256, 336, 8432, 65776):
         n_pad = (n + 255) // 256 * 256
-        assert F.workspace_bytes(d, n) == n_pad * per_tok
+        assert F.workspace_bytes(d, n) == n_pad * per_tok + part
     assert F.workspace_bytes(synth.Dims(3072, 24, 64, 9216), 10) == 0
     lay = F.workspace_layout(d, 8432)
     assert lay.n_pad == 8448 and lay.total == F.workspace_bytes(d, 8432)
-    assert lay.h == 0 and lay.q < lay.k < lay.vt < lay.cat < lay.total
-    assert all(off % 256 == 0 for off in (lay.q, lay.k, lay.vt, lay.cat))
+    assert lay.h == 0 and lay.q < lay.k < lay.vt < lay.cat < lay.part < lay.total
+    assert lay.total - lay.part == part
+    assert all(off % 256 == 0 for off in (lay.q, lay.k, lay.vt, lay.cat, lay.part))
 
 
 def test_layout_tokens():
