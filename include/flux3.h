@@ -127,11 +127,15 @@ size_t flux3_workspace_bytes(const flux3_dims *dims, int64_t n_tokens);
 
 /* Byte offsets of the intermediates a block leaves in the workspace, so a
  * caller can inspect them after the call: h = modulated LayerNorm output
- * bf16 [n_pad][width]; q, k = RMS-normalised, rotated queries/keys bf16
- * [heads][n_pad][128]; vt = values bf16 [heads][128][n_pad] with keys
- * permuted inside every 16 (groups of 4 in the order 0, 2, 1, 3); cat =
- * bf16 [n_pad][width + mlp_hidden] holding the attention output in columns
- * [0, width) and silu(gate)*up in [width, width + mlp_hidden); part =
+ * bf16 [n_pad][width], packed (below); q, k = RMS-normalised, rotated
+ * queries/keys bf16 [heads][n_pad][128]; vt = values bf16 [heads][128][n_pad]
+ * with keys permuted inside every 16 (groups of 4 in the order 0, 2, 1, 3);
+ * cat = bf16 [n_pad][width + mlp_hidden], packed, holding the attention
+ * output in columns [0, width) and silu(gate)*up in [width, width +
+ * mlp_hidden).  Packed: a [R][K] matrix is stored as 1-KiB blocks of 8 rows
+ * x 64 columns, block (r/8, c/64) at block index (r/8)*(K/64) + c/64; in a
+ * block, row r%8 takes 128 bytes whose 16-byte chunk j (columns 8j..8j+7 of
+ * the block) sits at chunk position j ^ ((r/2)%8).  part =
  * scratch of the output projection (fp32 partial tiles, 512 x 256 KiB; its
  * contents after a call are unspecified).  n_pad is n_tokens rounded up to
  * 256.  Returns FLUX3_E_UNSUPPORTED for bad dims. */

@@ -58,7 +58,7 @@ typedef const __attribute__((address_space(3))) bf16x8 lds_frag;
 
 struct AttnArgs {
   const bf16 *q, *k, *vt;
-  bf16* out;         // cat buffer, row stride ldo
+  bf16* out;         // cat buffer, packed operand layout of width ldo
   int M, n_pad, H, ldo;
   float scale_log2;  // log2(e) / sqrt(head_dim)
 };
@@ -379,7 +379,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_attention(AttnArgs p) {
   const float inv = 1.0f / l_tot;
   const int qi = q0 + r32;
   if (qi < M) {
-    bf16* dst = p.out + (size_t)qi * p.ldo + head * kHeadDim;
+    // the concatenation buffer is in the packed operand layout
 #pragma unroll
     for (int d = 0; d < 4; ++d)
 #pragma unroll
@@ -387,7 +387,8 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_attention(AttnArgs p) {
         bf16x4 v;
 #pragma unroll
         for (int e = 0; e < 4; ++e) v[e] = f2bf(o[d][4 * g + e] * inv);
-        *reinterpret_cast<bf16x4*>(dst + d * 32 + 8 * g + 4 * hh) = v;
+        const int col = head * kHeadDim + d * 32 + 8 * g + 4 * hh;
+        *reinterpret_cast<bf16x4*>(p.out + packed_index(qi, col, p.ldo)) = v;
       }
   }
 }

@@ -42,6 +42,19 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
 __device__ __forceinline__ float bf2f(bf16 v) { return (float)v; }
 __device__ __forceinline__ bf16 f2bf(float v) { return (bf16)v; }  // RNE
 
+// Packed operand layout of the bf16 activations the GEMMs read (the
+// modulated LayerNorm output and the attention / SwiGLU concatenation).  A
+// row-major [R][K] matrix (R % 8 == 0, K % 64 == 0) is stored as 1-KiB
+// blocks of 8 rows x 64 k-values, block (row / 8, k / 64) at block index
+// (row / 8) * (K / 64) + k / 64.  Inside a block row r8 = row % 8 takes 128
+// bytes, and its 16-byte chunk c (k-values 8c .. 8c + 7 of the block) sits
+// in slot c ^ ((row / 2) % 8) -- the XOR swizzle the GEMM keeps in LDS -- so
+// one 64-lane global->LDS load moves a whole block from contiguous memory.
+__host__ __device__ __forceinline__ size_t packed_index(size_t row, int k, int K) {
+  return ((((row >> 3) * (size_t)(K >> 6)) + (size_t)(k >> 6)) << 9) + ((row & 7) << 6) +
+         ((size_t)(((k >> 3) & 7) ^ ((int)(row >> 1) & 7)) << 3) + (size_t)(k & 7);
+}
+
 // Cross-lane exchange inside a wave (ds_bpermute based).
 __device__ __forceinline__ float xor_lane(float v, int mask) {
   return __shfl_xor(v, mask, kWave);

@@ -67,6 +67,8 @@ constexpr int LOADS_PER_OP = 64 / ROWS_PER_KB;         // 1-KiB blocks per wave 
 constexpr int LOADS_PER_SLICE = 2 * LOADS_PER_OP;      // per wave
 constexpr int KSTEPS = BK / 16;
 static_assert(LDS_BYTES <= 160 * 1024, "LDS ring too large");
+static_assert(BK == 64 && SWZ_DIV == 2 && CPR == 8,
+              "the packed operand layout holds 64-wide k blocks with this swizzle");
 static_assert(CPR >= 4 && ROWS_PER_KB <= 16, "slice geometry");
 static_assert((STAGES - 1) * LOADS_PER_SLICE <= 63, "vmcnt range");
 
@@ -91,9 +93,11 @@ __device__ __forceinline__ void tile_coords(int b, int n_m, int n_n, int& mt,
 }
 
 // Where this wave's share of one operand tile comes from: wave w loads tile
-// rows [64w, 64w + 64), i.e. the 32-row runs 2w (lo) and 2w + 1 (hi); each
-// run has a wave-uniform base pointer (its first row at k = 0) and all rows
-// share the stride ld.
+// rows [64w, 64w + 64).  Row-major operand: the 32-row runs 2w (lo) and
+// 2w + 1 (hi) each have a wave-uniform base pointer (first row, k = 0) and
+// all rows share the stride ld.  Packed operand: lo is the first of the 8
+// 8-row blocks at k = 0 (row 64w's row-major offset, row * K), ld the
+// stride between 8-row blocks (8 K); hi is unused.
 struct Src {
   const bf16* lo;
   const bf16* hi;
@@ -121,15 +125,30 @@ __device__ __forceinline__ void wait_vm() {
 
 // The i-th of this wave's direct loads for one slice (A blocks first, then
 // B): LOADS_PER_OP 1-KiB blocks per operand, rows [64w, 64w + 64) of the tile.
-template <int I>
-__device__ __forceinline__ void issue_load(const Src& S, int k, uint32_t dst, int wave,
+// A row-major operand (P false) fetches each lane's chunk from its row with
+// the LDS swizzle applied; a packed one (P true) already holds 1-KiB blocks
+// in LDS order, so lane l fetches bytes [16 l, 16 l + 16) of its block.
+// koff is the slice's k offset in elements of the operand's layout.
+template <int I, bool P>
+__device__ __forceinline__ void issue_load(const Src& S, int koff, uint32_t dst, int wave,
                                            int lane) {
   constexpr int i = I % LOADS_PER_OP;
-  const int rsub = lane / CPR, slot = lane % CPR;
-  const int rr = i * ROWS_PER_KB + rsub;                 // row within this wave's 64
-  const int c = slot ^ ((rr / SWZ_DIV) % CPR);
-  const bf16* g = (i * ROWS_PER_KB < 32 ? S.lo : S.hi) + (rr & 31) * S.ld + k + c * 8;
+  const bf16* g;
+  if constexpr (P) {
+    g = S.lo + i * S.ld + koff + lane * 8;
+  } else {
+    const int rsub = lane / CPR, slot = lane % CPR;
+    const int rr = i * ROWS_PER_KB + rsub;                 // row within this wave's 64
+    const int c = slot ^ ((rr / SWZ_DIV) % CPR);
+    g = (i * ROWS_PER_KB < 32 ? S.lo : S.hi) + (rr & 31) * S.ld + koff + c * 8;
+  }
   dma16(g, dst + (uint32_t)((64 * wave + i * ROWS_PER_KB) * ROW_BYTES));
+}
+
+// Element offset of k (a multiple of BK) in a row-major or packed operand.
+template <bool P>
+__device__ __forceinline__ int k_offset(int k) {
+  return P ? k * 8 : k;
 }
 
 struct Frags {
@@ -153,6 +172,7 @@ __device__ __forceinline__ void read_frag(Frags& f, const lds_u8* As, const lds_
 // Everything is held by value (wave-uniform values in scalar registers): a
 // pointer to a stack copy would be spilled and re-read from scratch, and
 // that read's wait would also wait for every direct load in flight.
+template <bool PA, bool PB>
 struct Stream {
   lds_u8* smem;
   Src A, B0, B1;
@@ -169,8 +189,8 @@ struct Stream {
     s = k_begin + min(s, nk - 1);   // past the end: re-fetch the last slice into a free buffer
     ld_dst = (uint32_t)(uintptr_t)(smem + buf * STAGE_BYTES);
     const bool ph0 = s < nk0;
-    ld_k_a = s * BK;
-    const int kb = ph0 ? s * BK : (s - nk0) * BK;
+    ld_k_a = k_offset<PA>(s * BK);
+    const int kb = k_offset<PB>(ph0 ? s * BK : (s - nk0) * BK);
     ld_b.lo = (ph0 ? B0.lo : B1.lo) + kb;
     ld_b.hi = (ph0 ? B0.hi : B1.hi) + kb;
     ld_b.ld = ph0 ? B0.ld : B1.ld;
@@ -178,9 +198,9 @@ struct Stream {
   template <int I>
   __device__ __forceinline__ void load() const {
     if constexpr (I < LOADS_PER_OP)
-      issue_load<I>(A, ld_k_a, ld_dst, wave, lane);
+      issue_load<I, PA>(A, ld_k_a, ld_dst, wave, lane);
     else
-      issue_load<I>(ld_b, 0, ld_dst + OP_BYTES, wave, lane);
+      issue_load<I, PB>(ld_b, 0, ld_dst + OP_BYTES, wave, lane);
   }
   template <int... I>
   __device__ __forceinline__ void load_all(std::integer_sequence<int, I...>) const {
@@ -195,8 +215,8 @@ struct Stream {
 // MFMA number IDX (block i = IDX/4, j = IDX%4) of a k-step, followed by at
 // most one memory instruction, then a scheduling barrier so that the exact
 // order (one memory op issued in the shadow of each MFMA) is kept.
-template <int KK, int IDX>
-__device__ __forceinline__ void kstep_op(const Stream& st, const Frags& cur, Frags& nxt, Acc& acc,
+template <int KK, int IDX, class ST>
+__device__ __forceinline__ void kstep_op(const ST& st, const Frags& cur, Frags& nxt, Acc& acc,
                                          const lds_u8* As, const lds_u8* Bs, int kk_next) {
   constexpr int i = IDX / 4, j = IDX % 4;
   acc.c[i][j] = mfma32(cur.a[i], cur.b[j], acc.c[i][j]);
@@ -211,8 +231,8 @@ __device__ __forceinline__ void kstep_op(const Stream& st, const Frags& cur, Fra
   __builtin_amdgcn_sched_barrier(0);
 }
 
-template <int KK, int... IDX>
-__device__ __forceinline__ void kstep_ops(const Stream& st, const Frags& cur, Frags& nxt,
+template <int KK, class ST, int... IDX>
+__device__ __forceinline__ void kstep_ops(const ST& st, const Frags& cur, Frags& nxt,
                                           Acc& acc, const lds_u8* As, const lds_u8* Bs,
                                           int kk_next, std::integer_sequence<int, IDX...>) {
   (kstep_op<KK, IDX>(st, cur, nxt, acc, As, Bs, kk_next), ...);
@@ -225,8 +245,8 @@ __device__ __forceinline__ void kstep_ops(const Stream& st, const Frags& cur, Fr
 // other waves at the workgroup barrier -- after which slice kt's buffer is
 // free and slice kt + 1 is complete -- then reads slice kt + 1's first
 // fragments during its last 8 MFMAs.
-template <int KK>
-__device__ __forceinline__ void mma_kstep(Stream& st, Frags& cur, Frags& nxt, Acc& acc, int kt,
+template <int KK, class ST>
+__device__ __forceinline__ void mma_kstep(ST& st, Frags& cur, Frags& nxt, Acc& acc, int kt,
                                           int buf, int buf_next) {
   if constexpr (KK + 1 < KSTEPS) {
     kstep_ops<KK>(st, cur, nxt, acc, st.a_buf(buf), st.b_buf(buf), KK + 1,
@@ -244,17 +264,19 @@ __device__ __forceinline__ void mma_kstep(Stream& st, Frags& cur, Frags& nxt, Ac
   }
 }
 
-// Main loop over the k slices [k_begin, k_end) of one tile.  Slices below
+// Main loop over the k slices [k_begin, k_end) of one tile; PA / PB say
+// whether A / B are in the packed operand layout.  Slices below
 // nk0 take their B rows from B0, the others (from slice nk0 on) from B1; A
 // runs straight through.  A ring of STAGES LDS buffers: while slice kt is
 // consumed, slices up to kt + STAGES - 1 are loading or loaded.  The caller
 // separates two calls on the same LDS with a workgroup barrier.
+template <bool PA, bool PB>
 __device__ __forceinline__ void gemm_mainloop(lds_u8* smem, Acc& acc, const Src& A,
                                               const Src& B0, int nk0, const Src& B1,
                                               int k_begin, int k_end) {
   static_assert(KSTEPS % 2 == 0, "slices start in the first fragment set");
   static_assert(LOADS_PER_SLICE <= 8 * (KSTEPS - 1), "loads must fit the early k-steps");
-  Stream st;
+  Stream<PA, PB> st;
   st.smem = smem;
   st.A = A;
   st.B0 = B0;
@@ -355,10 +377,10 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_gemm_proj(ProjArgs p) {
     const bf16* W = blk < 2 ? p.wg : p.wu;
     return W + (size_t)(hid0 + 64 * half + 32 * (blk & 1)) * D;
   };
-  Src H, W;
+  Src H, W;   // h is packed, the weights row-major
   H.lo = p.h + (size_t)(m0 + 64 * wave) * D;
-  H.hi = H.lo + (size_t)32 * D;
-  H.ld = D;
+  H.hi = H.lo;
+  H.ld = 8 * D;
   W.lo = w_run(2 * wave);
   W.hi = w_run(2 * wave + 1);
   W.ld = D;
@@ -369,19 +391,27 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_gemm_proj(ProjArgs p) {
   // exchange with lane ^ 32, and stores are 8 bytes wide.
   Acc acc;
   if (kind == 2)
-    gemm_mainloop(smem, acc, H, W, D / BK, W, 0, D / BK);
+    gemm_mainloop<true, false>(smem, acc, H, W, D / BK, W, 0, D / BK);
   else
-    gemm_mainloop(smem, acc, W, H, D / BK, H, 0, D / BK);
+    gemm_mainloop<false, true>(smem, acc, W, H, D / BK, H, 0, D / BK);
 
   const int r32 = lane & 31, hi = lane >> 5;
+  // The output tile is staged in LDS (free once every wave is past the main
+  // loop) so that the global stores are whole 16-byte chunks of contiguous
+  // rows.  Staged rows are 256 B (queries, keys, SwiGLU: one token's 128
+  // features) or 512 B (values: one dim's 256 tokens); chunk c of staged
+  // row r sits in slot c ^ (r % 16) or c ^ (r % 32) respectively, which
+  // spreads the lanes' 8-byte writes over the LDS banks.
+  typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+  typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+  __syncthreads();
   if (kind < 2) {
     // per-head RMSNorm + RoPE: this wave holds head head0 + wm for 128 tokens
-    const int head = head0 + wm;
     const float* nw = kind == 0 ? p.qn : p.kn;
-    bf16* dst = (kind == 0 ? p.q : p.k) + (size_t)head * p.n_pad * kHeadDim;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int m = m0 + wn * 128 + j * 32 + r32;
+      const int t = wn * 128 + j * 32 + r32;             // token within the tile
+      const int m = m0 + t;
       const bool live = m < p.M;
       float ss = 0.f;
 #pragma unroll
@@ -407,37 +437,58 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_gemm_proj(ProjArgs p) {
           o[1] = f2bf(live ? x0 * cs.y + x1 * cs.x : 0.f);
           o[2] = f2bf(live ? x2 * cs.z - x3 * cs.w : 0.f);
           o[3] = f2bf(live ? x2 * cs.w + x3 * cs.z : 0.f);
-          *reinterpret_cast<bf16x4*>(dst + (size_t)m * kHeadDim + d0) = o;
+          const int chunk = 4 * i + g;
+          *(lds_bf16x4*)(smem + wm * 65536 + t * 256 + ((chunk ^ (t & 15)) << 4) + 8 * hi) = o;
         }
     }
+    __syncthreads();
+    // 2 heads x 256 tokens of 256 B; a store instruction covers 4 rows (1 KiB
+    // contiguous in the head-major output)
+    bf16* out = kind == 0 ? p.q : p.k;
+#pragma unroll 4
+    for (int it = 0; it < 32; ++it) {
+      const int row = wave * 128 + it * 4 + (lane >> 4), chunk = lane & 15;
+      const int t = row & 255;
+      const u32x4 v = *(lds_u32x4*)(smem + row * 256 + ((chunk ^ (t & 15)) << 4));
+      bf16* dst = out + ((size_t)(head0 + (row >> 8)) * p.n_pad + m0 + t) * kHeadDim + chunk * 8;
+      *reinterpret_cast<u32x4*>(dst) = v;
+    }
   } else if (kind == 2) {
-    // values, transposed: vt[head][d][pos(m)], 4 consecutive tokens per store
-    const int head = head0 + wn;
-    bf16* dst = p.vt + (size_t)head * kHeadDim * p.n_pad;
+    // values, transposed: staged as [head][dim][256 token positions]
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const int mb = m0 + wm * 128 + i * 32 + 8 * g + 4 * hi;
+        const int mb = wm * 128 + i * 32 + 8 * g + 4 * hi;   // first of 4 tokens, tile-local
+        const int pos = vt_pos(mb);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const int d = j * 32 + r32;
+          const int r = wn * 128 + j * 32 + r32;             // head-local dim row
           bf16x4 v;
 #pragma unroll
           for (int e = 0; e < 4; ++e)
-            v[e] = f2bf(mb + e < p.M ? acc.c[i][j][4 * g + e] : 0.f);
-          *reinterpret_cast<bf16x4*>(dst + (size_t)d * p.n_pad + vt_pos(mb)) = v;
+            v[e] = f2bf(m0 + mb + e < p.M ? acc.c[i][j][4 * g + e] : 0.f);
+          *(lds_bf16x4*)(smem + r * 512 + (((pos >> 3) ^ (r & 31)) << 4) + (pos & 7) * 2) = v;
         }
       }
     }
+    __syncthreads();
+    // 256 rows (2 heads x 128 dims) of 512 B; a store covers 2 rows
+#pragma unroll 4
+    for (int it = 0; it < 32; ++it) {
+      const int row = wave * 64 + it * 2 + (lane >> 5), chunk = lane & 31;
+      const u32x4 v = *(lds_u32x4*)(smem + row * 512 + ((chunk ^ (row & 31)) << 4));
+      bf16* dst = p.vt + ((size_t)(head0 + (row >> 7)) * kHeadDim + (row & 127)) * p.n_pad + m0 +
+                  chunk * 8;
+      *reinterpret_cast<u32x4*>(dst) = v;
+    }
   } else {
-    // SwiGLU: register blocks 0,1 are gate rows, 2,3 the matching up rows
-    const int ldc = D + p.F;
+    // SwiGLU: register blocks 0,1 are gate rows, 2,3 the matching up rows;
+    // staged as [token][128 hidden units]
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int m = m0 + wn * 128 + j * 32 + r32;
-      const bool live = m < p.M;
-      bf16* dst = p.cat + (size_t)m * ldc + D + hid0 + 64 * wm;
+      const int t = wn * 128 + j * 32 + r32;
+      const bool live = m0 + t < p.M;
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -449,8 +500,20 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_gemm_proj(ProjArgs p) {
             const float a = gt * __builtin_amdgcn_rcpf(1.0f + __expf(-gt)) * up;
             o[e] = f2bf(live ? a : 0.f);
           }
-          *reinterpret_cast<bf16x4*>(dst + 32 * i + 8 * g + 4 * hi) = o;
+          const int chunk = 8 * wm + 4 * i + g;
+          *(lds_bf16x4*)(smem + t * 256 + ((chunk ^ (t & 15)) << 4) + 8 * hi) = o;
         }
+    }
+    __syncthreads();
+    // 256 token rows of 256 B; a store covers 4 rows, each 16-byte chunk to
+    // its slot of the packed concatenation
+    const int ldc = D + p.F;
+#pragma unroll 4
+    for (int it = 0; it < 16; ++it) {
+      const int t = wave * 64 + it * 4 + (lane >> 4), chunk = lane & 15;
+      const u32x4 v = *(lds_u32x4*)(smem + t * 256 + ((chunk ^ (t & 15)) << 4));
+      bf16* dst = p.cat + packed_index(m0 + t, D + hid0 + chunk * 8, ldc);
+      *reinterpret_cast<u32x4*>(dst) = v;
     }
   }
 }
@@ -538,9 +601,9 @@ __device__ __forceinline__ float4* slot_base(const OutArgs& p, int slot) {
 __device__ __forceinline__ void out_tile_ptrs(const OutArgs& p, int m0, int n0, int wave, Src& A,
                                               Src& B0, Src& B1) {
   const int D = p.D, F = p.F, ldc = D + F;
-  A.lo = p.cat + (size_t)(m0 + 64 * wave) * ldc;
-  A.hi = A.lo + (size_t)32 * ldc;
-  A.ld = ldc;
+  A.lo = p.cat + (size_t)(m0 + 64 * wave) * ldc;   // packed
+  A.hi = A.lo;
+  A.ld = 8 * ldc;
   B0.lo = p.wo + (size_t)(n0 + 64 * wave) * D;
   B0.hi = B0.lo + (size_t)32 * D;
   B0.ld = D;
@@ -572,7 +635,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_gemm_out(OutArgs p) {
     if (!first) __syncthreads();   // the previous tile's LDS reads are done
     first = false;
     Acc acc;
-    gemm_mainloop(smem, acc, A, B0, p.D / BK, B1, 0, nk);
+    gemm_mainloop<true, false>(smem, acc, A, B0, p.D / BK, B1, 0, nk);
     out_epilogue(p, acc, mt * BM, nt * BN, wm, wn, lane);
   }
   if (p.tail == 0) return;
@@ -595,7 +658,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_gemm_out(OutArgs p) {
     if (!first) __syncthreads();
     first = false;
     Acc acc;
-    gemm_mainloop(smem, acc, A, B0, p.D / BK, B1, kb, ke);
+    gemm_mainloop<true, false>(smem, acc, A, B0, p.D / BK, B1, kb, ke);
     if (kb == 0 && ke == nk) {
       out_epilogue(p, acc, mt * BM, nt * BN, wm, wn, lane);
     } else {

@@ -6,7 +6,8 @@
 // the Diffusers release post, everytik.com translation):
 //   h = (1 + scale_s) * (x - mean) / sqrt(var + eps) + shift_s
 // Statistics are fp32 over the row (biased variance, two passes over
-// registers); h is written as bf16, the GEMM operand type.
+// registers); h is written as bf16, the GEMM operand type, in the packed
+// operand layout (1-KiB blocks of 8 rows x 64 k, chunks swizzled).
 //
 // One wave per row; each lane holds width/64 values.  HBM-bound: reads 4 B
 // and writes 2 B per element (the modulation vectors stay in cache).
@@ -48,7 +49,6 @@ __global__ __launch_bounds__(256) void k_ln_modulate(
   const int sg = seg_of(segs, row);
   const float4* shift = reinterpret_cast<const float4*>(mod + (size_t)sg * 3 * D);
   const float4* scale = shift + D / 4;
-  bf16x4* hr = reinterpret_cast<bf16x4*>(h + (size_t)row * D);
 #pragma unroll
   for (int i = 0; i < V; ++i) {
     const int c = lane + 64 * i;
@@ -58,7 +58,7 @@ __global__ __launch_bounds__(256) void k_ln_modulate(
     o[1] = f2bf((1.0f + sc.y) * ((v[i].y - mean) * rstd) + sh.y);
     o[2] = f2bf((1.0f + sc.z) * ((v[i].z - mean) * rstd) + sh.z);
     o[3] = f2bf((1.0f + sc.w) * ((v[i].w - mean) * rstd) + sh.w);
-    hr[c] = o;
+    *reinterpret_cast<bf16x4*>(h + packed_index(row, 4 * c, D)) = o;
   }
 }
 
@@ -85,8 +85,7 @@ __global__ __launch_bounds__(256) void k_ln_modulate_any(
   const float* shift = mod + (size_t)sg * 3 * D;
   const float* scale = shift + D;
   for (int c = lane; c < D; c += 64)
-    h[(size_t)row * D + c] =
-        f2bf((1.0f + scale[c]) * ((xr[c] - mean) * rstd) + shift[c]);
+    h[packed_index(row, c, D)] = f2bf((1.0f + scale[c]) * ((xr[c] - mean) * rstd) + shift[c]);
 }
 
 hipError_t launch_ln_modulate(const BlockShape& bs, const float* x,

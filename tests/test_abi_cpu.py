@@ -10,6 +10,7 @@ import os
 import re
 import subprocess
 
+import numpy as np
 import pytest
 
 import latent_flow_matching_flux_amd as F
@@ -189,3 +190,16 @@ def test_binding_has_no_cpu_fallback(tmp_path):
             L.load(str(tmp_path / "missing.so"))
     finally:
         L._lib = saved
+
+
+def test_packed_layout_reader():
+    from layouts import unpack_rows, pack_rows_loops
+    rng = np.random.default_rng(0)
+    for R, K in ((8, 64), (16, 128), (24, 192)):
+        x = rng.standard_normal((R, K)).astype(np.float32)
+        p = pack_rows_loops(x)
+        # every 1-KiB block (512 bf16 values) holds 8 whole rows of 64 k-values
+        blk = p.reshape(-1, 512)
+        assert blk.shape[0] == (R // 8) * (K // 64)
+        assert np.array_equal(np.sort(blk[0]), np.sort(x[:8, :64].ravel()))
+        assert np.array_equal(unpack_rows(p, R, K), x)

@@ -14,6 +14,7 @@ from oracle import flux3_oracle as O
 
 pytestmark = pytest.mark.gpu
 
+from layouts import unpack_rows  # noqa: E402
 from gpu_util import (DEV, assert_close, assert_close_bf16, assert_close_stack,  # noqa: E402
                       bf16_to_np, rope_dev, seg_tuples, upload_weights, vt_unpermute,
                       workspace)
@@ -102,12 +103,12 @@ def test_block336_intermediates_and_output(norm_stress):
     def view(off, shape):
         nel = int(np.prod(shape))
         return bf16_to_np(ws[off:off + 2 * nel].view(torch.bfloat16).reshape(shape))
-    h = view(L.h, (n_pad, D))[:n]
+    h = unpack_rows(view(L.h, (n_pad * D,)), n_pad, D)[:n]
     q = view(L.q, (H, n_pad, 128))[:, :n].transpose(1, 0, 2)
     k = view(L.k, (H, n_pad, 128))[:, :n].transpose(1, 0, 2)
     vt = vt_unpermute(view(L.vt, (H, 128, n_pad)), n)
     v = vt.transpose(2, 0, 1)
-    cat = view(L.cat, (n_pad, D + Fh))[:n]
+    cat = unpack_rows(view(L.cat, (n_pad * (D + Fh),)), n_pad, D + Fh)[:n]
     assert_close_bf16(h, inter["h"], "K1 h")
     assert_close_bf16(q, inter["q"], "K2 q (RMSNorm+RoPE)")
     assert_close_bf16(k, inter["k"], "K2 k (RMSNorm+RoPE)")
