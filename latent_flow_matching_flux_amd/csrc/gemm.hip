@@ -35,42 +35,36 @@ constexpr int BM = 256, BN = 256;
 constexpr int NTHREADS = 256;
 constexpr int GROUP_M = 8;
 
-#ifndef FLUX3_GEMM_BK
-#define FLUX3_GEMM_BK 64
-#endif
-#ifndef FLUX3_GEMM_STAGES
-#define FLUX3_GEMM_STAGES 2
-#endif
-constexpr int BK = FLUX3_GEMM_BK;        // k depth of one LDS slice
-constexpr int STAGES = FLUX3_GEMM_STAGES;  // LDS ring: STAGES - 1 slices in flight
+constexpr int BK = 64;                   // k depth of one LDS slice
 
 typedef __attribute__((address_space(3))) unsigned char lds_u8;
 typedef __attribute__((address_space(3))) void lds_void;
 typedef const __attribute__((address_space(1))) void gvoid;
 
-// Geometry of one k-slice in LDS.  Tile row r (256 rows per operand)
-// occupies ROW_BYTES contiguous bytes, no padding; its 16-byte chunk c sits
-// in slot c ^ ((r / SWZ_DIV) % CPR), where SWZ_DIV rows span one 256-byte
-// bank cycle.  With 64 banks this keeps the MFMA fragment reads (32
-// consecutive rows, one chunk, per half-wave) conflict-free, and lets each
-// wave fill whole 1-KiB blocks with direct global->LDS loads: lane l of a
-// block writes slot l % CPR of row l / CPR, so it fetches chunk
+// Geometry of one operand's k-slice in LDS.  Tile row r (256 rows per
+// operand) occupies ROW_BYTES contiguous bytes, no padding; its 16-byte
+// chunk c sits in slot c ^ ((r / SWZ_DIV) % CPR), where SWZ_DIV rows span
+// one 256-byte bank cycle.  With 64 banks this keeps the MFMA fragment
+// reads (32 consecutive rows, one chunk, per half-wave) conflict-free, and
+// lets each wave fill whole 1-KiB blocks with direct global->LDS loads:
+// lane l of a block writes slot l % CPR of row l / CPR, so it fetches chunk
 // (l % CPR) ^ swizzle(row).
 constexpr int ROW_BYTES = BK * 2;
 constexpr int CPR = ROW_BYTES / 16;
 constexpr int ROWS_PER_KB = 1024 / ROW_BYTES;
 constexpr int SWZ_DIV = 256 / ROW_BYTES;
-constexpr int OP_BYTES = BM * ROW_BYTES;
-constexpr int STAGE_BYTES = 2 * OP_BYTES;              // A then B
-constexpr int LDS_BYTES = STAGES * STAGE_BYTES;
-constexpr int LOADS_PER_OP = 64 / ROWS_PER_KB;         // 1-KiB blocks per wave per operand
-constexpr int LOADS_PER_SLICE = 2 * LOADS_PER_OP;      // per wave
+constexpr int OP_BYTES = BM * ROW_BYTES;               // one operand's slice: 32 KiB
+// Each operand has its own ring of slices.  The one streaming the weights
+// (row-major, 8 rows per load, often from beyond L2) keeps 3 buffers, so its
+// loads run two slices ahead; the packed activation keeps 2 (one ahead).
+constexpr int DEEP_STAGES = 3, SHALLOW_STAGES = 2;
+constexpr int LDS_BYTES = (DEEP_STAGES + SHALLOW_STAGES) * OP_BYTES;
+constexpr int LOADS_PER_OP = 64 / ROWS_PER_KB;         // 1-KiB blocks per wave per operand slice
 constexpr int KSTEPS = BK / 16;
-static_assert(LDS_BYTES <= 160 * 1024, "LDS ring too large");
+static_assert(LDS_BYTES <= 160 * 1024, "LDS rings too large");
 static_assert(BK == 64 && SWZ_DIV == 2 && CPR == 8,
               "the packed operand layout holds 64-wide k blocks with this swizzle");
-static_assert(CPR >= 4 && ROWS_PER_KB <= 16, "slice geometry");
-static_assert((STAGES - 1) * LOADS_PER_SLICE <= 63, "vmcnt range");
+static_assert(LOADS_PER_OP == 8 && KSTEPS == 4, "load schedule: 8 loads in each of k-steps 0 and 1");
 
 struct Acc {
   f32x16 c[4][4];
@@ -172,49 +166,81 @@ __device__ __forceinline__ void read_frag(Frags& f, const lds_u8* As, const lds_
 // Everything is held by value (wave-uniform values in scalar registers): a
 // pointer to a stack copy would be spilled and re-read from scratch, and
 // that read's wait would also wait for every direct load in flight.
-template <bool PA, bool PB>
+// DEEP_B: B is the weight operand (3-slice ring), A the activation (2);
+// otherwise the other way round.
+template <bool PA, bool PB, bool DEEP_B>
 struct Stream {
+  static constexpr int SA = DEEP_B ? SHALLOW_STAGES : DEEP_STAGES;
+  static constexpr int SB = DEEP_B ? DEEP_STAGES : SHALLOW_STAGES;
+  static constexpr int B_BASE = SA * OP_BYTES;
   lds_u8* smem;
+  uint32_t lds0;       // LDS byte address of smem
   Src A, B0, B1;
   int nk0;             // slices [0, nk0) take B rows from B0, later ones from B1
   int k_begin, nk;     // this call covers slices [k_begin, k_begin + nk)
   int wave, lane, wm, wn;
-  // the slice whose loads are spread over the current slice's MFMAs
+  // the next A and B slices to load, spread over the current slice's MFMAs
   int ld_k_a;
+  uint32_t ld_dst_a;
   Src ld_b;            // B source of that slice, offset to its k
-  uint32_t ld_dst;
+  uint32_t ld_dst_b;
 
-  // s counts slices from k_begin
-  __device__ __forceinline__ void set_load(int s, int buf) {
-    s = k_begin + min(s, nk - 1);   // past the end: re-fetch the last slice into a free buffer
-    ld_dst = (uint32_t)(uintptr_t)(smem + buf * STAGE_BYTES);
-    const bool ph0 = s < nk0;
+  // s counts slices from k_begin; past the end the last slice is re-fetched
+  // into a free buffer
+  __device__ __forceinline__ void set_load_a(int s) {
+    ld_dst_a = lds0 + (uint32_t)((s % SA) * OP_BYTES);
+    s = k_begin + min(s, nk - 1);
     ld_k_a = k_offset<PA>(s * BK);
+  }
+  __device__ __forceinline__ void set_load_b(int s) {
+    ld_dst_b = lds0 + (uint32_t)(B_BASE + (s % SB) * OP_BYTES);
+    s = k_begin + min(s, nk - 1);
+    const bool ph0 = s < nk0;
     const int kb = k_offset<PB>(ph0 ? s * BK : (s - nk0) * BK);
     ld_b.lo = (ph0 ? B0.lo : B1.lo) + kb;
     ld_b.hi = (ph0 ? B0.hi : B1.hi) + kb;
     ld_b.ld = ph0 ? B0.ld : B1.ld;
   }
+  __device__ __forceinline__ void set_load_shallow(int s) {
+    if constexpr (DEEP_B) set_load_a(s); else set_load_b(s);
+  }
+  __device__ __forceinline__ void set_load_deep(int s) {
+    if constexpr (DEEP_B) set_load_b(s); else set_load_a(s);
+  }
+  // load I of the shallow (first) or deep (second) operand's pending slice
   template <int I>
-  __device__ __forceinline__ void load() const {
-    if constexpr (I < LOADS_PER_OP)
-      issue_load<I, PA>(A, ld_k_a, ld_dst, wave, lane);
+  __device__ __forceinline__ void load_shallow() const {
+    if constexpr (DEEP_B)
+      issue_load<I, PA>(A, ld_k_a, ld_dst_a, wave, lane);
     else
-      issue_load<I, PB>(ld_b, 0, ld_dst + OP_BYTES, wave, lane);
+      issue_load<I, PB>(ld_b, 0, ld_dst_b, wave, lane);
+  }
+  template <int I>
+  __device__ __forceinline__ void load_deep() const {
+    if constexpr (DEEP_B)
+      issue_load<I, PB>(ld_b, 0, ld_dst_b, wave, lane);
+    else
+      issue_load<I, PA>(A, ld_k_a, ld_dst_a, wave, lane);
   }
   template <int... I>
-  __device__ __forceinline__ void load_all(std::integer_sequence<int, I...>) const {
-    (load<I>(), ...);
+  __device__ __forceinline__ void load_shallow_all(std::integer_sequence<int, I...>) const {
+    (load_shallow<I>(), ...);
   }
-  __device__ __forceinline__ const lds_u8* a_buf(int buf) const { return smem + buf * STAGE_BYTES; }
-  __device__ __forceinline__ const lds_u8* b_buf(int buf) const {
-    return smem + buf * STAGE_BYTES + OP_BYTES;
+  template <int... I>
+  __device__ __forceinline__ void load_deep_all(std::integer_sequence<int, I...>) const {
+    (load_deep<I>(), ...);
+  }
+  __device__ __forceinline__ const lds_u8* a_buf(int s) const { return smem + (s % SA) * OP_BYTES; }
+  __device__ __forceinline__ const lds_u8* b_buf(int s) const {
+    return smem + B_BASE + (s % SB) * OP_BYTES;
   }
 };
 
 // MFMA number IDX (block i = IDX/4, j = IDX%4) of a k-step, followed by at
 // most one memory instruction, then a scheduling barrier so that the exact
-// order (one memory op issued in the shadow of each MFMA) is kept.
+// order (one memory op issued in the shadow of each MFMA) is kept.  MFMAs
+// 8..15 of k-step 0 carry the shallow operand's 8 loads of the pending
+// slice, those of k-step 1 the deep operand's.
 template <int KK, int IDX, class ST>
 __device__ __forceinline__ void kstep_op(const ST& st, const Frags& cur, Frags& nxt, Acc& acc,
                                          const lds_u8* As, const lds_u8* Bs, int kk_next) {
@@ -223,8 +249,8 @@ __device__ __forceinline__ void kstep_op(const ST& st, const Frags& cur, Frags& 
   constexpr bool last = KK == KSTEPS - 1;
   if constexpr (!last) {
     if constexpr (IDX < 8) read_frag<IDX>(nxt, As, Bs, st.wm, st.wn, st.lane, kk_next);
-    constexpr int dma = (IDX - 8) + 8 * KK;      // MFMAs 8..15 of early k-steps carry loads
-    if constexpr (IDX >= 8 && dma < LOADS_PER_SLICE) st.template load<dma>();
+    if constexpr (IDX >= 8 && KK == 0) st.template load_shallow<IDX - 8>();
+    if constexpr (IDX >= 8 && KK == 1) st.template load_deep<IDX - 8>();
   } else {
     if constexpr (IDX >= 8) read_frag<IDX - 8>(nxt, As, Bs, st.wm, st.wn, st.lane, 0);
   }
@@ -238,46 +264,47 @@ __device__ __forceinline__ void kstep_ops(const ST& st, const Frags& cur, Frags&
   (kstep_op<KK, IDX>(st, cur, nxt, acc, As, Bs, kk_next), ...);
 }
 
-// k-step KK of slice kt (LDS buffer buf).  Early k-steps read the next
-// k-step's fragments during their first 8 MFMAs and carry the direct loads
-// of slice kt + STAGES - 1 during the other 8.  The last k-step runs 8
-// MFMAs, waits for slice kt + 1 to have landed (for this wave) and meets the
-// other waves at the workgroup barrier -- after which slice kt's buffer is
-// free and slice kt + 1 is complete -- then reads slice kt + 1's first
-// fragments during its last 8 MFMAs.
+// k-step KK of slice kt.  Early k-steps read the next k-step's fragments
+// during their first 8 MFMAs and carry direct loads during the other 8
+// (the shallow operand's slice kt + 1, the deep operand's slice kt + 2).
+// The last k-step runs 8 MFMAs, waits until only the deep operand's loads
+// of this slice are in flight (so both operands' slice kt + 1 has landed
+// for this wave) and meets the other waves at the workgroup barrier --
+// after which slice kt's buffers are free and slice kt + 1 is complete --
+// then reads slice kt + 1's first fragments during its last 8 MFMAs.
 template <int KK, class ST>
-__device__ __forceinline__ void mma_kstep(ST& st, Frags& cur, Frags& nxt, Acc& acc, int kt,
-                                          int buf, int buf_next) {
+__device__ __forceinline__ void mma_kstep(ST& st, Frags& cur, Frags& nxt, Acc& acc, int kt) {
   if constexpr (KK + 1 < KSTEPS) {
-    kstep_ops<KK>(st, cur, nxt, acc, st.a_buf(buf), st.b_buf(buf), KK + 1,
+    kstep_ops<KK>(st, cur, nxt, acc, st.a_buf(kt), st.b_buf(kt), KK + 1,
                   std::make_integer_sequence<int, 16>{});
-    mma_kstep<KK + 1>(st, nxt, cur, acc, kt, buf, buf_next);
+    mma_kstep<KK + 1>(st, nxt, cur, acc, kt);
   } else {
-    kstep_ops<KK>(st, cur, nxt, acc, st.a_buf(buf), st.b_buf(buf), 0,
+    kstep_ops<KK>(st, cur, nxt, acc, st.a_buf(kt), st.b_buf(kt), 0,
                   std::integer_sequence<int, 0, 1, 2, 3, 4, 5, 6, 7>{});
-    wait_vm<(STAGES - 2) * LOADS_PER_SLICE>();
+    wait_vm<LOADS_PER_OP>();
     __syncthreads();
-    // slice kt's buffer is free from here on: it takes slice kt + STAGES
-    st.set_load(kt + STAGES, buf);
-    kstep_ops<KK>(st, cur, nxt, acc, st.a_buf(buf_next), st.b_buf(buf_next), 0,
+    // slice kt's buffers are free from here on
+    st.set_load_shallow(kt + SHALLOW_STAGES);
+    st.set_load_deep(kt + DEEP_STAGES);
+    kstep_ops<KK>(st, cur, nxt, acc, st.a_buf(kt + 1), st.b_buf(kt + 1), 0,
                   std::integer_sequence<int, 8, 9, 10, 11, 12, 13, 14, 15>{});
   }
 }
 
 // Main loop over the k slices [k_begin, k_end) of one tile; PA / PB say
-// whether A / B are in the packed operand layout.  Slices below
-// nk0 take their B rows from B0, the others (from slice nk0 on) from B1; A
-// runs straight through.  A ring of STAGES LDS buffers: while slice kt is
-// consumed, slices up to kt + STAGES - 1 are loading or loaded.  The caller
-// separates two calls on the same LDS with a workgroup barrier.
-template <bool PA, bool PB>
+// whether A / B are in the packed operand layout, DEEP_B whether B (else A)
+// is the weight operand with the deeper ring.  Slices below nk0 take their
+// B rows from B0, the others (from slice nk0 on) from B1; A runs straight
+// through.  The caller separates two calls on the same LDS with a workgroup
+// barrier.
+template <bool PA, bool PB, bool DEEP_B>
 __device__ __forceinline__ void gemm_mainloop(lds_u8* smem, Acc& acc, const Src& A,
                                               const Src& B0, int nk0, const Src& B1,
                                               int k_begin, int k_end) {
   static_assert(KSTEPS % 2 == 0, "slices start in the first fragment set");
-  static_assert(LOADS_PER_SLICE <= 8 * (KSTEPS - 1), "loads must fit the early k-steps");
-  Stream<PA, PB> st;
+  Stream<PA, PB, DEEP_B> st;
   st.smem = smem;
+  st.lds0 = (uint32_t)(uintptr_t)smem;
   st.A = A;
   st.B0 = B0;
   st.B1 = B1;
@@ -295,30 +322,31 @@ __device__ __forceinline__ void gemm_mainloop(lds_u8* smem, Acc& acc, const Src&
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc.c[i][j][e] = 0.f;
 
-  // prologue: slices 0 .. STAGES-2 in flight, slice STAGES-1 rides on slice 0
-#pragma unroll
-  for (int s = 0; s < STAGES - 1; ++s) {
-    st.set_load(s, s);
-    st.load_all(std::make_integer_sequence<int, LOADS_PER_SLICE>{});
-  }
-  st.set_load(STAGES - 1, STAGES - 1);
-  wait_vm<(STAGES - 2) * LOADS_PER_SLICE>();
+  // prologue: shallow slice 0, deep slices 0 and 1; shallow slice 1 and deep
+  // slice 2 ride on slice 0
+  const auto seq = std::make_integer_sequence<int, LOADS_PER_OP>{};
+  st.set_load_shallow(0);
+  st.load_shallow_all(seq);
+  st.set_load_deep(0);
+  st.load_deep_all(seq);
+  st.set_load_deep(1);
+  st.load_deep_all(seq);
+  st.set_load_shallow(1);
+  st.set_load_deep(2);
+  wait_vm<LOADS_PER_OP>();
   __syncthreads();
   Frags f0, f1;
-  read_frag<0>(f0, st.a_buf(0), st.b_buf(0), st.wm, st.wn, st.lane, 0);
-  read_frag<1>(f0, st.a_buf(0), st.b_buf(0), st.wm, st.wn, st.lane, 0);
-  read_frag<2>(f0, st.a_buf(0), st.b_buf(0), st.wm, st.wn, st.lane, 0);
-  read_frag<3>(f0, st.a_buf(0), st.b_buf(0), st.wm, st.wn, st.lane, 0);
-  read_frag<4>(f0, st.a_buf(0), st.b_buf(0), st.wm, st.wn, st.lane, 0);
-  read_frag<5>(f0, st.a_buf(0), st.b_buf(0), st.wm, st.wn, st.lane, 0);
-  read_frag<6>(f0, st.a_buf(0), st.b_buf(0), st.wm, st.wn, st.lane, 0);
-  read_frag<7>(f0, st.a_buf(0), st.b_buf(0), st.wm, st.wn, st.lane, 0);
-  int buf = 0;
-  for (int kt = 0; kt < st.nk; ++kt) {
-    const int buf_next = buf + 1 == STAGES ? 0 : buf + 1;
-    mma_kstep<0>(st, f0, f1, acc, kt, buf, buf_next);
-    buf = buf_next;
-  }
+  const lds_u8* a0 = st.a_buf(0);
+  const lds_u8* b0 = st.b_buf(0);
+  read_frag<0>(f0, a0, b0, st.wm, st.wn, st.lane, 0);
+  read_frag<1>(f0, a0, b0, st.wm, st.wn, st.lane, 0);
+  read_frag<2>(f0, a0, b0, st.wm, st.wn, st.lane, 0);
+  read_frag<3>(f0, a0, b0, st.wm, st.wn, st.lane, 0);
+  read_frag<4>(f0, a0, b0, st.wm, st.wn, st.lane, 0);
+  read_frag<5>(f0, a0, b0, st.wm, st.wn, st.lane, 0);
+  read_frag<6>(f0, a0, b0, st.wm, st.wn, st.lane, 0);
+  read_frag<7>(f0, a0, b0, st.wm, st.wn, st.lane, 0);
+  for (int kt = 0; kt < st.nk; ++kt) mma_kstep<0>(st, f0, f1, acc, kt);
   // the re-fetches issued by the last iterations must land before the
   // workgroup can release its LDS
   wait_vm<0>();
@@ -391,9 +419,9 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_gemm_proj(ProjArgs p) {
   // exchange with lane ^ 32, and stores are 8 bytes wide.
   Acc acc;
   if (kind == 2)
-    gemm_mainloop<true, false>(smem, acc, H, W, D / BK, W, 0, D / BK);
+    gemm_mainloop<true, false, true>(smem, acc, H, W, D / BK, W, 0, D / BK);
   else
-    gemm_mainloop<false, true>(smem, acc, W, H, D / BK, H, 0, D / BK);
+    gemm_mainloop<false, true, false>(smem, acc, W, H, D / BK, H, 0, D / BK);
 
   const int r32 = lane & 31, hi = lane >> 5;
   // The output tile is staged in LDS (free once every wave is past the main
@@ -635,7 +663,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_gemm_out(OutArgs p) {
     if (!first) __syncthreads();   // the previous tile's LDS reads are done
     first = false;
     Acc acc;
-    gemm_mainloop<true, false>(smem, acc, A, B0, p.D / BK, B1, 0, nk);
+    gemm_mainloop<true, false, true>(smem, acc, A, B0, p.D / BK, B1, 0, nk);
     out_epilogue(p, acc, mt * BM, nt * BN, wm, wn, lane);
   }
   if (p.tail == 0) return;
@@ -658,7 +686,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_gemm_out(OutArgs p) {
     if (!first) __syncthreads();
     first = false;
     Acc acc;
-    gemm_mainloop<true, false>(smem, acc, A, B0, p.D / BK, B1, kb, ke);
+    gemm_mainloop<true, false, true>(smem, acc, A, B0, p.D / BK, B1, kb, ke);
     if (kb == 0 && ke == nk) {
       out_epilogue(p, acc, mt * BM, nt * BN, wm, wn, lane);
     } else {
