@@ -28,6 +28,7 @@
 // a tile's max exceeds it by more than TAU, so exp2(s - m) <= 2^TAU and fp32
 // / bf16 never overflow.  Keys past the sequence end are masked in the last
 // tile (the workspace pads them with zeros).
+#include <algorithm>
 #include <type_traits>
 
 #include "common.hpp"
@@ -59,9 +60,35 @@ typedef const __attribute__((address_space(3))) bf16x8 lds_frag;
 struct AttnArgs {
   const bf16 *q, *k, *vt;
   bf16* out;         // cat buffer, packed operand layout of width ldo
+  float* part;       // partial-result slots of split query blocks (256 KiB each)
   int M, n_pad, H, ldo;
   float scale_log2;  // log2(e) / sqrt(head_dim)
+  int groups;        // persistent workgroups G
+  int dp_rounds;     // whole-unit rounds before the split tail
+  int tail;          // units left to the split (0: none)
+  int tail_ranges;   // ranges the tail's key tiles are cut into (<= G)
 };
+
+// A unit of work is one (head, 256-query block); unit L maps to it so that
+// the units an XCD runs (L % 8 equal) share heads and keep K and V in that
+// XCD's L2.
+__device__ __forceinline__ void unit_coords(int L, int nqb, int H, int& head, int& qblk) {
+  if (H % 8 == 0) {
+    const int xcd = L & 7, idx = L >> 3;
+    head = xcd * (H / 8) + idx / nqb;
+    qblk = idx % nqb;
+  } else {
+    head = L / nqb;
+    qblk = L % nqb;
+  }
+}
+
+// Partial result of a split unit, in a 256-KiB slot: O (unnormalised, fp32)
+// as float4 (wave, d, g, lane) at float4 index (16 wave + 4 d + g) 64 + lane
+// -- registers o[d][4g .. 4g + 3] of that lane -- then the reference max
+// m and the key sum l of query 32 wave + r at floats 32768 + (32 wave + r)
+// and 33024 + (32 wave + r).
+constexpr int PART_M = 32768, PART_L = 33024;
 
 template <int B, int E, class F>
 __device__ __forceinline__ void static_for(F&& f) {
@@ -254,49 +281,37 @@ __device__ __forceinline__ void rescale(f32x16 (&o)[4], const SoftState& st) {
   }
 }
 
-__global__ __launch_bounds__(NTHREADS, 1) void k_attention(AttnArgs p) {
-  __shared__ __attribute__((aligned(1024))) unsigned char smem_raw[LDS_BYTES];
-  const lds_u8* smem = (const lds_u8*)smem_raw;
-  const uint32_t lds0 = (uint32_t)(uintptr_t)smem_raw;
+// Attention of one unit (head, query block qblk) over key tiles
+// [t0, t0 + nt): normalised into the concatenation buffer when slot is
+// null, else the unnormalised O with its m and l into the slot.
+__device__ __forceinline__ void attend(const AttnArgs& p, const lds_u8* smem, uint32_t lds0,
+                                       int head, int qblk, int t0, int nt, float* slot) {
   const int t = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6), lane = t & 63;
   const int r32 = lane & 31, hh = lane >> 5;
-
-  // workgroup -> (head, query block); the workgroups an XCD runs (every 8th
-  // id) share heads so K and V stay in that XCD's L2
-  const int nqb = (p.M + AQ - 1) / AQ;
-  int head, qblk;
-  if (p.H % 8 == 0) {
-    const int b = blockIdx.x, xcd = b & 7, idx = b >> 3;
-    const int hpx = p.H / 8;
-    head = xcd * hpx + idx / nqb;
-    qblk = idx % nqb;
-  } else {
-    head = blockIdx.x / nqb;
-    qblk = blockIdx.x % nqb;
-  }
   const int q0 = qblk * AQ + wave * QW;
   const bf16* qh = p.q + (size_t)head * p.n_pad * kHeadDim;
   const bf16* kh = p.k + (size_t)head * p.n_pad * kHeadDim;
   const bf16* vh = p.vt + (size_t)head * kHeadDim * p.n_pad;
-  const int nkv = (p.M + AKV - 1) / AKV;
   const int M = p.M;
   const float sc = p.scale_log2;
+  const int kbase = t0 * AKV;   // first key of the range
 
   bf16x8 qf[8];
 #pragma unroll
   for (int ks = 0; ks < 8; ++ks)
     qf[ks] = *reinterpret_cast<const bf16x8*>(qh + (size_t)(q0 + r32) * kHeadDim + ks * 16 + hh * 8);
 
-  // DMA group g (issued at the top of tile g): K tile g+4 and V^T tile g+2,
-  // indices clamped to the last tile; the prologue issues groups -4..-1.
+  // DMA group g (issued at the top of tile g of the range): K tile g+4 and
+  // V^T tile g+2, indices clamped to the range; the prologue issues groups
+  // -4..-1.
   const DmaLanes dl = dma_lanes(p.n_pad, wave, lane);
   auto k_stage = [](int tile) { return (uint32_t)((tile & (NSTAGE - 1)) * K_BYTES); };
   auto v_stage = [](int tile) { return (uint32_t)(V_RING + (tile & (NSTAGE - 1)) * V_BYTES); };
   auto issue_group = [&](int g) {
     const int kt = g + 4, vt = g + 2;
-    issue_k(kh, min(kt, nkv - 1) * AKV, lds0 + k_stage(kt), dl, wave);
-    issue_v(vh, max(0, min(vt, nkv - 1)) * AKV, lds0 + v_stage(vt), dl, wave);
+    issue_k(kh, kbase + min(kt, nt - 1) * AKV, lds0 + k_stage(kt), dl, wave);
+    issue_v(vh, kbase + max(0, min(vt, nt - 1)) * AKV, lds0 + v_stage(vt), dl, wave);
   };
 #pragma unroll
   for (int g = -4; g < 0; ++g) issue_group(g);
@@ -324,47 +339,50 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_attention(AttnArgs p) {
   __syncthreads();
   region<true, false, false, false>(S0, k_stage(0), o, 0, P1, S1, P1, st, qf, smem, sc, 0, M, lane);
 
+  // the range's last tile runs with the key mask (a no-op unless it is the
+  // sequence's last tile)
   top(0);
-  if (nkv == 1) {
-    region<false, false, true, true>(S1, 0, o, 0, P1, S0, P0, st, qf, smem, sc, 0, M, lane);
+  if (nt == 1) {
+    region<false, false, true, true>(S1, 0, o, 0, P1, S0, P0, st, qf, smem, sc, kbase, M, lane);
     rescale(o, st);
     wait_vm<0>();
     __syncthreads();
     region<false, true, false, false>(S1, 0, o, v_stage(0), P0, S0, P1, st, qf, smem, sc, 0, M, lane);
   } else {
-    region<true, false, true, false>(S1, k_stage(1), o, 0, P1, S0, P0, st, qf, smem, sc, 0, M, lane);
+    region<true, false, true, false>(S1, k_stage(1), o, 0, P1, S0, P0, st, qf, smem, sc, kbase, M,
+                                     lane);
     rescale(o, st);
     int it = 1;
-    for (; it + 1 < nkv - 1; it += 2) {
+    for (; it + 1 < nt - 1; it += 2) {
       // it odd: scores in S1, probabilities to P1; then it+1 even
       top(it);
       region<true, true, true, false>(S0, k_stage(it + 1), o, v_stage(it - 1), P0, S1, P1, st, qf,
-                                      smem, sc, it * AKV, M, lane);
+                                      smem, sc, kbase + it * AKV, M, lane);
       rescale(o, st);
       top(it + 1);
       region<true, true, true, false>(S1, k_stage(it + 2), o, v_stage(it), P1, S0, P0, st, qf,
-                                      smem, sc, (it + 1) * AKV, M, lane);
+                                      smem, sc, kbase + (it + 1) * AKV, M, lane);
       rescale(o, st);
     }
-    if (it < nkv - 1) {
-      // it = nkv-2 (odd), then the last tile nkv-1 (even)
+    if (it < nt - 1) {
+      // it = nt-2 (odd), then the last tile nt-1 (even)
       top(it);
       region<true, true, true, false>(S0, k_stage(it + 1), o, v_stage(it - 1), P0, S1, P1, st, qf,
-                                      smem, sc, it * AKV, M, lane);
+                                      smem, sc, kbase + it * AKV, M, lane);
       rescale(o, st);
       top(it + 1);
       region<false, true, true, true>(S1, 0, o, v_stage(it), P1, S0, P0, st, qf, smem, sc,
-                                      (it + 1) * AKV, M, lane);
+                                      kbase + (it + 1) * AKV, M, lane);
       rescale(o, st);
       wait_vm<0>();
       __syncthreads();
       region<false, true, false, false>(S1, 0, o, v_stage(it + 1), P0, S0, P1, st, qf, smem, sc, 0,
                                         M, lane);
     } else {
-      // it = nkv-1 (odd) is the last tile
+      // it = nt-1 (odd) is the last tile
       top(it);
       region<false, true, true, true>(S0, 0, o, v_stage(it - 1), P0, S1, P1, st, qf, smem, sc,
-                                      it * AKV, M, lane);
+                                      kbase + it * AKV, M, lane);
       rescale(o, st);
       wait_vm<0>();
       __syncthreads();
@@ -376,6 +394,20 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_attention(AttnArgs p) {
   const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(st.l_sum),
                                                    __float_as_uint(st.l_sum), false, false);
   const float l_tot = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+  if (slot) {
+    float4* so = reinterpret_cast<float4*>(slot) + (size_t)wave * 16 * 64 + lane;
+#pragma unroll
+    for (int d = 0; d < 4; ++d)
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+        so[(4 * d + g) * 64] = make_float4(o[d][4 * g], o[d][4 * g + 1], o[d][4 * g + 2],
+                                           o[d][4 * g + 3]);
+    if (hh == 0) {
+      slot[PART_M + wave * 32 + r32] = st.m_ref;
+      slot[PART_L + wave * 32 + r32] = l_tot;
+    }
+    return;
+  }
   const float inv = 1.0f / l_tot;
   const int qi = q0 + r32;
   if (qi < M) {
@@ -393,6 +425,130 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_attention(AttnArgs p) {
   }
 }
 
+// Persistent workgroups: dp_rounds rounds of whole units (G at a time),
+// then, if the leftover units would leave most of a round idle, their key
+// tiles split evenly over tail_ranges ranges (SplitK: one unit = its nkv key
+// tiles).  A unit a range covers whole is finished at once; the partial
+// results of a unit cut by range boundaries go to slots that
+// k_attention_fixup merges.
+__global__ __launch_bounds__(NTHREADS, 1) void k_attention(AttnArgs p) {
+  __shared__ __attribute__((aligned(1024))) unsigned char smem_raw[LDS_BYTES];
+  const lds_u8* smem = (const lds_u8*)smem_raw;
+  const uint32_t lds0 = (uint32_t)(uintptr_t)smem_raw;
+  const int nqb = (p.M + AQ - 1) / AQ;
+  const int nkv = (p.M + AKV - 1) / AKV;
+  const int units = nqb * p.H;
+  const int G = p.groups;
+  // the tail range of this workgroup (empty without a tail)
+  SplitK sk;
+  sk.nk = nkv;
+  sk.G = p.tail_ranges > 0 ? p.tail_ranges : 1;
+  sk.total = (int64_t)p.tail * nkv;
+  const int v = range_of_block(blockIdx.x, G);
+  int64_t s = 0, s_end = 0;
+  if (p.tail > 0 && v < sk.G) {
+    s = sk.start(v);
+    s_end = sk.start(v + 1);
+  }
+  const int unit0 = p.dp_rounds * G;
+  // one loop over this workgroup's work items -- whole units, then tail
+  // segments -- so that the unit body is instantiated once
+  int r = 0;
+  bool first = true;
+  for (;;) {
+    int head, qblk, t0, nt;
+    float* slot = nullptr;
+    if (r < p.dp_rounds && r * G + (int)blockIdx.x < units) {
+      unit_coords(r * G + blockIdx.x, nqb, p.H, head, qblk);
+      t0 = 0;
+      nt = nkv;
+      ++r;
+    } else if (s < s_end) {
+      r = p.dp_rounds;
+      const int u = (int)(s / nkv);
+      const int kb = (int)(s - (int64_t)u * nkv);
+      const int ke = (int)min<int64_t>(nkv, kb + (s_end - s));
+      unit_coords(unit0 + u, nqb, p.H, head, qblk);
+      t0 = kb;
+      nt = ke - kb;
+      if (nt != nkv) slot = p.part + (size_t)sk.slot(v, u) * 65536;
+      s += nt;
+    } else {
+      break;
+    }
+    if (!first) __syncthreads();   // the previous item's LDS reads are done
+    first = false;
+    attend(p, smem, lds0, head, qblk, t0, nt, slot);
+  }
+}
+
+// Merges the partial results of every tail unit cut by a range boundary, in
+// range (key) order: m = max m_i, O = sum 2^(m_i - m) O_i, l = sum 2^(m_i -
+// m) l_i, out = O / l.  Workgroup i looks at the boundary between ranges i
+// and i + 1 and takes its unit if no earlier boundary falls inside it; a
+// thread handles the registers one attention lane held.
+__global__ __launch_bounds__(NTHREADS) void k_attention_fixup(AttnArgs p) {
+  const int nqb = (p.M + AQ - 1) / AQ;
+  const int nkv = (p.M + AKV - 1) / AKV;
+  SplitK sk;
+  sk.nk = nkv;
+  sk.G = p.tail_ranges;
+  sk.total = (int64_t)p.tail * nkv;
+  const int i = blockIdx.x;
+  const int64_t b = sk.start(i + 1);
+  if (b % nkv == 0) return;                        // boundary on a unit edge
+  const int u = (int)(b / nkv);
+  if (sk.start(i) > (int64_t)u * nkv) return;      // an earlier boundary owns the unit
+  const int v_first = sk.range_of((int64_t)u * nkv);
+  const int v_last = sk.range_of((int64_t)(u + 1) * nkv - 1);
+  const int t = threadIdx.x;
+  const int wave = t >> 6, lane = t & 63, r32 = lane & 31, hh = lane >> 5;
+  const int qw = wave * 32 + r32;                  // query within the unit
+
+  float m = -INFINITY;
+  for (int v = v_first; v <= v_last; ++v) {
+    if (sk.start(v + 1) == sk.start(v)) continue;   // empty range
+    m = fmaxf(m, p.part[(size_t)sk.slot(v, u) * 65536 + PART_M + qw]);
+  }
+  float4 acc[16];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) acc[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+  float l = 0.f;
+  for (int v = v_first; v <= v_last; ++v) {
+    if (sk.start(v + 1) == sk.start(v)) continue;
+    const float* slot = p.part + (size_t)sk.slot(v, u) * 65536;
+    const float w = __builtin_amdgcn_exp2f(slot[PART_M + qw] - m);
+    l += w * slot[PART_L + qw];
+    const float4* so = reinterpret_cast<const float4*>(slot) + (size_t)wave * 16 * 64 + lane;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const float4 x = so[j * 64];
+      acc[j].x += w * x.x;
+      acc[j].y += w * x.y;
+      acc[j].z += w * x.z;
+      acc[j].w += w * x.w;
+    }
+  }
+  int head, qblk;
+  unit_coords(p.dp_rounds * p.groups + u, nqb, p.H, head, qblk);
+  const int qi = qblk * AQ + qw;
+  if (qi >= p.M) return;
+  const float inv = 1.0f / l;
+#pragma unroll
+  for (int d = 0; d < 4; ++d)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const float4 x = acc[4 * d + g];
+      bf16x4 v;
+      v[0] = f2bf(x.x * inv);
+      v[1] = f2bf(x.y * inv);
+      v[2] = f2bf(x.z * inv);
+      v[3] = f2bf(x.w * inv);
+      const int col = head * kHeadDim + d * 32 + 8 * g + 4 * hh;
+      *reinterpret_cast<bf16x4*>(p.out + packed_index(qi, col, p.ldo)) = v;
+    }
+}
+
 }  // namespace
 
 hipError_t launch_attention(const BlockShape& bs, const WsPtrs& ws, hipStream_t s) {
@@ -401,13 +557,34 @@ hipError_t launch_attention(const BlockShape& bs, const WsPtrs& ws, hipStream_t 
   p.k = static_cast<const bf16*>(ws.k);
   p.vt = static_cast<const bf16*>(ws.vt);
   p.out = static_cast<bf16*>(ws.cat);
+  p.part = static_cast<float*>(ws.part);
   p.M = bs.M;
   p.n_pad = bs.n_pad;
   p.H = bs.H;
   p.ldo = bs.D + bs.F;
   p.scale_log2 = 1.4426950408889634f / sqrtf((float)kHeadDim);
   const int nqb = (bs.M + AQ - 1) / AQ;
-  hipLaunchKernelGGL(k_attention, dim3(nqb * bs.H), dim3(NTHREADS), 0, s, p);
+  const int nkv = (bs.M + AKV - 1) / AKV;
+  const int units = nqb * bs.H;
+  const int G = stream_k_groups();
+  p.groups = G;
+  p.dp_rounds = units / G;
+  p.tail = units % G;
+  // a tail filling most of a round runs whole; a thin one has its key tiles
+  // spread over up to G ranges of at least 4 tiles each
+  if (p.tail * 10 > G * 7) {
+    p.dp_rounds += 1;
+    p.tail = 0;
+  }
+  p.tail_ranges = 0;
+  if (p.tail > 0) {
+    const int64_t items = (int64_t)p.tail * nkv;
+    p.tail_ranges = (int)std::min<int64_t>(G, std::max<int64_t>(1, items / 4));
+  }
+  hipLaunchKernelGGL(k_attention, dim3(G), dim3(NTHREADS), 0, s, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || p.tail_ranges < 2) return e;
+  hipLaunchKernelGGL(k_attention_fixup, dim3(p.tail_ranges - 1), dim3(NTHREADS), 0, s, p);
   return hipGetLastError();
 }
 

@@ -55,6 +55,33 @@ __host__ __device__ __forceinline__ size_t packed_index(size_t row, int k, int K
          ((size_t)(((k >> 3) & 7) ^ ((int)(row >> 1) & 7)) << 3) + (size_t)(k & 7);
 }
 
+// Even split of a run of work items over G persistent workgroups (the
+// stream-K tails of the output GEMM and of attention).  Units of nk items
+// each (a GEMM tile's k slices, an attention query block's key tiles) lie
+// end to end, unit t owning items [t nk, (t + 1) nk); range v covers items
+// [start(v), start(v + 1)) with start(v) = floor(v total / G).  A unit cut
+// by range boundaries leaves one partial result per range that touches it:
+// a range's first segment in slot 2v, its last (when in another unit) in
+// slot 2v + 1, so 2G slots cover any split.
+struct SplitK {
+  int64_t total;   // units * nk
+  int G, nk;
+  __device__ __forceinline__ int64_t start(int v) const { return total * v / G; }
+  // range holding item s
+  __device__ __forceinline__ int range_of(int64_t s) const {
+    return (int)(((s + 1) * G - 1) / total);
+  }
+  __device__ __forceinline__ int slot(int v, int t) const {
+    return 2 * v + (t == (int)(start(v) / nk) ? 0 : 1);
+  }
+};
+
+// Physical workgroup id -> range: the workgroups one XCD runs (every 8th id)
+// take consecutive ranges, so they work on neighbouring units.
+__device__ __forceinline__ int range_of_block(int b, int G) {
+  return (G % 8 == 0) ? (b % 8) * (G / 8) + b / 8 : b;
+}
+
 // Cross-lane exchange inside a wave (ds_bpermute based).
 __device__ __forceinline__ float xor_lane(float v, int mask) {
   return __shfl_xor(v, mask, kWave);

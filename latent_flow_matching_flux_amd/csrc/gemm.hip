@@ -571,25 +571,6 @@ struct OutArgs {
 // by the fixup kernel from the partials of its ranges, in k order.  A
 // range's first segment writes slot 2v, its last (when it is another tile)
 // slot 2v + 1.
-struct SplitK {
-  int64_t total;   // tail * nk
-  int G, nk;
-  __device__ __forceinline__ int64_t start(int v) const { return total * v / G; }
-  // range holding slice s
-  __device__ __forceinline__ int range_of(int64_t s) const {
-    return (int)(((s + 1) * G - 1) / total);
-  }
-  __device__ __forceinline__ int slot(int v, int t) const {
-    return 2 * v + (t == (int)(start(v) / nk) ? 0 : 1);
-  }
-};
-
-// Physical workgroup id -> range: the workgroups one XCD runs (every 8th id)
-// take consecutive ranges, so they work on neighbouring tiles.
-__device__ __forceinline__ int range_of_block(int b, int G) {
-  return (G % 8 == 0) ? (b % 8) * (G / 8) + b / 8 : b;
-}
-
 // x[m][n] += gate_s[n] * v for one accumulator value.
 __device__ __forceinline__ void out_update(const OutArgs& p, int m, int n, float v) {
   const float* gate = p.mod + (size_t)seg_of(p.segs, m) * 3 * p.D + 2 * p.D;
