@@ -16,6 +16,14 @@ rate at which tokens go through transformer blocks.  Per-kernel durations
 come from HIP events the library records around each of its launches on the
 launch stream, inside the timed region.
 
+The JSON line also carries the single joint block at 8432 tokens, timed
+apart from the step loop: 5 warm-up and 20 timed calls, each bracketed by
+HIP events on the launch stream, rotating 4 weight copies (980 MB) so that
+no call finds its weights in the 256 MB Infinity Cache; median and minimum,
+block tokens/s = N / t_block, and GEMM / attention TFLOP/s from the
+library's per-kernel events over those calls.  Peak: the 2516.6 TFLOP/s of
+AMD's MI355X spec, next to CUs x clock x 4096 from the device query.
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
 """
 import argparse
@@ -60,6 +68,60 @@ def measured_traffic(launch_tokens):
     if t.get("source_hash") != source_hash() or t.get("tokens") != launch_tokens:
         return None
     return t.get("bytes_per_launch")
+
+
+def time_joint_block(F, dims, lay, segs, n, rand, rand_block, reps=20, warmup=5, copies=4):
+    """One joint block over all n tokens: median/min of `reps` event-timed
+    calls with rotating weight copies, plus per-kernel GEMM and attention
+    rates over the same calls."""
+    import statistics
+    import torch
+    dev = torch.device("cuda:0")
+    D = dims.width
+    blocks = [rand_block() for _ in range(copies)]
+    x0 = rand(n, D, dtype=torch.float32)
+    x = torch.empty_like(x0)
+    mod = rand(len(segs), 3, D, std=0.07, dtype=torch.float32)
+    rope = torch.empty((n, 64, 2), dtype=torch.float32, device=dev)
+    F.rope_tables_build(lay, rope)
+    ws = torch.empty(F.workspace_bytes(dims, n), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+    for i in range(warmup):
+        x.copy_(x0)
+        F.block_forward(dims, blocks[i % copies], x, segs, mod, rope, ws, stream=stream)
+    torch.cuda.synchronize()
+    F.profile_reset()
+    F.profile_enable(True)
+    events = []
+    for i in range(reps):
+        x.copy_(x0)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        F.block_forward(dims, blocks[i % copies], x, segs, mod, rope, ws, stream=stream)
+        e1.record(stream)
+        events.append((e0, e1))
+    torch.cuda.synchronize()
+    F.profile_enable(False)
+    stats = {k: F.profile_read(k) for k in F.KERNELS}
+    F.profile_reset()
+    assert torch.isfinite(x).all(), "non-finite block output"
+    ms = sorted(a.elapsed_time(b) for a, b in events)
+    proj_fpt, out_fpt = gemm_flops_per_token(dims)
+    gemm_flops = (proj_fpt + out_fpt) * n * reps
+    attn_flops = 4.0 * D * n * n * reps
+    gemm_ms = stats["gemm_proj"]["total_ms"] + stats["gemm_out"]["total_ms"]
+    attn_ms = stats["attention"]["total_ms"]
+    block_flops = (proj_fpt + out_fpt) * n + 4.0 * D * n * n
+    med = statistics.median(ms)
+    return {"tokens": n, "reps": reps, "warmup": warmup, "weight_copies": copies,
+            "median_ms": med, "min_ms": ms[0],
+            "tokens_per_s": n / (med * 1e-3),
+            "tflops": block_flops / (med * 1e-3) / 1e12,
+            "frac_peak": block_flops / (med * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+            "gemm_tflops": gemm_flops / (gemm_ms * 1e-3) / 1e12,
+            "attention_tflops": attn_flops / (attn_ms * 1e-3) / 1e12,
+            "kernel_ms": {k: v["total_ms"] / reps for k, v in stats.items()}}
 
 
 def cpu_baseline(workload_name):
@@ -199,6 +261,15 @@ def main():
                 "traffic": measured_traffic(n),
                 "work_per_launch": f"{proj_fpt / 1e6:.2f} MFLOP/token x {gp['tokens'] / max(gp['launches'], 1):.0f} tokens (mean over stage-1 and stage-2 launches)"}
 
+    # single joint block over all tokens (the same segments and layout)
+    block = time_joint_block(F, dims, lay, segs, n, rand, rand_block)
+    block["gemm_frac_peak"] = block["gemm_tflops"] / PEAK_BF16_TFLOPS
+    block["attention_frac_peak"] = block["attention_tflops"] / PEAK_BF16_TFLOPS
+    devinfo = F.device_query(0)
+    peak = {"spec_tflops": PEAK_BF16_TFLOPS, "derived_tflops": devinfo["bf16_dense_tflops"],
+            "compute_units": devinfo["compute_units"], "clock_mhz": devinfo["clock_khz"] / 1e3,
+            "arch": devinfo["arch"], "rule": "CUs x clock x 4096 FLOP/clk (dense bf16 MFMA)"}
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(args.workload)
@@ -224,6 +295,8 @@ def main():
         "step_frac_peak": step_flops / (ms_per_step * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
         "stack_tokens_per_s": n / (ms_per_step / 1e3),
         "kernels": kern,
+        "block": block,
+        "peak": peak,
         "roofline": roofline,
         "cpu_baseline": cpu,
     }

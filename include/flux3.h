@@ -225,6 +225,19 @@ void flux3_profile_reset(void);
  * cannot be read. */
 flux3_status flux3_profile_read(int32_t kernel, flux3_kernel_stats *out);
 
+/* What the kernels run on: compute units and shader clock of a HIP device,
+ * its architecture name, and the dense bf16 MFMA peak those imply for the
+ * gfx950 matrix cores (4096 FLOP per clock per CU): CUs x clock x 4096.
+ * FLUX3_E_INVALID for a NULL out, FLUX3_E_HIP if the device cannot be
+ * queried.  Host-only; enqueues nothing. */
+typedef struct {
+  int32_t compute_units;
+  int32_t clock_khz;          /* maximum shader clock */
+  double bf16_dense_tflops;   /* compute_units * clock * 4096 / 1e12 */
+  char arch[64];              /* e.g. "gfx950:sramecc+:xnack-" */
+} flux3_device_info;
+flux3_status flux3_device_query(int32_t device, flux3_device_info *out);
+
 /* Debug switch: when non-zero every launch is followed by a stream
  * synchronisation and an error check, so a faulting kernel is named in
  * flux3_last_error_detail().  Off by default. */

@@ -7,9 +7,11 @@ binding with the same entry-point names.
 from ._lib import (Flux3Error, Dims, Segment, BlockWeights, RopeLayout, WorkspaceLayout,
                    load, layout_tokens, rope_tables_build, workspace_bytes, workspace_layout,
                    block_forward, stack_forward, set_debug_sync, status_string, EXPORTS,
-                   LIB_PATH, KERNELS, profile_enable, profile_reset, profile_read)
+                   LIB_PATH, KERNELS, profile_enable, profile_reset, profile_read,
+                   device_query)
 
 __all__ = ["Flux3Error", "Dims", "Segment", "BlockWeights", "RopeLayout", "WorkspaceLayout",
            "load", "layout_tokens", "rope_tables_build", "workspace_bytes", "workspace_layout",
            "block_forward", "stack_forward", "set_debug_sync", "status_string", "EXPORTS",
-           "LIB_PATH", "KERNELS", "profile_enable", "profile_reset", "profile_read"]
+           "LIB_PATH", "KERNELS", "profile_enable", "profile_reset", "profile_read",
+           "device_query"]

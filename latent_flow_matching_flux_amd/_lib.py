@@ -22,7 +22,8 @@ MAX_REFS = 15
 EXPORTS = ("flux3_layout_tokens", "flux3_rope_tables_build", "flux3_workspace_bytes",
            "flux3_workspace_layout_get", "flux3_block_forward", "flux3_stack_forward",
            "flux3_profile_enable", "flux3_profile_reset", "flux3_profile_read",
-           "flux3_set_debug_sync", "flux3_status_string", "flux3_last_error_detail")
+           "flux3_device_query", "flux3_set_debug_sync", "flux3_status_string",
+           "flux3_last_error_detail")
 KERNELS = ("rope_tables", "ln_modulate", "gemm_proj", "attention", "gemm_out")
 
 
@@ -58,6 +59,11 @@ class RopeLayout(ctypes.Structure):
 class KernelStats(ctypes.Structure):
     _fields_ = [("launches", ctypes.c_int64), ("total_ms", ctypes.c_double),
                 ("tokens", ctypes.c_double), ("tokens_sq", ctypes.c_double)]
+
+
+class DeviceInfo(ctypes.Structure):
+    _fields_ = [("compute_units", ctypes.c_int32), ("clock_khz", ctypes.c_int32),
+                ("bf16_dense_tflops", ctypes.c_double), ("arch", ctypes.c_char * 64)]
 
 
 class WorkspaceLayout(ctypes.Structure):
@@ -99,6 +105,8 @@ def load(path=LIB_PATH):
     lib.flux3_profile_reset.restype = None
     lib.flux3_profile_read.argtypes = [i32, P(KernelStats)]
     lib.flux3_profile_read.restype = i32
+    lib.flux3_device_query.argtypes = [i32, P(DeviceInfo)]
+    lib.flux3_device_query.restype = i32
     lib.flux3_set_debug_sync.argtypes = [i32]
     lib.flux3_set_debug_sync.restype = None
     lib.flux3_status_string.argtypes = [i32]
@@ -255,6 +263,14 @@ def profile_read(kernel):
     _check(load().flux3_profile_read(idx, ctypes.byref(out)))
     return {"launches": out.launches, "total_ms": out.total_ms, "tokens": out.tokens,
             "tokens_sq": out.tokens_sq}
+
+
+def device_query(device=0):
+    """flux3_device_query: CU count, clock, arch and the implied bf16 MFMA peak."""
+    out = DeviceInfo()
+    _check(load().flux3_device_query(device, ctypes.byref(out)))
+    return {"compute_units": out.compute_units, "clock_khz": out.clock_khz,
+            "bf16_dense_tflops": out.bf16_dense_tflops, "arch": out.arch.decode()}
 
 
 def set_debug_sync(on):

@@ -381,6 +381,22 @@ flux3_status flux3_stack_forward(const flux3_dims* dims, const flux3_block_weigh
   return ok();
 }
 
+flux3_status flux3_device_query(int32_t device, flux3_device_info* out) {
+  if (!out) return fail(FLUX3_E_INVALID, "out is NULL");
+  memset(out, 0, sizeof *out);
+  int cus = 0, clk = 0;
+  hipError_t e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&clk, hipDeviceAttributeClockRate, device);
+  hipDeviceProp_t prop;
+  if (e == hipSuccess) e = hipGetDeviceProperties(&prop, device);
+  if (e != hipSuccess) return fail(FLUX3_E_HIP, "device %d query: %s", device, hipGetErrorString(e));
+  out->compute_units = cus;
+  out->clock_khz = clk;
+  out->bf16_dense_tflops = (double)cus * (double)clk * 1e3 * 4096.0 / 1e12;
+  snprintf(out->arch, sizeof out->arch, "%s", prop.gcnArchName);
+  return ok();
+}
+
 void flux3_set_debug_sync(int32_t on) { g_debug_sync = on; }
 
 void flux3_profile_enable(int32_t on) { g_prof_on = on != 0; }

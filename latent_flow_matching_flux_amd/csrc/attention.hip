@@ -484,25 +484,25 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_attention(AttnArgs p) {
 
 // Merges the partial results of every tail unit cut by a range boundary, in
 // range (key) order: m = max m_i, O = sum 2^(m_i - m) O_i, l = sum 2^(m_i -
-// m) l_i, out = O / l.  Workgroup i looks at the boundary between ranges i
-// and i + 1 and takes its unit if no earlier boundary falls inside it; a
-// thread handles the registers one attention lane held.
-__global__ __launch_bounds__(NTHREADS) void k_attention_fixup(AttnArgs p) {
+// m) l_i, out = O / l.  Workgroup (i, w) looks at the boundary between
+// ranges i and i + 1, takes its unit if no earlier boundary falls inside
+// it, and merges the 32 queries of attention wave w; a thread handles the
+// registers one attention lane held.
+__global__ __launch_bounds__(64) void k_attention_fixup(AttnArgs p) {
   const int nqb = (p.M + AQ - 1) / AQ;
   const int nkv = (p.M + AKV - 1) / AKV;
   SplitK sk;
   sk.nk = nkv;
   sk.G = p.tail_ranges;
   sk.total = (int64_t)p.tail * nkv;
-  const int i = blockIdx.x;
+  const int i = blockIdx.x / WAVES, wave = blockIdx.x % WAVES;
   const int64_t b = sk.start(i + 1);
   if (b % nkv == 0) return;                        // boundary on a unit edge
   const int u = (int)(b / nkv);
   if (sk.start(i) > (int64_t)u * nkv) return;      // an earlier boundary owns the unit
   const int v_first = sk.range_of((int64_t)u * nkv);
   const int v_last = sk.range_of((int64_t)(u + 1) * nkv - 1);
-  const int t = threadIdx.x;
-  const int wave = t >> 6, lane = t & 63, r32 = lane & 31, hh = lane >> 5;
+  const int lane = threadIdx.x, r32 = lane & 31, hh = lane >> 5;
   const int qw = wave * 32 + r32;                  // query within the unit
 
   float m = -INFINITY;
@@ -584,7 +584,7 @@ hipError_t launch_attention(const BlockShape& bs, const WsPtrs& ws, hipStream_t 
   hipLaunchKernelGGL(k_attention, dim3(G), dim3(NTHREADS), 0, s, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.tail_ranges < 2) return e;
-  hipLaunchKernelGGL(k_attention_fixup, dim3(p.tail_ranges - 1), dim3(NTHREADS), 0, s, p);
+  hipLaunchKernelGGL(k_attention_fixup, dim3((p.tail_ranges - 1) * WAVES), dim3(64), 0, s, p);
   return hipGetLastError();
 }
 
