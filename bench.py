@@ -155,6 +155,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default="edit8432")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-block", action="store_true",
+                    help="skip the single-block timing (profiling runs of the step alone)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path; run with --gpus 1",
@@ -262,9 +264,11 @@ def main():
                 "work_per_launch": f"{proj_fpt / 1e6:.2f} MFLOP/token x {gp['tokens'] / max(gp['launches'], 1):.0f} tokens (mean over stage-1 and stage-2 launches)"}
 
     # single joint block over all tokens (the same segments and layout)
-    block = time_joint_block(F, dims, lay, segs, n, rand, rand_block)
-    block["gemm_frac_peak"] = block["gemm_tflops"] / PEAK_BF16_TFLOPS
-    block["attention_frac_peak"] = block["attention_tflops"] / PEAK_BF16_TFLOPS
+    block = None
+    if not args.no_block:
+        block = time_joint_block(F, dims, lay, segs, n, rand, rand_block)
+        block["gemm_frac_peak"] = block["gemm_tflops"] / PEAK_BF16_TFLOPS
+        block["attention_frac_peak"] = block["attention_tflops"] / PEAK_BF16_TFLOPS
     devinfo = F.device_query(0)
     peak = {"spec_tflops": PEAK_BF16_TFLOPS, "derived_tflops": devinfo["bf16_dense_tflops"],
             "compute_units": devinfo["compute_units"], "clock_mhz": devinfo["clock_khz"] / 1e3,

@@ -772,18 +772,16 @@ hipError_t launch_gemm_proj(const BlockShape& bs, const BlockWeightsDev& w,
   return hipGetLastError();
 }
 
+// Persistent workgroups for the split kernels: one per CU of the current
+// device, at most kMaxSplitGroups (the workspace's partial slots).  Queried
+// on every call; the library keeps no state across calls.
 int stream_k_groups() {
-  static int groups[64] = {0};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return kMaxSplitGroups;
-  if (groups[dev] == 0) {
-    int cus = 0;
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        cus <= 0)
-      cus = kMaxSplitGroups;
-    groups[dev] = cus < kMaxSplitGroups ? cus : kMaxSplitGroups;
-  }
-  return groups[dev];
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      cus <= 0)
+    return kMaxSplitGroups;
+  return cus < kMaxSplitGroups ? cus : kMaxSplitGroups;
 }
 
 hipError_t launch_gemm_out(const BlockShape& bs, const BlockWeightsDev& w,
