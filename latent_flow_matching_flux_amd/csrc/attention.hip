@@ -155,6 +155,7 @@ typedef f32x16 STile[2];        // S^T of one tile: [32-key block]
 typedef uint32_t PTile[2][2][4];
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
+constexpr bf16x2 kOnes2 = {(__bf16)1.0f, (__bf16)1.0f};
 
 __device__ __forceinline__ bf16x8 pfrag(const uint32_t (&w)[4]) {
   const u32x4 v = {w[0], w[1], w[2], w[3]};
@@ -171,7 +172,7 @@ __device__ __forceinline__ void pin(T& v) {
 // Per-query online softmax state of one lane.
 struct SoftState {
   float m_ref;   // reference max, log2 domain
-  float l_sum;   // running sum of exp2(s - m_ref) over this lane's keys
+  float l_sum;   // running sum of the bf16-rounded exp2(s - m_ref) over this lane's keys
   float alpha;   // factor O must take before the next PV (1 if m_ref held)
   bool moved;    // wave-uniform: m_ref moved in the last softmax
 };
@@ -255,11 +256,11 @@ __device__ __forceinline__ void region(STile& Sn, uint32_t k_off, f32x16 (&o)[4]
         constexpr int idx = 2 * (i - 9);
         f32x2 pp;
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
+        for (int u = 0; u < 2; ++u)
           pp[u] = __builtin_amdgcn_exp2f(__builtin_fmaf(vals[idx + u], scale, -st.m_ref));
-          l += pp[u];
-        }
         const bf16x2 pb = __builtin_convertvector(pp, bf16x2);
+        // the running sum takes the bf16 probabilities the PV product uses
+        l = __builtin_amdgcn_fdot2_f32_bf16(pb, kOnes2, l, false);
         uint32_t w = __builtin_bit_cast(uint32_t, pb);
         pin(w);
         Pc[idx >> 4][(idx >> 3) & 1][(idx & 7) >> 1] = w;
