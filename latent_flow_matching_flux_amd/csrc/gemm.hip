@@ -424,18 +424,38 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_gemm_proj(ProjArgs p) {
     gemm_mainloop<false, true, false>(smem, acc, W, H, D / BK, H, 0, D / BK);
 
   const int r32 = lane & 31, hi = lane >> 5;
-  // The output tile is staged in LDS (free once every wave is past the main
-  // loop) so that the global stores are whole 16-byte chunks of contiguous
-  // rows.  Staged rows are 256 B (queries, keys, SwiGLU: one token's 128
-  // features) or 512 B (values: one dim's 256 tokens); chunk c of staged
-  // row r sits in slot c ^ (r % 16) or c ^ (r % 32) respectively, which
-  // spreads the lanes' 8-byte writes over the LDS banks.
+  // LDS is free once every wave is past the main loop.  Values and SwiGLU
+  // stage their output tile there so that the global stores are whole
+  // 16-byte chunks of contiguous rows: staged rows are 256 B (SwiGLU: one
+  // token's 128 features) or 512 B (values: one dim's 256 tokens), chunk c
+  // of staged row r in slot c ^ (r % 16) or c ^ (r % 32) respectively,
+  // which spreads the lanes' 8-byte writes over the banks.  Queries and
+  // keys use it for the tile's RoPE rows instead.
   typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
   typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
   __syncthreads();
   if (kind < 2) {
-    // per-head RMSNorm + RoPE: this wave holds head head0 + wm for 128 tokens
+    // The RoPE rows of the tile's 256 tokens go to LDS first, by direct
+    // loads (2 rows of 512 B per load; rows past the last token repeat it).
+    // Chunk c (4 floats = 2 pairs) of row t sits in slot c ^ (t % 32), so the
+    // 32 lanes of a read, 32 consecutive tokens at one chunk, hit different
+    // banks.  Then per-head RMSNorm + RoPE: this wave holds head head0 + wm
+    // for 128 tokens and stores its 4 consecutive dims per register group.
+    const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
+    const float* rope = reinterpret_cast<const float*>(p.rope);
+#pragma unroll 8
+    for (int it = 0; it < 32; ++it) {
+      const int row = wave * 64 + it * 2 + (lane >> 5);
+      const int c = (lane & 31) ^ (row & 31);
+      const int m = min(m0 + row, p.M - 1);
+      dma16(reinterpret_cast<const bf16*>(rope + (size_t)m * 2 * kRopePairs + c * 4),
+            lds0 + (uint32_t)((wave * 64 + it * 2) * 512));
+    }
+    wait_vm<0>();
+    __syncthreads();
+    typedef const __attribute__((address_space(3))) f32x4 lds_f4;
     const float* nw = kind == 0 ? p.qn : p.kn;
+    bf16* dst = (kind == 0 ? p.q : p.k) + (size_t)(head0 + wm) * p.n_pad * kHeadDim;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int t = wn * 128 + j * 32 + r32;             // token within the tile
@@ -448,14 +468,13 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_gemm_proj(ProjArgs p) {
         for (int e = 0; e < 16; ++e) ss += acc.c[i][j][e] * acc.c[i][j][e];
       ss += xor_lane(ss, 32);
       const float rs = 1.0f / sqrtf(ss * (1.0f / kHeadDim) + p.eps);
-      const float* rr = reinterpret_cast<const float*>(p.rope) + (size_t)(live ? m : 0) * 2 * kRopePairs;
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           const int d0 = i * 32 + 8 * g + 4 * hi;          // 4 consecutive dims = 2 pairs
           const float4 wv = *reinterpret_cast<const float4*>(nw + d0);
-          const float4 cs = *reinterpret_cast<const float4*>(rr + d0);   // cos0 sin0 cos1 sin1
+          const f32x4 cs = *(lds_f4*)(smem + t * 512 + (((d0 >> 2) ^ (t & 31)) << 4));   // cos0 sin0 cos1 sin1
           const float x0 = acc.c[i][j][4 * g + 0] * rs * wv.x;
           const float x1 = acc.c[i][j][4 * g + 1] * rs * wv.y;
           const float x2 = acc.c[i][j][4 * g + 2] * rs * wv.z;
@@ -465,21 +484,8 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_gemm_proj(ProjArgs p) {
           o[1] = f2bf(live ? x0 * cs.y + x1 * cs.x : 0.f);
           o[2] = f2bf(live ? x2 * cs.z - x3 * cs.w : 0.f);
           o[3] = f2bf(live ? x2 * cs.w + x3 * cs.z : 0.f);
-          const int chunk = 4 * i + g;
-          *(lds_bf16x4*)(smem + wm * 65536 + t * 256 + ((chunk ^ (t & 15)) << 4) + 8 * hi) = o;
+          *reinterpret_cast<bf16x4*>(dst + (size_t)m * kHeadDim + d0) = o;
         }
-    }
-    __syncthreads();
-    // 2 heads x 256 tokens of 256 B; a store instruction covers 4 rows (1 KiB
-    // contiguous in the head-major output)
-    bf16* out = kind == 0 ? p.q : p.k;
-#pragma unroll 4
-    for (int it = 0; it < 32; ++it) {
-      const int row = wave * 128 + it * 4 + (lane >> 4), chunk = lane & 15;
-      const int t = row & 255;
-      const u32x4 v = *(lds_u32x4*)(smem + row * 256 + ((chunk ^ (t & 15)) << 4));
-      bf16* dst = out + ((size_t)(head0 + (row >> 8)) * p.n_pad + m0 + t) * kHeadDim + chunk * 8;
-      *reinterpret_cast<u32x4*>(dst) = v;
     }
   } else if (kind == 2) {
     // values, transposed: staged as [head][dim][256 token positions]
