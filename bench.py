@@ -2,14 +2,16 @@
 """Throughput of the FLUX.3 Image Klein block stack on one MI355X.
 
 One step is the whole hot path over one batch: the rotary tables for the
-token layout, then the two-stage stack -- 5 per-mode blocks on each stream
-(text, noisy image, reference; each stream attends only to itself) and 28
-joint blocks over the concatenated sequence -- on the single-reference edit
-workload [240 text | 64x64 image | 64x64 reference] = 8432 tokens at width
-3072, 24 heads x 128, SwiGLU hidden 9216, bf16 operands with fp32
-accumulation and an fp32 residual stream.  Weights (43 distinct blocks) are
-seeded random N(0, 0.02^2) in bf16, tokens N(0, 1), modulation vectors
-N(0, 0.07^2); everything is resident in HBM before timing starts.
+token layout, the two stages' modulation vectors from the timesteps (image
+t drawn U(0, 1) with seed 0, text and reference t = 0), then the two-stage
+stack -- 5 per-mode blocks on each stream (text, noisy image, reference;
+each stream attends only to itself) and 28 joint blocks over the
+concatenated sequence -- on the single-reference edit workload [240 text |
+64x64 image | 64x64 reference] = 8432 tokens at width 3072, 24 heads x 128,
+SwiGLU hidden 9216, bf16 operands with fp32 accumulation and an fp32
+residual stream.  Weights (43 distinct blocks, the timestep embedder and
+6 modulation linears) are seeded random N(0, 0.02^2) in bf16, tokens
+N(0, 1); everything is resident in HBM before timing starts.
 
 value = block-token passes per second = (5 + 28) * 8432 / step time, the
 rate at which tokens go through transformer blocks.  Per-kernel durations
@@ -193,14 +195,23 @@ def main():
     joint = [rand_block() for _ in range(N_JOINT)]
     x0 = rand(n, D, dtype=torch.float32)
     x = torch.empty_like(x0)
-    m1 = rand(len(segs), 3, D, std=0.07, dtype=torch.float32)
-    m2 = rand(len(segs), 3, D, std=0.07, dtype=torch.float32)
+    # timestep path: one embedder, a modulation linear per (stage, mode)
+    emb_w = {"w1": rand(D, 256, std=0.02), "w2": rand(D, D, std=0.02)}
+    mod_w = [dict(emb_w, w_mod={m: rand(3 * D, D, std=0.02) for m in modes}) for _ in range(2)]
+    import numpy as np
+    t_image = float(np.random.default_rng(0).uniform())
+    t_by_mode = (0.0, t_image, 0.0)
+    m1 = torch.empty((len(segs), 3, D), dtype=torch.float32, device=dev)
+    m2 = torch.empty_like(m1)
+    mws = torch.empty(F.modulation_workspace_bytes(dims), dtype=torch.uint8, device=dev)
     rope = torch.empty((n, 64, 2), dtype=torch.float32, device=dev)
     ws = torch.empty(F.workspace_bytes(dims, n), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
 
     def step():
         F.rope_tables_build(lay, rope, stream=stream)
+        F.modulation_forward(dims, mod_w[0], t_by_mode, segs, m1, mws, stream=stream)
+        F.modulation_forward(dims, mod_w[1], t_by_mode, segs, m2, mws, stream=stream)
         x.copy_(x0)
         F.stack_forward(dims, per_mode, joint, x, segs, m1, m2, rope, ws, stream=stream)
 
@@ -244,6 +255,10 @@ def main():
             entry["gbs"] = 6.0 * D * st["tokens"] / (ms * 1e-3) / 1e9 if ms > 0 else 0.0
         elif k == "rope_tables":
             entry["gbs"] = 512.0 * st["tokens"] / (ms * 1e-3) / 1e9 if ms > 0 else 0.0
+        elif k == "modulation":
+            # weights read once per call: embedder + one linear per used mode
+            wbytes = 2.0 * (D * 256 + D * D + len(modes) * 3 * D * D)
+            entry["gbs"] = wbytes * st["launches"] / (ms * 1e-3) / 1e9 if ms > 0 else 0.0
         if "tflops" in entry:
             entry["frac_peak"] = entry["tflops"] / PEAK_BF16_TFLOPS
         kern[k] = entry
@@ -291,10 +306,12 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": f"{args.workload}: {wl.description}; rope tables + "
-                               f"{N_PM} per-mode blocks per stream + {N_JOINT} joint blocks",
+        "config": {"workload": f"{args.workload}: {wl.description}; rope tables + 2 stages' "
+                               f"modulation from t + {N_PM} per-mode blocks per stream + "
+                               f"{N_JOINT} joint blocks",
                    "tokens": n, "width": D, "heads": dims.heads, "head_dim": dims.head_dim,
-                   "mlp_hidden": Fh, "segments": [[s.start, s.count, s.mode] for s in segs]},
+                   "mlp_hidden": Fh, "segments": [[s.start, s.count, s.mode] for s in segs],
+                   "t_image": t_image, "t_text": 0.0, "t_reference": 0.0},
         "step_tflops": step_flops / (ms_per_step * 1e-3) / 1e12,
         "step_frac_peak": step_flops / (ms_per_step * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
         "stack_tokens_per_s": n / (ms_per_step / 1e3),

@@ -196,6 +196,58 @@ flux3_status flux3_stack_forward(const flux3_dims *dims,
                                  void *workspace, size_t workspace_bytes,
                                  void *stream);
 
+/* ---------------------------------------------------------------------------
+ * Modulation from timesteps.  Each block's adaLN (shift, scale, gate) comes
+ * from the timestep embedding ("Speed, architecture, and how the tokens
+ * move", 15jq.com post: image tokens take the current timestep, text and
+ * reference tokens t = 0; "What step distillation removed",
+ * rohitghumare.com guide: a 256 -> width -> width embedder with no biases,
+ * and for the distilled flow map a second embedder of the target timestep
+ * whose output is added; "The denoise loop", same guide: timesteps are
+ * sigmas scaled by 1000):
+ *   e(t)   = [cos(1000 t f_i), sin(1000 t f_i)],  f_i = 10000^(-i/128), i < 128
+ *   E(t)   = W2 silu(W1 e(t));  E'(t) = W2' silu(W1' e(t))
+ *   mod[s] = W_mod[mode_s] silu(E(t_mode_s) + E'(t_target))
+ * split in the order shift, scale, gate.
+ * ------------------------------------------------------------------------- */
+
+/* Weights, bf16 in torch Linear layout [out][in]: the embedder w1
+ * [width][256] and w2 [width][width]; the target embedder w1_tgt, w2_tgt
+ * (same shapes; unused and may be NULL when t_target < 0); and one stage's
+ * modulation linears w_mod[mode] [3*width][width] (mode 0 text, 1 image,
+ * 2 reference; a mode no segment uses may be NULL). */
+typedef struct {
+  const void *w1, *w2, *w1_tgt, *w2_tgt;
+  const void *w_mod[3];
+} flux3_modulation_weights;
+
+/* Workspace bytes flux3_modulation_forward needs: fp32 [4][256] + [8][width]
+ * (an embedding, a hidden vector and E per timestep); 0 if dims are
+ * unsupported. */
+size_t flux3_modulation_workspace_bytes(const flux3_dims *dims);
+
+/* One stage's modulation vectors for every segment.
+ *   t_by_mode: host float[3], the timestep of each mode (text, image,
+ *              reference); the model uses 0 for text and reference.  Values
+ *              of the modes the segments use must be finite.
+ *   t_target : the flow-map target timestep, or any negative value for none.
+ *   segs     : host [n_segs], as for flux3_block_forward (tiling [0, N) in
+ *              the order text, image, reference).
+ *   mod      : device fp32 [n_segs][3][width] out, the layout
+ *              flux3_block_forward and flux3_stack_forward take; segments of
+ *              one mode get the same vectors.
+ *   workspace: device, >= flux3_modulation_workspace_bytes(dims) bytes,
+ *              256-byte aligned.
+ * width must be <= 4096.  Matrix-vector work over the weights (about 190 MB
+ * per call at width 3072), bound by HBM.  Errors as for flux3_block_forward;
+ * on error nothing is enqueued. */
+flux3_status flux3_modulation_forward(const flux3_dims *dims,
+                                      const flux3_modulation_weights *w,
+                                      const float *t_by_mode, float t_target,
+                                      const flux3_segment *segs, int32_t n_segs,
+                                      float *mod, void *workspace,
+                                      size_t workspace_bytes, void *stream);
+
 /* Kernel timing, for benchmarks and profiling.  While enabled, every kernel
  * launch is bracketed by a pair of HIP events recorded on the launch stream,
  * so the durations are those of the kernels themselves on the stream they
@@ -211,7 +263,8 @@ enum {
   FLUX3_K_GEMM_PROJ = 2,
   FLUX3_K_ATTENTION = 3,
   FLUX3_K_GEMM_OUT = 4,
-  FLUX3_K_COUNT = 5
+  FLUX3_K_MODULATION = 5,   /* one record per flux3_modulation_forward call */
+  FLUX3_K_COUNT = 6
 };
 typedef struct {
   int64_t launches;

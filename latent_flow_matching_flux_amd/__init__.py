@@ -8,10 +8,12 @@ from ._lib import (Flux3Error, Dims, Segment, BlockWeights, RopeLayout, Workspac
                    load, layout_tokens, rope_tables_build, workspace_bytes, workspace_layout,
                    block_forward, stack_forward, set_debug_sync, status_string, EXPORTS,
                    LIB_PATH, KERNELS, profile_enable, profile_reset, profile_read,
-                   device_query)
+                   device_query, modulation_workspace_bytes, modulation_forward,
+                   ModulationWeights)
 
 __all__ = ["Flux3Error", "Dims", "Segment", "BlockWeights", "RopeLayout", "WorkspaceLayout",
            "load", "layout_tokens", "rope_tables_build", "workspace_bytes", "workspace_layout",
            "block_forward", "stack_forward", "set_debug_sync", "status_string", "EXPORTS",
            "LIB_PATH", "KERNELS", "profile_enable", "profile_reset", "profile_read",
-           "device_query"]
+           "device_query", "modulation_workspace_bytes", "modulation_forward",
+           "ModulationWeights"]

@@ -21,10 +21,11 @@ MAX_REFS = 15
 # exported symbols, in the order include/flux3.h declares them
 EXPORTS = ("flux3_layout_tokens", "flux3_rope_tables_build", "flux3_workspace_bytes",
            "flux3_workspace_layout_get", "flux3_block_forward", "flux3_stack_forward",
+           "flux3_modulation_workspace_bytes", "flux3_modulation_forward",
            "flux3_profile_enable", "flux3_profile_reset", "flux3_profile_read",
            "flux3_device_query", "flux3_set_debug_sync", "flux3_status_string",
            "flux3_last_error_detail")
-KERNELS = ("rope_tables", "ln_modulate", "gemm_proj", "attention", "gemm_out")
+KERNELS = ("rope_tables", "ln_modulate", "gemm_proj", "attention", "gemm_out", "modulation")
 
 
 class Flux3Error(RuntimeError):
@@ -46,6 +47,11 @@ class Segment(ctypes.Structure):
 class BlockWeights(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in
                 ("wq", "wk", "wv", "wo", "w_gate", "w_up", "w_down", "q_norm", "k_norm")]
+
+
+class ModulationWeights(ctypes.Structure):
+    _fields_ = [("w1", ctypes.c_void_p), ("w2", ctypes.c_void_p), ("w1_tgt", ctypes.c_void_p),
+                ("w2_tgt", ctypes.c_void_p), ("w_mod", ctypes.c_void_p * 3)]
 
 
 class RopeLayout(ctypes.Structure):
@@ -99,6 +105,11 @@ def load(path=LIB_PATH):
     lib.flux3_stack_forward.argtypes = [P(Dims), P(BlockWeights), i32, P(BlockWeights), i32,
                                         vp, i64, P(Segment), i32, vp, vp, i64, vp, vp, sz, vp]
     lib.flux3_stack_forward.restype = i32
+    lib.flux3_modulation_workspace_bytes.argtypes = [P(Dims)]
+    lib.flux3_modulation_workspace_bytes.restype = sz
+    lib.flux3_modulation_forward.argtypes = [P(Dims), P(ModulationWeights), P(ctypes.c_float),
+                                             ctypes.c_float, P(Segment), i32, vp, vp, sz, vp]
+    lib.flux3_modulation_forward.restype = i32
     lib.flux3_profile_enable.argtypes = [i32]
     lib.flux3_profile_enable.restype = None
     lib.flux3_profile_reset.argtypes = []
@@ -245,6 +256,30 @@ def stack_forward(dims, per_mode, joint, x, segs, mod_stage1, mod_stage2, rope, 
                                       _ptr(mod_stage1), _ptr(mod_stage2), mod_block_stride,
                                       _ptr(rope), _ptr(workspace), workspace_nbytes,
                                       _stream_handle(stream)))
+
+
+def modulation_workspace_bytes(dims):
+    return load().flux3_modulation_workspace_bytes(ctypes.byref(make_dims(dims)))
+
+
+def modulation_forward(dims, w, t_by_mode, segs, mod, workspace, t_target=None,
+                       workspace_nbytes=None, stream=None):
+    """flux3_modulation_forward: one stage's [n_segs][3][width] modulation
+    vectors from timesteps.  w: dict with w1, w2, optional w1_tgt, w2_tgt,
+    and w_mod (a {mode: tensor} dict or a 3-list, None for unused modes);
+    t_by_mode: 3 timesteps (text, image, reference)."""
+    wm = w.get("w_mod", {})
+    mods = [wm.get(m) if isinstance(wm, dict) else wm[m] for m in range(3)]
+    W = ModulationWeights(_ptr(w.get("w1")), _ptr(w.get("w2")), _ptr(w.get("w1_tgt")),
+                          _ptr(w.get("w2_tgt")), (ctypes.c_void_p * 3)(*[_ptr(t) for t in mods]))
+    t = (ctypes.c_float * 3)(*[float(v) for v in t_by_mode])
+    seg_arr, n_segs = make_segments(segs)
+    if workspace_nbytes is None:
+        workspace_nbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(load().flux3_modulation_forward(ctypes.byref(make_dims(dims)), ctypes.byref(W), t,
+                                           -1.0 if t_target is None else float(t_target),
+                                           seg_arr, n_segs, _ptr(mod), _ptr(workspace),
+                                           workspace_nbytes, _stream_handle(stream)))
 
 
 def profile_enable(on):

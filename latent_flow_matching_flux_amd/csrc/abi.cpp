@@ -7,6 +7,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <cmath>
+
 #include <vector>
 
 #include "../../include/flux3.h"
@@ -378,6 +380,82 @@ flux3_status flux3_stack_forward(const flux3_dims* dims, const flux3_block_weigh
                   rope, workspace, s);
     if (r != FLUX3_OK) return r;
   }
+  return ok();
+}
+
+size_t flux3_modulation_workspace_bytes(const flux3_dims* dims) {
+  if (check_dims(dims) != FLUX3_OK) return 0;
+  return align_up(flux3::modulation_workspace_floats(dims->width) * sizeof(float), kBufAlign);
+}
+
+flux3_status flux3_modulation_forward(const flux3_dims* dims, const flux3_modulation_weights* w,
+                                      const float* t_by_mode, float t_target,
+                                      const flux3_segment* segs, int32_t n_segs, float* mod,
+                                      void* workspace, size_t workspace_bytes, void* stream) {
+  flux3_status r = check_dims(dims);
+  if (r != FLUX3_OK) return r;
+  const int D = dims->width;
+  if (D > 4096) return fail(FLUX3_E_UNSUPPORTED, "modulation supports width <= 4096, got %d", D);
+  if (!w) return fail(FLUX3_E_INVALID, "weights struct is NULL");
+  if (!t_by_mode) return fail(FLUX3_E_INVALID, "t_by_mode is NULL");
+  if (!segs || n_segs < 1) return fail(FLUX3_E_SHAPE, "n_segs %d (need >= 1) or segs NULL", n_segs);
+  const int64_t n = (int64_t)segs[n_segs - 1].start + segs[n_segs - 1].count;
+  if (n < 1 || n > kMaxTokens) return fail(FLUX3_E_SHAPE, "segments cover %lld tokens", (long long)n);
+  flux3::SegTableHost st;
+  if ((r = check_segments(segs, n_segs, n, &st)) != FLUX3_OK) return r;
+  const void* mats[4] = {w->w1, w->w2, w->w1_tgt, w->w2_tgt};
+  static const char* names[4] = {"w1", "w2", "w1_tgt", "w2_tgt"};
+  if (t_target != t_target) return fail(FLUX3_E_INVALID, "t_target is NaN");
+  const bool target = t_target >= 0.f;
+  for (int i = 0; i < (target ? 4 : 2); ++i) {
+    if (!mats[i]) return fail(FLUX3_E_INVALID, "%s is NULL", names[i]);
+    if (!aligned16(mats[i])) return fail(FLUX3_E_ALIGN, "%s is not 16-byte aligned", names[i]);
+  }
+  if (target && !std::isfinite(t_target)) return fail(FLUX3_E_INVALID, "t_target is not finite");
+  // distinct timesteps of the modes in use, in mode order; the target last
+  flux3::ModulationShape ms;
+  memset(&ms, 0, sizeof ms);
+  ms.D = D;
+  int32_t seg_mode[FLUX3_MAX_SEGMENTS];
+  bool used[3] = {false, false, false};
+  for (int i = 0; i < n_segs; ++i) {
+    seg_mode[i] = segs[i].mode;
+    used[segs[i].mode] = true;
+  }
+  for (int m = 0; m < 3; ++m) {
+    if (!used[m]) continue;
+    if (!w->w_mod[m]) return fail(FLUX3_E_INVALID, "w_mod[%d] is NULL but a segment uses mode %d", m, m);
+    if (!aligned16(w->w_mod[m])) return fail(FLUX3_E_ALIGN, "w_mod[%d] is not 16-byte aligned", m);
+    const float t = t_by_mode[m];
+    if (!std::isfinite(t)) return fail(FLUX3_E_INVALID, "t_by_mode[%d] is not finite", m);
+    int j = 0;
+    while (j < ms.n_t && ms.t[j] != t) ++j;
+    if (j == ms.n_t) ms.t[ms.n_t++] = t;
+    ms.t_index[m] = j;
+  }
+  if (target) {
+    ms.has_target = 1;
+    ms.t[ms.n_t] = t_target;
+  }
+  if (!mod) return fail(FLUX3_E_INVALID, "mod is NULL");
+  if (!aligned16(mod)) return fail(FLUX3_E_ALIGN, "mod is not 16-byte aligned");
+  const size_t need = flux3_modulation_workspace_bytes(dims);
+  if (!workspace) return fail(FLUX3_E_INVALID, "workspace is NULL");
+  if ((reinterpret_cast<uintptr_t>(workspace) & (kBufAlign - 1)) != 0)
+    return fail(FLUX3_E_ALIGN, "workspace is not %zu-byte aligned", kBufAlign);
+  if (workspace_bytes < need)
+    return fail(FLUX3_E_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, need);
+  flux3::ModulationWeightsDev wd;
+  wd.w1 = w->w1;
+  wd.w2 = w->w2;
+  wd.w1_tgt = w->w1_tgt;
+  wd.w2_tgt = w->w2_tgt;
+  for (int m = 0; m < 3; ++m) wd.w_mod[m] = w->w_mod[m];
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int pi = prof_begin(FLUX3_K_MODULATION, (double)n, s);
+  hipError_t e = flux3::launch_modulation(ms, wd, st, seg_mode, mod, static_cast<float*>(workspace), s);
+  prof_end(pi, s);
+  if ((r = after_launch(e, "modulation", s)) != FLUX3_OK) return r;
   return ok();
 }
 

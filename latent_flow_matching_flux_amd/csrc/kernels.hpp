@@ -44,6 +44,26 @@ struct BlockWeightsDev {
   const float *q_norm, *k_norm;
 };
 
+// Timestep path (NEXT-1): distinct timesteps of the used modes first, the
+// flow-map target last when present; t_index[mode] indexes t.
+struct ModulationShape {
+  int32_t D;
+  int32_t n_t;         // distinct timesteps of the modes the segments use (1..3)
+  int32_t has_target;
+  float t[4];
+  int32_t t_index[3];
+};
+
+struct ModulationWeightsDev {
+  const void *w1, *w2, *w1_tgt, *w2_tgt;
+  const void* w_mod[3];
+};
+
+size_t modulation_workspace_floats(int D);
+hipError_t launch_modulation(const ModulationShape& ms, const ModulationWeightsDev& w,
+                             const SegTableHost& segs, const int32_t* seg_mode, float* mod,
+                             float* ws, hipStream_t s);
+
 hipError_t launch_rope_tables(const RopeLayoutDev& lay, float* rope, int64_t n,
                               hipStream_t s);
 hipError_t launch_ln_modulate(const BlockShape& bs, const float* x,

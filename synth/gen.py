@@ -21,6 +21,10 @@ T_WQ, T_WK, T_WV, T_WO, T_WGATE, T_WUP, T_WDOWN, T_QNORM, T_KNORM = range(9)
 # stream ids for non-weight tensors (block_id slot)
 _X_STREAM = 1_000_000
 _MOD_STREAM = 2_000_000
+_TIME_STREAM = 3_000_000   # timestep embedder and modulation linears
+# tensor ids of the timestep path
+T_EMB_W1, T_EMB_W2, T_TGT_W1, T_TGT_W2 = range(4)
+T_WMOD0 = 10               # + 3 * stage + mode
 
 
 def _rng(*key):
@@ -70,6 +74,23 @@ def block_weights(seed, block_id, dims, norm_stress=False, std=WEIGHT_STD):
     else:
         w["q_norm"] = np.ones(hd, np.float32)
         w["k_norm"] = np.ones(hd, np.float32)
+    return w
+
+
+def modulation_weights(seed, width, stages=(0,), modes=(0, 1, 2), target=False,
+                       std=WEIGHT_STD):
+    """Weights of the timestep path as bf16 bits, torch-Linear layout: the
+    embedder w1 [width][256], w2 [width][width]; with target, the flow-map
+    target embedder w1_tgt, w2_tgt; and w_mod[stage][mode] [3*width][width]
+    for the listed stages and modes.  All N(0, std^2) before rounding."""
+    D = width
+    w = {"w1": _normal_bf16((D, 256), std, seed, _TIME_STREAM, T_EMB_W1),
+         "w2": _normal_bf16((D, D), std, seed, _TIME_STREAM, T_EMB_W2)}
+    if target:
+        w["w1_tgt"] = _normal_bf16((D, 256), std, seed, _TIME_STREAM, T_TGT_W1)
+        w["w2_tgt"] = _normal_bf16((D, D), std, seed, _TIME_STREAM, T_TGT_W2)
+    w["w_mod"] = {st: {m: _normal_bf16((3 * D, D), std, seed, _TIME_STREAM, T_WMOD0 + 3 * st + m)
+                       for m in modes} for st in stages}
     return w
 
 

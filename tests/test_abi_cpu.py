@@ -203,3 +203,32 @@ def test_packed_layout_reader():
         assert blk.shape[0] == (R // 8) * (K // 64)
         assert np.array_equal(np.sort(blk[0]), np.sort(x[:8, :64].ravel()))
         assert np.array_equal(unpack_rows(p, R, K), x)
+
+
+def test_modulation_workspace_and_validation():
+    d = _dims()
+    assert F.modulation_workspace_bytes(synth.DIMS) == (4 * 256 + 8 * 3072) * 4
+    assert F.modulation_workspace_bytes(synth.Dims(3072, 24, 64, 9216)) == 0
+    lib = F.load()
+    segs = [(0, 240, 0), (240, 4096, 1), (4336, 4096, 2)]
+    seg_arr, n_segs = L.make_segments(segs)
+    ws_bytes = F.modulation_workspace_bytes(synth.DIMS)
+
+    def call(w=None, t=(0.0, 0.5, 0.0), t_target=-1.0, dims=None, mod=FAKE, ws=FAKE,
+             nbytes=ws_bytes):
+        W = w if w is not None else L.ModulationWeights(FAKE, FAKE, None, None,
+                                                        (ctypes.c_void_p * 3)(FAKE, FAKE, FAKE))
+        tt = (ctypes.c_float * 3)(*t) if t is not None else None
+        return lib.flux3_modulation_forward(ctypes.byref(dims or d), ctypes.byref(W), tt,
+                                            t_target, seg_arr, n_segs, mod, ws, nbytes, 0)
+
+    assert call(t=None) == E_INVALID
+    assert call(t=(0.0, float("nan"), 0.0)) == E_INVALID
+    assert call(t_target=float("nan")) == E_INVALID
+    assert call(t_target=0.1) == E_INVALID            # target embedder missing
+    no_ref = L.ModulationWeights(FAKE, FAKE, None, None, (ctypes.c_void_p * 3)(FAKE, FAKE, None))
+    assert call(w=no_ref) == E_INVALID                # a segment uses mode 2
+    assert call(dims=_dims(width=5120, heads=40, hidden=15360)) == E_UNSUPPORTED
+    assert call(nbytes=ws_bytes - 4) == E_WORKSPACE
+    assert call(mod=FAKE + 4) == E_ALIGN
+    assert call(ws=FAKE + 16) == E_ALIGN
