@@ -577,32 +577,67 @@ struct OutArgs {
 // by the fixup kernel from the partials of its ranges, in k order.  A
 // range's first segment writes slot 2v, its last (when it is another tile)
 // slot 2v + 1.
-// x[m][n] += gate_s[n] * v for one accumulator value.
-__device__ __forceinline__ void out_update(const OutArgs& p, int m, int n, float v) {
-  const float* gate = p.mod + (size_t)seg_of(p.segs, m) * 3 * p.D + 2 * p.D;
-  p.x[(size_t)m * p.D + n] += gate[n] * v;
+// gate_s row of the segment holding token row m.
+__device__ __forceinline__ const float* gate_row(const OutArgs& p, int m) {
+  return p.mod + (size_t)seg_of(p.segs, m) * 3 * p.D + 2 * p.D;
+}
+
+// x += gate_s * acc for row block i of a wave (32 rows x 128 columns).
+// Lane l holds column l % 32 of each 32-column block j and rows
+// 8 (e / 4) + 4 (l / 32) + e % 4, e < 16.  Every load is issued before the
+// first store and none sits behind a branch: row indices past the last token
+// are clamped for the loads, and only the stores are predicated.  When the
+// wave's 128 rows lie in one segment (gate_one != null) its gate values are
+// read once per tile.
+__device__ __forceinline__ void out_rows(const OutArgs& p, const f32x16 (&v)[4], int i, int m0,
+                                         int n0, int wm, int wn, int lane,
+                                         const float* gate_one) {
+  const int D = p.D;
+  const int mb = m0 + wm * 128 + i * 32 + 4 * (lane >> 5);
+  const int nb = n0 + wn * 128 + (lane & 31);
+  float xv[16][4];
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    const int m = min(mb + 8 * (e >> 2) + (e & 3), p.M - 1);
+    const float* xr = p.x + (size_t)m * D + nb;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) xv[e][j] = xr[32 * j];
+  }
+  float gv[4];
+  if (gate_one) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) gv[j] = gate_one[nb + 32 * j];
+  }
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    const int m = mb + 8 * (e >> 2) + (e & 3);
+    if (!gate_one) {
+      const float* g = gate_row(p, min(m, p.M - 1)) + nb;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) gv[j] = g[32 * j];
+    }
+    if (m < p.M) {
+      float* xr = p.x + (size_t)m * D + nb;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) xr[32 * j] = xv[e][j] + gv[j] * v[j][e];
+    }
+  }
+}
+
+// The gate row shared by all 128 rows of wave row-block wm, or null when
+// they straddle a segment boundary.
+__device__ __forceinline__ const float* wave_gate(const OutArgs& p, int m0, int wm) {
+  const int first = min(m0 + wm * 128, p.M - 1), last = min(m0 + wm * 128 + 127, p.M - 1);
+  const int s = seg_of(p.segs, first);
+  return s == seg_of(p.segs, last) ? p.mod + (size_t)s * 3 * p.D + 2 * p.D : nullptr;
 }
 
 // x += gate_s * acc for the tile's live rows.
 __device__ __forceinline__ void out_epilogue(const OutArgs& p, const Acc& acc, int m0, int n0,
                                              int wm, int wn, int lane) {
-  const int D = p.D;
-  const int r32 = lane & 31, hi = lane >> 5;
+  const float* g = wave_gate(p, m0, wm);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-#pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const int m = m0 + wm * 128 + i * 32 + 8 * (e >> 2) + 4 * hi + (e & 3);
-      if (m >= p.M) continue;
-      const float* gate = p.mod + (size_t)seg_of(p.segs, m) * 3 * D + 2 * D;
-      float* xr = p.x + (size_t)m * D;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int n = n0 + wn * 128 + j * 32 + r32;
-        xr[n] += gate[n] * acc.c[i][j][e];
-      }
-    }
-  }
+  for (int i = 0; i < 4; ++i) out_rows(p, acc.c[i], i, m0, n0, wm, wn, lane, g);
 }
 
 // Partial slot layout: float4 q = 4 (4 i + j) + g of a lane holds
@@ -638,39 +673,42 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_gemm_out(OutArgs p) {
   const int n_tiles = n_m * n_n;
   const int nk = (p.D + p.F) / BK;
   const int G = p.groups;
-  bool first = true;
-
-  for (int r = 0; r < p.dp_rounds; ++r) {
-    const int L = r * G + blockIdx.x;
-    if (L >= n_tiles) break;
-    int mt, nt;
-    tile_coords(L, n_m, n_n, mt, nt);
-    Src A, B0, B1;
-    out_tile_ptrs(p, mt * BM, nt * BN, wave, A, B0, B1);
-    if (!first) __syncthreads();   // the previous tile's LDS reads are done
-    first = false;
-    Acc acc;
-    gemm_mainloop<true, false, true>(smem, acc, A, B0, p.D / BK, B1, 0, nk);
-    out_epilogue(p, acc, mt * BM, nt * BN, wm, wn, lane);
-  }
-  if (p.tail == 0) return;
-
+  // this workgroup's tail range (empty without a tail)
   SplitK sk;
   sk.nk = nk;
   sk.G = G;
   sk.total = (int64_t)p.tail * nk;
   const int tile0 = p.dp_rounds * G;
   const int v = range_of_block(blockIdx.x, G);
-  const int64_t s_end = sk.start(v + 1);
-  for (int64_t s = sk.start(v); s < s_end;) {
-    const int tt = (int)(s / nk);
-    const int kb = (int)(s - (int64_t)tt * nk);
-    const int ke = (int)min<int64_t>(nk, kb + (s_end - s));
-    int mt, nt;
-    tile_coords(tile0 + tt, n_m, n_n, mt, nt);
+  int64_t s = 0, s_end = 0;
+  if (p.tail > 0) {
+    s = sk.start(v);
+    s_end = sk.start(v + 1);
+  }
+  // one loop over the work items -- whole tiles, then the tail range's
+  // segments -- so that the main loop is instantiated once
+  int r = 0;
+  bool first = true;
+  for (;;) {
+    int mt, nt, kb, ke, tt = 0;
+    if (r < p.dp_rounds && r * G + (int)blockIdx.x < n_tiles) {
+      tile_coords(r * G + blockIdx.x, n_m, n_n, mt, nt);
+      kb = 0;
+      ke = nk;
+      ++r;
+    } else if (s < s_end) {
+      r = p.dp_rounds;
+      tt = (int)(s / nk);
+      kb = (int)(s - (int64_t)tt * nk);
+      ke = (int)min<int64_t>(nk, kb + (s_end - s));
+      tile_coords(tile0 + tt, n_m, n_n, mt, nt);
+      s += ke - kb;
+    } else {
+      break;
+    }
     Src A, B0, B1;
     out_tile_ptrs(p, mt * BM, nt * BN, wave, A, B0, B1);
-    if (!first) __syncthreads();
+    if (!first) __syncthreads();   // the previous item's LDS reads are done
     first = false;
     Acc acc;
     gemm_mainloop<true, false, true>(smem, acc, A, B0, p.D / BK, B1, kb, ke);
@@ -689,7 +727,6 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_gemm_out(OutArgs p) {
                 make_float4(c[4 * g], c[4 * g + 1], c[4 * g + 2], c[4 * g + 3]);
           }
     }
-    s += ke - kb;
   }
 }
 
@@ -698,7 +735,10 @@ constexpr int FIX_SPLIT = 16;   // fixup workgroups per split tile
 // Sums the partials of every tail tile cut by a range boundary, in k order,
 // and applies the epilogue.  Workgroups (i, c) look at the boundary between
 // ranges i and i + 1 and take part c of its tile if no earlier boundary
-// falls inside the tile; a thread handles one float4 of the slot layout.
+// falls inside the tile.  A thread takes the float4s of four neighbouring
+// lanes of one accumulator group -- 4 rows x 4 consecutive columns, 64
+// contiguous bytes of a slot -- so that it updates x with float4 accesses;
+// x and gate are loaded before the partials are summed.
 __global__ __launch_bounds__(NTHREADS) void k_gemm_out_fixup(OutArgs p) {
   const int n_n = p.D / BN;
   const int n_m = p.n_pad / BM;
@@ -714,36 +754,50 @@ __global__ __launch_bounds__(NTHREADS) void k_gemm_out_fixup(OutArgs p) {
   const int v_first = sk.range_of((int64_t)tt * sk.nk);
   const int v_last = sk.range_of((int64_t)(tt + 1) * sk.nk - 1);
 
-  // float4 index inside the slot: (64 w + q) 64 + l
-  const int f = chunk * (BM * BN / 4 / FIX_SPLIT) + threadIdx.x;
+  // float4 f0 .. f0 + 3 of the slot: lanes l0 .. l0 + 3 of group (w, q)
+  const int f0 = 4 * (chunk * NTHREADS + threadIdx.x);
+  const int l0 = f0 & 63, q = (f0 >> 6) & 63, w = f0 >> 12;
+  const int ij = q >> 2, g = q & 3, ii = ij >> 2, jj = ij & 3;
+  int mt, nt;
+  tile_coords(p.dp_rounds * p.groups + tt, n_m, n_n, mt, nt);
+  const int m = mt * BM + (w >> 1) * 128 + ii * 32 + 8 * g + 4 * (l0 >> 5);
+  const int n = nt * BN + (w & 1) * 128 + jj * 32 + (l0 & 31);
+  float4 xv[4], gv[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int mr = min(m + r, p.M - 1);
+    xv[r] = *reinterpret_cast<const float4*>(p.x + (size_t)mr * p.D + n);
+    gv[r] = *reinterpret_cast<const float4*>(gate_row(p, mr) + n);
+  }
   float4 sum[4];
 #pragma unroll
   for (int u = 0; u < 4; ++u) sum[u] = make_float4(0.f, 0.f, 0.f, 0.f);
   for (int v = v_first; v <= v_last; ++v) {
     if (sk.start(v + 1) == sk.start(v)) continue;   // empty range (fewer slices than ranges)
-    const float4* src = slot_base(p, sk.slot(v, tt)) + f;
+    const float4* src = slot_base(p, sk.slot(v, tt)) + f0;
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      const float4 x = src[u * NTHREADS];
+      const float4 x = src[u];
       sum[u].x += x.x;
       sum[u].y += x.y;
       sum[u].z += x.z;
       sum[u].w += x.w;
     }
   }
-  int mt, nt;
-  tile_coords(p.dp_rounds * p.groups + tt, n_m, n_n, mt, nt);
+  // sum[u] holds column n + u, rows m .. m + 3
+  const float c[4][4] = {{sum[0].x, sum[1].x, sum[2].x, sum[3].x},
+                         {sum[0].y, sum[1].y, sum[2].y, sum[3].y},
+                         {sum[0].z, sum[1].z, sum[2].z, sum[3].z},
+                         {sum[0].w, sum[1].w, sum[2].w, sum[3].w}};
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int idx = f + u * NTHREADS;
-    const int l = idx & 63, q = (idx >> 6) & 63, w = idx >> 12;
-    const int ij = q >> 2, g = q & 3, ii = ij >> 2, jj = ij & 3;
-    const int m = mt * BM + (w >> 1) * 128 + ii * 32 + 8 * g + 4 * (l >> 5);
-    const int n = nt * BN + (w & 1) * 128 + jj * 32 + (l & 31);
-    const float vals[4] = {sum[u].x, sum[u].y, sum[u].z, sum[u].w};
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-      if (m + e < p.M) out_update(p, m + e, n, vals[e]);
+  for (int r = 0; r < 4; ++r) {
+    if (m + r >= p.M) continue;
+    float4 o = xv[r];
+    o.x += gv[r].x * c[r][0];
+    o.y += gv[r].y * c[r][1];
+    o.z += gv[r].z * c[r][2];
+    o.w += gv[r].w * c[r][3];
+    *reinterpret_cast<float4*>(p.x + (size_t)(m + r) * p.D + n) = o;
   }
 }
 
