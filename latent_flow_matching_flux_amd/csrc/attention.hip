@@ -483,13 +483,38 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_attention(AttnArgs p) {
   }
 }
 
-// Merges the partial results of every tail unit cut by a range boundary, in
-// range (key) order: m = max m_i, O = sum 2^(m_i - m) O_i, l = sum 2^(m_i -
-// m) l_i, out = O / l.  Workgroup (i, w) looks at the boundary between
-// ranges i and i + 1, takes its unit if no earlier boundary falls inside
-// it, and merges the 32 queries of attention wave w; a thread handles the
-// registers one attention lane held.
-__global__ __launch_bounds__(64) void k_attention_fixup(AttnArgs p) {
+// Merges the partial results of every tail unit cut by a range boundary:
+// m = max m_i, O = sum 2^(m_i - m) O_i, l = sum 2^(m_i - m) l_i, out = O / l.
+// Workgroup (i, w) looks at the boundary between ranges i and i + 1, takes
+// its unit if no earlier boundary falls inside it, and merges the 32
+// queries of attention wave w.  Its NW waves share the unit's pieces (wave
+// k takes pieces k, k + NW, ..., two at a time, folding them into a running
+// (m, l, O) the way the attention loop does); waves 1 .. NW-1 hand their
+// running results to wave 0 through LDS, and wave 0 folds them in, in wave
+// order, and writes the output.  A lane handles the registers one attention
+// lane held.  One wave serves units of a few pieces; four share the many
+// pieces of a unit cut into short ranges.
+
+__device__ __forceinline__ void fold_piece(float& m, float& l, float4 (&acc)[16], float mv, float lv,
+                                           const float4 (&o)[16]) {
+  const float mn = fmaxf(m, mv);
+  const float a = __builtin_amdgcn_exp2f(m - mn), b = __builtin_amdgcn_exp2f(mv - mn);
+  l = a * l + b * lv;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    acc[j].x = a * acc[j].x + b * o[j].x;
+    acc[j].y = a * acc[j].y + b * o[j].y;
+    acc[j].z = a * acc[j].z + b * o[j].z;
+    acc[j].w = a * acc[j].w + b * o[j].w;
+  }
+  m = mn;
+}
+
+template <int NW>
+__global__ __launch_bounds__(64 * NW) void k_attention_fixup(AttnArgs p) {
+  constexpr int NX = NW > 1 ? NW - 1 : 1;   // LDS hand-over slots
+  __shared__ float4 s_acc[NX][16][64];
+  __shared__ float s_m[NX][64], s_l[NX][64];
   const int nqb = (p.M + AQ - 1) / AQ;
   const int nkv = (p.M + AKV - 1) / AKV;
   SplitK sk;
@@ -503,31 +528,53 @@ __global__ __launch_bounds__(64) void k_attention_fixup(AttnArgs p) {
   if (sk.start(i) > (int64_t)u * nkv) return;      // an earlier boundary owns the unit
   const int v_first = sk.range_of((int64_t)u * nkv);
   const int v_last = sk.range_of((int64_t)(u + 1) * nkv - 1);
-  const int lane = threadIdx.x, r32 = lane & 31, hh = lane >> 5;
+  const int k = threadIdx.x >> 6, lane = threadIdx.x & 63, r32 = lane & 31, hh = lane >> 5;
   const int qw = wave * 32 + r32;                  // query within the unit
 
-  float m = -INFINITY;
-  for (int v = v_first; v <= v_last; ++v) {
-    if (sk.start(v + 1) == sk.start(v)) continue;   // empty range
-    m = fmaxf(m, p.part[(size_t)sk.slot(v, u) * 65536 + PART_M + qw]);
-  }
+  // this wave's running merge of pieces v_first + k, + NW, ...  A range of
+  // at least one key tile always holds a live key, so every stored m is
+  // finite; an empty range (start(v + 1) == start(v)) stored nothing.
+  float m = -INFINITY, l = 0.f;
   float4 acc[16];
 #pragma unroll
   for (int j = 0; j < 16; ++j) acc[j] = make_float4(0.f, 0.f, 0.f, 0.f);
-  float l = 0.f;
-  for (int v = v_first; v <= v_last; ++v) {
-    if (sk.start(v + 1) == sk.start(v)) continue;
-    const float* slot = p.part + (size_t)sk.slot(v, u) * 65536;
-    const float w = __builtin_amdgcn_exp2f(slot[PART_M + qw] - m);
-    l += w * slot[PART_L + qw];
-    const float4* so = reinterpret_cast<const float4*>(slot) + (size_t)wave * 16 * 64 + lane;
+  for (int v0 = v_first + k; v0 <= v_last; v0 += 2 * NW) {
+    const int v1 = v0 + NW;
+    const bool has0 = sk.start(v0 + 1) != sk.start(v0);
+    const bool has1 = v1 <= v_last && sk.start(v1 + 1) != sk.start(v1);
+    const float* s0 = p.part + (size_t)sk.slot(has0 ? v0 : v_first, u) * 65536;
+    const float* s1 = p.part + (size_t)sk.slot(has1 ? v1 : v_first, u) * 65536;
+    float4 o0[16], o1[16];
+    const float4* so0 = reinterpret_cast<const float4*>(s0) + (size_t)wave * 16 * 64 + lane;
+    const float4* so1 = reinterpret_cast<const float4*>(s1) + (size_t)wave * 16 * 64 + lane;
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
-      const float4 x = so[j * 64];
-      acc[j].x += w * x.x;
-      acc[j].y += w * x.y;
-      acc[j].z += w * x.z;
-      acc[j].w += w * x.w;
+      o0[j] = so0[j * 64];
+      o1[j] = so1[j * 64];
+    }
+    const float m0 = s0[PART_M + qw], l0 = s0[PART_L + qw];
+    const float m1 = s1[PART_M + qw], l1 = s1[PART_L + qw];
+    if (has0) fold_piece(m, l, acc, m0, l0, o0);
+    if (has1) fold_piece(m, l, acc, m1, l1, o1);
+  }
+  if (NW > 1) {
+    if (k > 0) {
+#pragma unroll
+      for (int j = 0; j < 16; ++j) s_acc[k - 1][j][lane] = acc[j];
+      s_m[k - 1][lane] = m;
+      s_l[k - 1][lane] = l;
+    }
+    __syncthreads();
+    if (k > 0) return;
+    // wave 0 folds in the other waves' results, in wave order
+#pragma unroll
+    for (int w = 0; w < NW - 1; ++w) {
+      const float mw = s_m[w][lane];
+      if (mw == -INFINITY) continue;   // a wave that found no piece
+      float4 ow[16];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) ow[j] = s_acc[w][j][lane];
+      fold_piece(m, l, acc, mw, s_l[w][lane], ow);
     }
   }
   int head, qblk;
@@ -540,13 +587,13 @@ __global__ __launch_bounds__(64) void k_attention_fixup(AttnArgs p) {
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       const float4 x = acc[4 * d + g];
-      bf16x4 v;
-      v[0] = f2bf(x.x * inv);
-      v[1] = f2bf(x.y * inv);
-      v[2] = f2bf(x.z * inv);
-      v[3] = f2bf(x.w * inv);
+      bf16x4 o;
+      o[0] = f2bf(x.x * inv);
+      o[1] = f2bf(x.y * inv);
+      o[2] = f2bf(x.z * inv);
+      o[3] = f2bf(x.w * inv);
       const int col = head * kHeadDim + d * 32 + 8 * g + 4 * hh;
-      *reinterpret_cast<bf16x4*>(p.out + packed_index(qi, col, p.ldo)) = v;
+      *reinterpret_cast<bf16x4*>(p.out + packed_index(qi, col, p.ldo)) = o;
     }
 }
 
@@ -585,7 +632,13 @@ hipError_t launch_attention(const BlockShape& bs, const WsPtrs& ws, hipStream_t 
   hipLaunchKernelGGL(k_attention, dim3(G), dim3(NTHREADS), 0, s, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.tail_ranges < 2) return e;
-  hipLaunchKernelGGL(k_attention_fixup, dim3((p.tail_ranges - 1) * WAVES), dim3(64), 0, s, p);
+  // pieces a unit can be cut into: ranges hold at least items / ranges tiles
+  const int64_t per_range = (int64_t)p.tail * nkv / p.tail_ranges;
+  const int64_t pieces = (nkv + per_range - 1) / per_range + 1;
+  if (pieces <= 4)
+    hipLaunchKernelGGL(k_attention_fixup<1>, dim3((p.tail_ranges - 1) * WAVES), dim3(64), 0, s, p);
+  else
+    hipLaunchKernelGGL(k_attention_fixup<4>, dim3((p.tail_ranges - 1) * WAVES), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 
