@@ -455,12 +455,24 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_gemm_proj(ProjArgs p) {
     __syncthreads();
     typedef const __attribute__((address_space(3))) f32x4 lds_f4;
     const float* nw = kind == 0 ? p.qn : p.kn;
-    bf16* dst = (kind == 0 ? p.q : p.k) + (size_t)(head0 + wm) * p.n_pad * kHeadDim;
+    bf16* dst = (kind == 0 ? p.q : p.k) + (size_t)head0 * p.n_pad * kHeadDim;
+    // the norm weights of this lane's 64 dims, loaded once
+    float4 nwv[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+        nwv[i][g] = *reinterpret_cast<const float4*>(nw + i * 32 + 8 * g + 4 * hi);
+    // Output rows go out through the 32 KiB of LDS past the RoPE rows, one
+    // register block j at a time: the four waves' 32 tokens x 128 dims
+    // (staged row (2 wm + wn) 32 + token, 256 B, 16-byte chunk c in slot
+    // c ^ (row % 16)), then stored as whole rows, 1 KiB per instruction.
+    // A lane's own 8-byte pieces would touch 32 token rows per instruction.
+    constexpr int STAGE = 256 * 512;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int t = wn * 128 + j * 32 + r32;             // token within the tile
-      const int m = m0 + t;
-      const bool live = m < p.M;
+      const bool live = m0 + t < p.M;
       float ss = 0.f;
 #pragma unroll
       for (int i = 0; i < 4; ++i)
@@ -468,13 +480,24 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_gemm_proj(ProjArgs p) {
         for (int e = 0; e < 16; ++e) ss += acc.c[i][j][e] * acc.c[i][j][e];
       ss += xor_lane(ss, 32);
       const float rs = 1.0f / sqrtf(ss * (1.0f / kHeadDim) + p.eps);
+      const int srow = (2 * wm + wn) * 32 + r32;
+      // all of the token's RoPE chunks first: a read placed after a staging
+      // write would wait for it
+      f32x4 csv[4][4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int d0 = i * 32 + 8 * g + 4 * hi;
+          csv[i][g] = *(lds_f4*)(smem + t * 512 + (((d0 >> 2) ^ (t & 31)) << 4));
+        }
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           const int d0 = i * 32 + 8 * g + 4 * hi;          // 4 consecutive dims = 2 pairs
-          const float4 wv = *reinterpret_cast<const float4*>(nw + d0);
-          const f32x4 cs = *(lds_f4*)(smem + t * 512 + (((d0 >> 2) ^ (t & 31)) << 4));   // cos0 sin0 cos1 sin1
+          const float4 wv = nwv[i][g];
+          const f32x4 cs = csv[i][g];                      // cos0 sin0 cos1 sin1
           const float x0 = acc.c[i][j][4 * g + 0] * rs * wv.x;
           const float x1 = acc.c[i][j][4 * g + 1] * rs * wv.y;
           const float x2 = acc.c[i][j][4 * g + 2] * rs * wv.z;
@@ -484,8 +507,19 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_gemm_proj(ProjArgs p) {
           o[1] = f2bf(live ? x0 * cs.y + x1 * cs.x : 0.f);
           o[2] = f2bf(live ? x2 * cs.z - x3 * cs.w : 0.f);
           o[3] = f2bf(live ? x2 * cs.w + x3 * cs.z : 0.f);
-          *reinterpret_cast<bf16x4*>(dst + (size_t)m * kHeadDim + d0) = o;
+          *(lds_bf16x4*)(smem + STAGE + srow * 256 + (((d0 >> 3) ^ (srow & 15)) << 4) + 8 * hi) = o;
         }
+      __syncthreads();
+      // 128 staged rows; wave w stores rows 32 w .. 32 w + 31, 4 per instruction
+#pragma unroll
+      for (int it = 0; it < 8; ++it) {
+        const int row = wave * 32 + it * 4 + (lane >> 4), c = lane & 15;
+        const u32x4 v = *(lds_u32x4*)(smem + STAGE + row * 256 + ((c ^ (row & 15)) << 4));
+        const int run = row >> 5;                        // 2 head + token half
+        const int tok = m0 + (run & 1) * 128 + j * 32 + (row & 31);
+        *reinterpret_cast<u32x4*>(dst + ((size_t)(run >> 1) * p.n_pad + tok) * kHeadDim + c * 8) = v;
+      }
+      if (j < 3) __syncthreads();   // staging free for the next block
     }
   } else if (kind == 2) {
     // values, transposed: staged as [head][dim][256 token positions]
@@ -569,7 +603,7 @@ struct OutArgs {
 // XCD-grouped order of tile_coords.  The first dp_rounds * G of them go
 // whole, G at a time (the workgroups of one XCD then walk the same k
 // slices of neighbouring tiles together and share them in L2).  The last
-// `tail` tiles, when they would leave most of a round idle, are split
+// `tail` tiles, when they would leave over 15% of a round idle, are split
 // stream-K fashion: their k slices, laid end to end (tail tile t owns
 // slices [t nk, (t + 1) nk)), are cut into G equal ranges, range v from
 // start(v) = floor(v total / G).  A tail tile one range covers whole gets
@@ -865,9 +899,10 @@ hipError_t launch_gemm_out(const BlockShape& bs, const BlockWeightsDev& w,
   const int G = p.groups;
   p.dp_rounds = n_tiles / G;
   p.tail = n_tiles % G;
-  // a tail filling most of a round runs whole (its tiles keep sharing L2);
-  // a thin one is spread over all workgroups
-  if (p.tail * 10 > G * 7) {
+  // a tail filling nearly a whole round runs whole (its tiles keep sharing
+  // L2); a thinner one is spread over all workgroups (at 4096 tokens, 192
+  // tiles on 256 CUs: 328 us split against 351 us whole)
+  if (p.tail * 20 > G * 17) {
     p.dp_rounds += 1;
     p.tail = 0;
   }
