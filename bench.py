@@ -11,7 +11,9 @@ concatenated sequence -- on the single-reference edit workload [240 text |
 SwiGLU hidden 9216, bf16 operands with fp32 accumulation and an fp32
 residual stream.  Weights (43 distinct blocks, the timestep embedder and
 6 modulation linears) are seeded random N(0, 0.02^2) in bf16, tokens
-N(0, 1); everything is resident in HBM before timing starts.
+N(0, 1); everything is resident in HBM before timing starts.  The block
+matrices are copied once, at load, into the GEMMs' packed operand layout
+(flux3_weights_pack; --linear-weights keeps torch's Linear layout).
 
 value = block-token passes per second = (5 + 28) * 8432 / step time, the
 rate at which tokens go through transformer blocks.  Per-kernel durations
@@ -157,6 +159,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default="edit8432")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--linear-weights", action="store_true",
+                    help="keep the weights in Linear layout instead of packing them at load")
     ap.add_argument("--no-block", action="store_true",
                     help="skip the single-block timing (profiling runs of the step alone)")
     args = ap.parse_args()
@@ -185,10 +189,15 @@ def main():
         return (torch.randn(*shape, generator=g, device=dev, dtype=torch.float32) * std).to(dtype)
 
     def rand_block():
-        return {"wq": rand(D, D, std=0.02), "wk": rand(D, D, std=0.02), "wv": rand(D, D, std=0.02),
-                "wo": rand(D, D, std=0.02), "w_gate": rand(Fh, D, std=0.02),
-                "w_up": rand(Fh, D, std=0.02), "w_down": rand(D, Fh, std=0.02),
-                "q_norm": torch.ones(128, device=dev), "k_norm": torch.ones(128, device=dev)}
+        w = {"wq": rand(D, D, std=0.02), "wk": rand(D, D, std=0.02), "wv": rand(D, D, std=0.02),
+             "wo": rand(D, D, std=0.02), "w_gate": rand(Fh, D, std=0.02),
+             "w_up": rand(Fh, D, std=0.02), "w_down": rand(D, Fh, std=0.02),
+             "q_norm": torch.ones(128, device=dev), "k_norm": torch.ones(128, device=dev)}
+        if args.linear_weights:
+            return w
+        # static weights go to the GEMMs' packed operand layout once, at load
+        buf = torch.empty(F.weights_packed_bytes(dims), dtype=torch.uint8, device=dev)
+        return F.weights_pack(dims, w, buf)
 
     modes = sorted({s.mode for s in segs})
     per_mode = {m: [rand_block() for _ in range(N_PM)] for m in modes}
@@ -311,7 +320,9 @@ def main():
                                f"{N_JOINT} joint blocks",
                    "tokens": n, "width": D, "heads": dims.heads, "head_dim": dims.head_dim,
                    "mlp_hidden": Fh, "segments": [[s.start, s.count, s.mode] for s in segs],
-                   "t_image": t_image, "t_text": 0.0, "t_reference": 0.0},
+                   "t_image": t_image, "t_text": 0.0, "t_reference": 0.0,
+                   "weight_layout": "linear" if args.linear_weights else
+                   "packed once at load (flux3_weights_pack)"},
         "step_tflops": step_flops / (ms_per_step * 1e-3) / 1e12,
         "step_frac_peak": step_flops / (ms_per_step * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
         "stack_tokens_per_s": n / (ms_per_step / 1e3),

@@ -77,8 +77,13 @@ typedef struct {
   int32_t mode; /* FLUX3_MODE_* */
 } flux3_segment;
 
-/* One block's weights, all device pointers.  Matrices are bf16 in torch
- * Linear layout [out][in], row-major, no biases [P3 block listing; P4]:
+/* Layouts of a block's weight matrices (flux3_block_weights.layout). */
+enum { FLUX3_WEIGHTS_LINEAR = 0, FLUX3_WEIGHTS_PACKED = 1 };
+
+/* One block's weights, all device pointers.  Matrices are bf16, no biases
+ * [P3 block listing; P4], in torch Linear layout [out][in] row-major
+ * (layout = FLUX3_WEIGHTS_LINEAR, the zero value) or in the packed operand
+ * layout that flux3_weights_pack writes (FLUX3_WEIGHTS_PACKED):
  *   wq, wk, wv, wo : [width][width]
  *   w_gate, w_up   : [mlp_hidden][width]   (silu acts on the w_gate branch)
  *   w_down         : [width][mlp_hidden]
@@ -87,7 +92,31 @@ typedef struct {
   const void *wq, *wk, *wv, *wo;
   const void *w_gate, *w_up, *w_down;
   const float *q_norm, *k_norm;
+  int32_t layout;
 } flux3_block_weights;
+
+/* Bytes of one block's seven matrices in the packed operand layout (each
+ * matrix starts on a 256-byte boundary); 0 if dims are unsupported. */
+size_t flux3_weights_packed_bytes(const flux3_dims *dims);
+
+/* Copies one block's Linear-layout matrices into buffer in the packed
+ * operand layout the GEMMs load from (the same layout as the workspace's
+ * packed activations, see flux3_workspace_layout_get): an [R][K] matrix
+ * becomes 1-KiB blocks of 8 rows x 64 k, so that every direct load of the
+ * GEMMs' weight slices moves one contiguous KiB instead of 8 row pieces of
+ * 128 bytes.  Done once per weight set (weights are static); the block
+ * results are bit-identical to those from the Linear layout.
+ *   in     : layout FLUX3_WEIGHTS_LINEAR, all pointers valid and aligned.
+ *   buffer : device, >= flux3_weights_packed_bytes(dims), 256-byte aligned;
+ *            owned by the caller and must outlive every use of *out.
+ *   out    : host struct filled with pointers into buffer, the norm
+ *            pointers of in, and layout FLUX3_WEIGHTS_PACKED.
+ * Asynchronous on stream.  Errors: FLUX3_E_INVALID (null or packed in),
+ * FLUX3_E_UNSUPPORTED (dims), FLUX3_E_ALIGN, FLUX3_E_WORKSPACE (buffer too
+ * small), FLUX3_E_HIP. */
+flux3_status flux3_weights_pack(const flux3_dims *dims, const flux3_block_weights *in,
+                                void *buffer, size_t buffer_bytes, flux3_block_weights *out,
+                                void *stream);
 
 /* Token layout of one call: n_text text tokens, a grid_h x grid_w noisy
  * image grid (raster order), then n_refs reference grids ref_h[k] x ref_w[k]

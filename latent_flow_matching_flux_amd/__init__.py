@@ -9,11 +9,13 @@ from ._lib import (Flux3Error, Dims, Segment, BlockWeights, RopeLayout, Workspac
                    block_forward, stack_forward, set_debug_sync, status_string, EXPORTS,
                    LIB_PATH, KERNELS, profile_enable, profile_reset, profile_read,
                    device_query, modulation_workspace_bytes, modulation_forward,
-                   ModulationWeights)
+                   ModulationWeights, weights_packed_bytes, weights_pack, WEIGHTS_LINEAR,
+                   WEIGHTS_PACKED)
 
 __all__ = ["Flux3Error", "Dims", "Segment", "BlockWeights", "RopeLayout", "WorkspaceLayout",
            "load", "layout_tokens", "rope_tables_build", "workspace_bytes", "workspace_layout",
            "block_forward", "stack_forward", "set_debug_sync", "status_string", "EXPORTS",
            "LIB_PATH", "KERNELS", "profile_enable", "profile_reset", "profile_read",
            "device_query", "modulation_workspace_bytes", "modulation_forward",
-           "ModulationWeights"]
+           "ModulationWeights", "weights_packed_bytes", "weights_pack", "WEIGHTS_LINEAR",
+           "WEIGHTS_PACKED"]

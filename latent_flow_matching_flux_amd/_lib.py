@@ -21,6 +21,7 @@ MAX_REFS = 15
 # exported symbols, in the order include/flux3.h declares them
 EXPORTS = ("flux3_layout_tokens", "flux3_rope_tables_build", "flux3_workspace_bytes",
            "flux3_workspace_layout_get", "flux3_block_forward", "flux3_stack_forward",
+           "flux3_weights_packed_bytes", "flux3_weights_pack",
            "flux3_modulation_workspace_bytes", "flux3_modulation_forward",
            "flux3_profile_enable", "flux3_profile_reset", "flux3_profile_read",
            "flux3_device_query", "flux3_set_debug_sync", "flux3_status_string",
@@ -44,9 +45,13 @@ class Segment(ctypes.Structure):
     _fields_ = [("start", ctypes.c_int32), ("count", ctypes.c_int32), ("mode", ctypes.c_int32)]
 
 
+WEIGHTS_LINEAR, WEIGHTS_PACKED = 0, 1
+MATRICES = ("wq", "wk", "wv", "wo", "w_gate", "w_up", "w_down")
+
+
 class BlockWeights(ctypes.Structure):
-    _fields_ = [(n, ctypes.c_void_p) for n in
-                ("wq", "wk", "wv", "wo", "w_gate", "w_up", "w_down", "q_norm", "k_norm")]
+    _fields_ = [(n, ctypes.c_void_p) for n in MATRICES + ("q_norm", "k_norm")] + \
+               [("layout", ctypes.c_int32)]
 
 
 class ModulationWeights(ctypes.Structure):
@@ -105,6 +110,10 @@ def load(path=LIB_PATH):
     lib.flux3_stack_forward.argtypes = [P(Dims), P(BlockWeights), i32, P(BlockWeights), i32,
                                         vp, i64, P(Segment), i32, vp, vp, i64, vp, vp, sz, vp]
     lib.flux3_stack_forward.restype = i32
+    lib.flux3_weights_packed_bytes.argtypes = [P(Dims)]
+    lib.flux3_weights_packed_bytes.restype = sz
+    lib.flux3_weights_pack.argtypes = [P(Dims), P(BlockWeights), vp, sz, P(BlockWeights), vp]
+    lib.flux3_weights_pack.restype = i32
     lib.flux3_modulation_workspace_bytes.argtypes = [P(Dims)]
     lib.flux3_modulation_workspace_bytes.restype = sz
     lib.flux3_modulation_forward.argtypes = [P(Dims), P(ModulationWeights), P(ctypes.c_float),
@@ -170,11 +179,31 @@ def make_segments(segs):
 
 
 def make_weights(w):
-    """BlockWeights from a dict of tensors (keys as in the header struct)."""
+    """BlockWeights from a dict of tensors (keys as in the header struct; an
+    optional "layout" entry, default WEIGHTS_LINEAR)."""
     if isinstance(w, BlockWeights):
         return w
-    return BlockWeights(*[_ptr(w.get(k)) for k in
-                          ("wq", "wk", "wv", "wo", "w_gate", "w_up", "w_down", "q_norm", "k_norm")])
+    return BlockWeights(*[_ptr(w.get(k)) for k in MATRICES + ("q_norm", "k_norm")],
+                        int(w.get("layout", WEIGHTS_LINEAR)))
+
+
+def weights_packed_bytes(dims):
+    return load().flux3_weights_packed_bytes(ctypes.byref(make_dims(dims)))
+
+
+def weights_pack(dims, w, buffer, stream=None):
+    """flux3_weights_pack: copy a block's Linear-layout matrices into buffer
+    (device, >= weights_packed_bytes(dims) bytes) in the packed operand
+    layout.  Returns the BlockWeights pointing into buffer (layout
+    WEIGHTS_PACKED); buffer must stay alive while it is used."""
+    out = BlockWeights()
+    _check(load().flux3_weights_pack(ctypes.byref(make_dims(dims)), ctypes.byref(make_weights(w)),
+                                     _ptr(buffer), buffer.numel() * buffer.element_size()
+                                     if hasattr(buffer, "numel") else 0,
+                                     ctypes.byref(out), _stream_handle(stream)))
+    # the struct points into buffer and at the caller's norm vectors
+    out._keep = (buffer, w.get("q_norm"), w.get("k_norm")) if isinstance(w, dict) else (buffer, w)
+    return out
 
 
 def make_layout(lay):

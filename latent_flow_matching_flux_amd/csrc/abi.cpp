@@ -117,6 +117,9 @@ flux3_status check_weights(const flux3_block_weights* w, const char* what, int i
     if (!aligned16(ptrs[i]))
       return fail(FLUX3_E_ALIGN, "%s[%d].%s is not 16-byte aligned", what, idx, names[i]);
   }
+  if (w->layout != FLUX3_WEIGHTS_LINEAR && w->layout != FLUX3_WEIGHTS_PACKED)
+    return fail(FLUX3_E_INVALID, "%s[%d].layout %d is not a FLUX3_WEIGHTS_* value", what, idx,
+                w->layout);
   return FLUX3_OK;
 }
 
@@ -177,6 +180,7 @@ flux3::BlockWeightsDev dev_weights(const flux3_block_weights& w) {
   d.wq = w.wq; d.wk = w.wk; d.wv = w.wv; d.wo = w.wo;
   d.w_gate = w.w_gate; d.w_up = w.w_up; d.w_down = w.w_down;
   d.q_norm = w.q_norm; d.k_norm = w.k_norm;
+  d.packed = w.layout == FLUX3_WEIGHTS_PACKED;
   return d;
 }
 
@@ -290,6 +294,48 @@ flux3_status flux3_workspace_layout_get(const flux3_dims* dims, int64_t n_tokens
   if (n_tokens < 0 || n_tokens > kMaxTokens)
     return fail(FLUX3_E_SHAPE, "n_tokens %lld outside [0, %lld]", (long long)n_tokens, (long long)kMaxTokens);
   layout_of(dims, n_tokens, out);
+  return ok();
+}
+
+size_t flux3_weights_packed_bytes(const flux3_dims* dims) {
+  if (check_dims(dims) != FLUX3_OK) return 0;
+  const size_t D = (size_t)dims->width, F = (size_t)dims->mlp_hidden;
+  return 4 * align_up(D * D * 2, kBufAlign) + 3 * align_up(D * F * 2, kBufAlign);
+}
+
+flux3_status flux3_weights_pack(const flux3_dims* dims, const flux3_block_weights* in,
+                                void* buffer, size_t buffer_bytes, flux3_block_weights* out,
+                                void* stream) {
+  flux3_status r = check_dims(dims);
+  if (r != FLUX3_OK) return r;
+  if ((r = check_weights(in, "in", 0)) != FLUX3_OK) return r;
+  if (in->layout != FLUX3_WEIGHTS_LINEAR)
+    return fail(FLUX3_E_INVALID, "in is already packed");
+  if (!out) return fail(FLUX3_E_INVALID, "out is NULL");
+  if (!buffer) return fail(FLUX3_E_WORKSPACE, "buffer is NULL");
+  if ((reinterpret_cast<uintptr_t>(buffer) & (kBufAlign - 1)) != 0)
+    return fail(FLUX3_E_ALIGN, "buffer is not %zu-byte aligned", kBufAlign);
+  const size_t need = flux3_weights_packed_bytes(dims);
+  if (buffer_bytes < need)
+    return fail(FLUX3_E_WORKSPACE, "buffer has %zu bytes, needs %zu", buffer_bytes, need);
+  const int D = dims->width, F = dims->mlp_hidden;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const void* src[7] = {in->wq, in->wk, in->wv, in->wo, in->w_gate, in->w_up, in->w_down};
+  const int rows[7] = {D, D, D, D, F, F, D};
+  const int cols[7] = {D, D, D, D, D, D, F};
+  static const char* names[7] = {"wq", "wk", "wv", "wo", "w_gate", "w_up", "w_down"};
+  void* dst[7];
+  char* b = static_cast<char*>(buffer);
+  for (int i = 0; i < 7; ++i) {
+    dst[i] = b;
+    b += align_up((size_t)rows[i] * cols[i] * 2, kBufAlign);
+    hipError_t e = flux3::launch_pack_rows(src[i], dst[i], rows[i], cols[i], s);
+    if ((r = after_launch(e, names[i], s)) != FLUX3_OK) return r;
+  }
+  *out = *in;
+  out->wq = dst[0]; out->wk = dst[1]; out->wv = dst[2]; out->wo = dst[3];
+  out->w_gate = dst[4]; out->w_up = dst[5]; out->w_down = dst[6];
+  out->layout = FLUX3_WEIGHTS_PACKED;
   return ok();
 }
 

@@ -371,6 +371,9 @@ __device__ __forceinline__ int vt_pos(int m) {
   return (m & ~15) | (gp << 2) | (m & 3);
 }
 
+// PW: the weights come in the packed operand layout (flux3_weights_pack),
+// else in Linear layout.
+template <bool PW>
 __global__ __launch_bounds__(NTHREADS, 1) void k_gemm_proj(ProjArgs p) {
   __shared__ __attribute__((aligned(1024))) unsigned char smem_raw[LDS_BYTES];
   lds_u8* smem = (lds_u8*)smem_raw;
@@ -410,8 +413,8 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_gemm_proj(ProjArgs p) {
   H.hi = H.lo;
   H.ld = 8 * D;
   W.lo = w_run(2 * wave);
-  W.hi = w_run(2 * wave + 1);
-  W.ld = D;
+  W.hi = w_run(2 * wave + 1);   // = lo + 32 D: a wave's 64 rows are consecutive rows of one matrix
+  W.ld = PW ? 8 * D : D;
   // Values use C = h . Wv^T (a lane then holds 4 consecutive tokens of one
   // dim, the order of the transposed store).  Queries, keys and SwiGLU use
   // C^T = W . h^T: a lane holds one token and 4 consecutive features per
@@ -419,9 +422,9 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_gemm_proj(ProjArgs p) {
   // exchange with lane ^ 32, and stores are 8 bytes wide.
   Acc acc;
   if (kind == 2)
-    gemm_mainloop<true, false, true>(smem, acc, H, W, D / BK, W, 0, D / BK);
+    gemm_mainloop<true, PW, true>(smem, acc, H, W, D / BK, W, 0, D / BK);
   else
-    gemm_mainloop<false, true, false>(smem, acc, W, H, D / BK, H, 0, D / BK);
+    gemm_mainloop<PW, true, false>(smem, acc, W, H, D / BK, H, 0, D / BK);
 
   const int r32 = lane & 31, hi = lane >> 5;
   // LDS is free once every wave is past the main loop.  Values and SwiGLU
@@ -682,6 +685,7 @@ __device__ __forceinline__ float4* slot_base(const OutArgs& p, int slot) {
   return reinterpret_cast<float4*>(p.part + (size_t)slot * BM * BN);
 }
 
+template <bool PW>
 __device__ __forceinline__ void out_tile_ptrs(const OutArgs& p, int m0, int n0, int wave, Src& A,
                                               Src& B0, Src& B1) {
   const int D = p.D, F = p.F, ldc = D + F;
@@ -690,12 +694,13 @@ __device__ __forceinline__ void out_tile_ptrs(const OutArgs& p, int m0, int n0, 
   A.ld = 8 * ldc;
   B0.lo = p.wo + (size_t)(n0 + 64 * wave) * D;
   B0.hi = B0.lo + (size_t)32 * D;
-  B0.ld = D;
+  B0.ld = PW ? 8 * D : D;
   B1.lo = p.wd + (size_t)(n0 + 64 * wave) * F;
   B1.hi = B1.lo + (size_t)32 * F;
-  B1.ld = F;
+  B1.ld = PW ? 8 * F : F;
 }
 
+template <bool PW>
 __global__ __launch_bounds__(NTHREADS, 1) void k_gemm_out(OutArgs p) {
   __shared__ __attribute__((aligned(1024))) unsigned char smem_raw[LDS_BYTES];
   lds_u8* smem = (lds_u8*)smem_raw;
@@ -741,11 +746,11 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_gemm_out(OutArgs p) {
       break;
     }
     Src A, B0, B1;
-    out_tile_ptrs(p, mt * BM, nt * BN, wave, A, B0, B1);
+    out_tile_ptrs<PW>(p, mt * BM, nt * BN, wave, A, B0, B1);
     if (!first) __syncthreads();   // the previous item's LDS reads are done
     first = false;
     Acc acc;
-    gemm_mainloop<true, false, true>(smem, acc, A, B0, p.D / BK, B1, kb, ke);
+    gemm_mainloop<true, PW, true>(smem, acc, A, B0, p.D / BK, B1, kb, ke);
     if (kb == 0 && ke == nk) {
       out_epilogue(p, acc, mt * BM, nt * BN, wm, wn, lane);
     } else {
@@ -835,7 +840,28 @@ __global__ __launch_bounds__(NTHREADS) void k_gemm_out_fixup(OutArgs p) {
   }
 }
 
+// Linear-layout [R][K] bf16 matrix -> the packed operand layout, one thread
+// per 16-byte chunk (8 consecutive k-values of one row).
+__global__ __launch_bounds__(256) void k_pack_rows(const bf16* __restrict__ in,
+                                                   bf16* __restrict__ out, int R, int K) {
+  const int64_t cpr = K / 8;
+  const int64_t id = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (id >= (int64_t)R * cpr) return;
+  const int64_t r = id / cpr;
+  const int k = (int)(id - r * cpr) * 8;
+  *reinterpret_cast<u32x4*>(out + packed_index(r, k, K)) =
+      *reinterpret_cast<const u32x4*>(in + r * K + k);
+}
+
 }  // namespace
+
+hipError_t launch_pack_rows(const void* in, void* out, int R, int K, hipStream_t s) {
+  const int64_t chunks = (int64_t)R * (K / 8);
+  if (chunks == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_pack_rows, dim3((unsigned)((chunks + 255) / 256)), dim3(256), 0, s,
+                     static_cast<const bf16*>(in), static_cast<bf16*>(out), R, K);
+  return hipGetLastError();
+}
 
 hipError_t launch_gemm_proj(const BlockShape& bs, const BlockWeightsDev& w,
                             const float* rope, const WsPtrs& ws, float eps,
@@ -862,7 +888,10 @@ hipError_t launch_gemm_proj(const BlockShape& bs, const BlockWeightsDev& w,
   p.eps = eps;
   const int n_n = 3 * (bs.H / 2) + bs.F / 128;
   const int n_m = bs.n_pad / BM;
-  hipLaunchKernelGGL(k_gemm_proj, dim3(n_m * n_n), dim3(NTHREADS), 0, s, p);
+  if (w.packed)
+    hipLaunchKernelGGL(k_gemm_proj<true>, dim3(n_m * n_n), dim3(NTHREADS), 0, s, p);
+  else
+    hipLaunchKernelGGL(k_gemm_proj<false>, dim3(n_m * n_n), dim3(NTHREADS), 0, s, p);
   return hipGetLastError();
 }
 
@@ -906,7 +935,10 @@ hipError_t launch_gemm_out(const BlockShape& bs, const BlockWeightsDev& w,
     p.dp_rounds += 1;
     p.tail = 0;
   }
-  hipLaunchKernelGGL(k_gemm_out, dim3(G), dim3(NTHREADS), 0, s, p);
+  if (w.packed)
+    hipLaunchKernelGGL(k_gemm_out<true>, dim3(G), dim3(NTHREADS), 0, s, p);
+  else
+    hipLaunchKernelGGL(k_gemm_out<false>, dim3(G), dim3(NTHREADS), 0, s, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.tail == 0 || G < 2) return e;
   hipLaunchKernelGGL(k_gemm_out_fixup, dim3((G - 1) * FIX_SPLIT), dim3(NTHREADS), 0, s, p);

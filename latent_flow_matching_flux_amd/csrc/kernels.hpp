@@ -42,7 +42,11 @@ constexpr size_t kSplitSlotBytes = 256 * 256 * 4;
 struct BlockWeightsDev {
   const void *wq, *wk, *wv, *wo, *w_gate, *w_up, *w_down;
   const float *q_norm, *k_norm;
+  bool packed;   // matrices in the packed operand layout
 };
+
+// Linear-layout [R][K] bf16 (R % 8 == 0, K % 64 == 0) -> packed operand layout.
+hipError_t launch_pack_rows(const void* in, void* out, int R, int K, hipStream_t s);
 
 // Timestep path (NEXT-1): distinct timesteps of the used modes first, the
 // flow-map target last when present; t_index[mode] indexes t.

@@ -232,3 +232,37 @@ def test_modulation_workspace_and_validation():
     assert call(nbytes=ws_bytes - 4) == E_WORKSPACE
     assert call(mod=FAKE + 4) == E_ALIGN
     assert call(ws=FAKE + 16) == E_ALIGN
+
+
+def test_weights_pack_sizes_and_validation():
+    lib = F.load()
+    d = _dims()
+    D, Fh = 3072, 9216
+    assert F.weights_packed_bytes(synth.DIMS) == 2 * (4 * D * D + 3 * D * Fh) == 245366784
+    assert lib.flux3_weights_packed_bytes(ctypes.byref(_dims(head_dim=64))) == 0
+    need = F.weights_packed_bytes(synth.DIMS)
+    out = L.BlockWeights()
+
+    def pack(w=None, buf=FAKE + (1 << 32), nbytes=need, o=out, dims=d):
+        return lib.flux3_weights_pack(ctypes.byref(dims), None if w is False else
+                                      ctypes.byref(w if w is not None else _w()), buf, nbytes,
+                                      None if o is None else ctypes.byref(o), 0)
+
+    assert pack(w=False) == E_INVALID                     # no input struct
+    packed = _w()
+    packed.layout = L.WEIGHTS_PACKED
+    assert pack(w=packed) == E_INVALID                    # already packed
+    assert b"already packed" in lib.flux3_last_error_detail()
+    assert pack(o=None) == E_INVALID
+    assert pack(buf=None) == E_WORKSPACE
+    assert pack(buf=FAKE + 16) == E_ALIGN
+    assert pack(nbytes=need - 1) == E_WORKSPACE
+    assert pack(dims=_dims(width=3000)) == E_UNSUPPORTED
+    w = _w()
+    w.w_up = FAKE + 8
+    assert pack(w=w) == E_ALIGN
+    # a block call rejects an unknown layout value before anything runs
+    bad = _w()
+    bad.layout = 7
+    assert _call_block(w=bad) == E_INVALID
+    assert b"layout" in lib.flux3_last_error_detail()
