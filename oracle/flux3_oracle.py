@@ -26,6 +26,9 @@ and axis a owning head dims [32a, 32a+32); image/reference h, w = row/2,
 col/2 taken as real division on the token-grid index (hw_scale = 0.5);
 attention scale 1/sqrt(128); an output projection after attention; no
 biases; SwiGLU with silu on the gate branch; shift, scale, gate order.
+Around the stack: separate input linears for image and reference latent
+tokens; an output layer of LayerNorm (no affine), (shift, scale) from a
+D -> 2D linear of the image timestep's embedding, and a D -> 128 linear.
 
 Precision: float64 by default (pass dtype=np.float32 for the large timing
 runs).  Every function follows its definition directly; the only blocking is
@@ -36,7 +39,8 @@ Parity status per function (pins live in tests/test_oracle_pins.py):
   token_positions, rope_tables, apply_rope, layer_norm, modulate,
   rms_norm_heads, attention, silu, swiglu_mlp, block_forward,
   block_forward_rows, stack_forward, timestep_embedding,
-  modulation_from_t, shifted_sigmas: all pinned.
+  modulation_from_t, shifted_sigmas, euler_step, input_projection,
+  final_modulation, output_layer, transformer_forward: all pinned.
 """
 import numpy as np
 
@@ -340,6 +344,76 @@ def modulation_from_t(t_by_mode, w1, w2, w_mod, t_target=None, w1_tgt=None,
         m = as_float(w_mod[mode], dtype) @ silu(e)
         out[mode] = m.reshape(3, -1)
     return out
+
+
+# --------------------------------------------------------------------------
+# the whole transformer call around the stack
+#   [P1] "Speed, architecture, and how the tokens move" (token kinds, the
+#   20,480-value text vectors, image tokens of 128 values, dropping text and
+#   references at the end); [P4] "The text encoder", "The latent space and
+#   the VAE", "Inside the transformer", "What step distillation removed"
+# --------------------------------------------------------------------------
+def input_projection(text, image, refs, w_text, w_img_in, w_ref_in, dtype=np.float64):
+    """Residual-stream input [text | image | refs] in the sequence order of
+    stage 2: text vectors (8 stacked 2,560-value encoder states = 20,480)
+    through the text linear, image and reference latent tokens (128 values)
+    through their own input linears; no biases.  Returns [N][D]."""
+    parts = []
+    for a, w in ((text, w_text), (image, w_img_in), (refs, w_ref_in)):
+        a = as_float(a, dtype)
+        if a.shape[0]:
+            parts.append(a @ as_float(w, dtype).T)
+    return np.concatenate(parts, axis=0)
+
+
+def final_modulation(t, w1, w2, w_final, t_target=None, w1_tgt=None, w2_tgt=None,
+                     dtype=np.float64):
+    """(shift, scale) of the output layer: the image timestep's embedding (plus
+    the flow-map target embedding, which reaches the output layer too [P4
+    "What step distillation removed"]) through silu and a bias-free D -> 2D
+    linear, split shift then scale.  Returns [2][D]."""
+    e = as_float(w2, dtype) @ silu(as_float(w1, dtype) @ timestep_embedding(t))
+    if t_target is not None:
+        e = e + as_float(w2_tgt, dtype) @ silu(as_float(w1_tgt, dtype) @ timestep_embedding(t_target))
+    return (as_float(w_final, dtype) @ silu(e)).reshape(2, -1)
+
+
+def output_layer(x_img, shift, scale, w_out, dtype=np.float64, eps=EPS_LN):
+    """Image tokens only: LayerNorm without affine, the output modulation,
+    then the bias-free D -> 128 linear back to latent-token size
+    [P4 "Inside the transformer"].  Returns the velocity [n_img][128]."""
+    h = modulate(layer_norm(as_float(x_img, dtype), eps), as_float(shift, dtype),
+                 as_float(scale, dtype))
+    return h @ as_float(w_out, dtype).T
+
+
+def transformer_forward(text, image, refs, segs, io_w, emb_w, w_mod, per_mode, joint, rope,
+                        t, t_target=None, dtype=np.float64):
+    """One transformer call: input projections, the two stages' modulation
+    from the timesteps (image tokens t, text and references 0), the two-stage
+    stack, then the output layer on the image rows.
+
+    io_w: {w_text, w_img_in, w_ref_in, w_final, w_out}; emb_w: {w1, w2} and,
+    for the distilled model, {w1_tgt, w2_tgt}; w_mod[stage][mode] the
+    per-(stage, mode) modulation linears.  segs: (start, count, mode) in the
+    order text, image, references.  Returns the velocity of the image tokens.
+    """
+    x = input_projection(text, image, refs, io_w["w_text"], io_w["w_img_in"],
+                         io_w["w_ref_in"], dtype)
+    modes = sorted({m for _s, _c, m in segs})
+    t_by_mode = {m: (t if m == MODE_IMAGE else 0.0) for m in modes}
+    tgt = dict(t_target=t_target, w1_tgt=emb_w.get("w1_tgt"), w2_tgt=emb_w.get("w2_tgt"))
+    mods = []
+    for stage in range(2):
+        per = modulation_from_t(t_by_mode, emb_w["w1"], emb_w["w2"], w_mod[stage],
+                                dtype=dtype, **tgt)
+        mods.append(np.stack([per[m] for _s, _c, m in segs]))
+    x = stack_forward(x, per_mode, joint, segs, mods[0], mods[1], rope, dtype=dtype)
+    shift, scale = final_modulation(t, emb_w["w1"], emb_w["w2"], io_w["w_final"], dtype=dtype,
+                                    **tgt)
+    img = [(st, c) for st, c, m in segs if m == MODE_IMAGE]
+    rows = np.concatenate([np.arange(st, st + c) for st, c in img])
+    return output_layer(x[rows], shift, scale, io_w["w_out"], dtype)
 
 
 # --------------------------------------------------------------------------

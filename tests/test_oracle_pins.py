@@ -537,3 +537,95 @@ def test_euler_step_and_x0():
     for i in range(16):
         y = O.euler_step(y, v, s[i], s[i + 1])
     np.testing.assert_allclose(y, x - v, atol=1e-12)
+
+
+# --------------------------------------------------------------------------
+# the transformer call around the stack: input linears, output layer
+# --------------------------------------------------------------------------
+def _io_case(D=128, text_dim=96, lat=32):
+    io = {"w_text": _rand(D, text_dim) * 0.05, "w_img_in": _rand(D, lat) * 0.05,
+          "w_ref_in": _rand(D, lat) * 0.05, "w_final": _rand(2 * D, D) * 0.05,
+          "w_out": _rand(lat, D) * 0.05}
+    emb = {"w1": _rand(D, 256) * 0.05, "w2": _rand(D, D) * 0.05,
+           "w1_tgt": _rand(D, 256) * 0.05, "w2_tgt": _rand(D, D) * 0.05}
+    w_mod = [{m: _rand(3 * D, D) * 0.05 for m in range(3)} for _ in range(2)]
+    return io, emb, w_mod
+
+
+def test_input_projection_vs_torch_linear():
+    io, _emb, _wm = _io_case()
+    text, image, refs = _rand(3, 96), _rand(4, 32), _rand(4, 32)
+    x = O.input_projection(text, image, refs, io["w_text"], io["w_img_in"], io["w_ref_in"])
+    lin = torch.nn.functional.linear
+    want = torch.cat([lin(torch.from_numpy(a), torch.from_numpy(io[k]))
+                      for a, k in ((text, "w_text"), (image, "w_img_in"), (refs, "w_ref_in"))])
+    np.testing.assert_allclose(x, want.numpy(), rtol=1e-13, atol=1e-13)
+    # each token kind goes through its own matrix, in the order text, image, refs
+    z = O.input_projection(text, image, refs, io["w_text"], np.zeros_like(io["w_img_in"]),
+                           io["w_ref_in"])
+    assert np.all(z[3:7] == 0) and np.array_equal(z[:3], x[:3]) and np.array_equal(z[7:], x[7:])
+
+
+def test_output_layer_vs_torch_and_special_cases():
+    io, _emb, _wm = _io_case()
+    x = _rand(5, 128) * 3 + 1
+    zero = np.zeros(128)
+    v = O.output_layer(x, zero, zero, io["w_out"])
+    xt = torch.from_numpy(x)
+    ln = torch.nn.functional.layer_norm(xt, (128,), eps=1e-6)
+    want = torch.nn.functional.linear(ln, torch.from_numpy(io["w_out"])).numpy()
+    np.testing.assert_allclose(v, want, rtol=1e-12, atol=1e-12)
+    assert v.shape == (5, 32)
+    # scale = -1 removes the normalised input: every token gets shift . w_out
+    shift = _rand(128)
+    v = O.output_layer(x, shift, -np.ones(128), io["w_out"])
+    np.testing.assert_allclose(v, np.tile(io["w_out"] @ shift, (5, 1)), rtol=1e-12, atol=1e-12)
+
+
+def test_final_modulation_shares_the_embedder():
+    _io, emb, w_mod = _io_case()
+    # with the first two thirds of the image-mode linear, the output layer's
+    # (shift, scale) equal that mode's (shift, scale)
+    wf = w_mod[1][1][:256]
+    for t, tt in ((0.3, None), (0.7, 0.4)):
+        kw = dict(t_target=tt, w1_tgt=emb["w1_tgt"], w2_tgt=emb["w2_tgt"]) if tt is not None else {}
+        got = O.final_modulation(t, emb["w1"], emb["w2"], wf, **kw)
+        ref = O.modulation_from_t({1: t}, emb["w1"], emb["w2"], w_mod[1], **kw)[1]
+        np.testing.assert_array_equal(got, ref[:2])
+    # it follows the image timestep (unlike text and reference modulation)
+    a = O.final_modulation(0.2, emb["w1"], emb["w2"], _io_case()[0]["w_final"])
+    b = O.final_modulation(0.9, emb["w1"], emb["w2"], _io_case()[0]["w_final"])
+    assert not np.allclose(a, b)
+
+
+def _transformer_case(n_pm, n_joint):
+    D, per_mode, joint, segs, tab = _stack_case(n_pm=n_pm, n_joint=n_joint)
+    io, emb, w_mod = _io_case(D)
+    text, image, refs = _rand(3, 96), _rand(4, 32), _rand(4, 32)
+    return D, per_mode, joint, segs, tab, io, emb, w_mod, text, image, refs
+
+
+def test_transformer_without_blocks_is_output_layer_of_image_inputs():
+    D, per_mode, _j, segs, tab, io, emb, w_mod, text, image, refs = _transformer_case(0, 0)
+    per_mode = {m: [] for m in range(3)}
+    v = O.transformer_forward(text, image, refs, segs, io, emb, w_mod, per_mode, [], tab, t=0.6)
+    x_img = torch.nn.functional.linear(torch.from_numpy(image), torch.from_numpy(io["w_img_in"]))
+    shift, scale = O.final_modulation(0.6, emb["w1"], emb["w2"], io["w_final"])
+    h = torch.nn.functional.layer_norm(x_img, (D,), eps=1e-6) * (1 + torch.from_numpy(scale)) \
+        + torch.from_numpy(shift)
+    want = torch.nn.functional.linear(h, torch.from_numpy(io["w_out"])).numpy()
+    np.testing.assert_allclose(v, want, rtol=1e-12, atol=1e-12)
+
+
+def test_transformer_stage_structure():
+    D, per_mode, joint, segs, tab, io, emb, w_mod, text, image, refs = _transformer_case(1, 1)
+    run = lambda tx, rf, jt: O.transformer_forward(tx, image, rf, segs, io, emb, w_mod, per_mode,
+                                                   jt, tab, t=0.5, t_target=0.25)
+    a = run(text, refs, [])
+    # stage 1 alone: the image velocity ignores the text and the reference
+    np.testing.assert_array_equal(a, run(text + 1.0, refs * 2.0, []))
+    # a joint block lets both reach it
+    b = run(text, refs, joint)
+    assert not np.allclose(b, run(text + 1.0, refs, joint))
+    assert not np.allclose(b, run(text, refs * 2.0, joint))
+    assert a.shape == (4, 32)
