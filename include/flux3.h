@@ -277,6 +277,81 @@ flux3_status flux3_modulation_forward(const flux3_dims *dims,
                                       float *mod, void *workspace,
                                       size_t workspace_bytes, void *stream);
 
+/* ---------------------------------------------------------------------------
+ * One whole transformer call: the block stack with the linears around it
+ * ("Speed, architecture, and how the tokens move", 15jq.com post: text
+ * tokens as 20,480-value vectors, noisy image and reference tokens of 128
+ * values, text and references dropped at the end; "The text encoder", "The
+ * latent space and the VAE", "Inside the transformer", rohitghumare.com
+ * guide: a linear to width 3072 for the text, an output linear from 3072
+ * back to 128; no biases anywhere):
+ *   x      = [text W_text^T | image W_img_in^T | refs W_ref_in^T]   (fp32)
+ *   mod_1, mod_2 = each stage's modulation from t (image) and 0 (text,
+ *            references), plus the target embedding when t_target >= 0
+ *   x      = stack(x)                            (flux3_stack_forward)
+ *   (shift, scale) = W_final silu(E(t) + E'(t_target))
+ *   v      = ((1 + scale) LayerNorm(x_image) + shift) W_out^T
+ * The inputs are rounded to bf16, the GEMM operand type, on the device; the
+ * residual stream and the velocity are fp32.
+ * ------------------------------------------------------------------------- */
+
+/* Token vector sizes at the call's edges: text_dim = 20480 (8 stacked
+ * 2,560-value text-encoder states), latent_dim = 128 (one 2x2 patch of the
+ * 32-channel latent).  text_dim % 64 == 0; latent_dim % 64 == 0 and
+ * latent_dim <= 256. */
+typedef struct {
+  int32_t text_dim;
+  int32_t latent_dim;
+} flux3_io_dims;
+
+/* The linears around the stack, bf16 in torch Linear layout [out][in]:
+ *   w_text   [width][text_dim]     (may be NULL without text tokens)
+ *   w_img_in [width][latent_dim]
+ *   w_ref_in [width][latent_dim]   (may be NULL without reference tokens;
+ *                                   pass w_img_in to share one input linear)
+ *   w_final  [2 width][width]      output layer (shift, scale)
+ *   w_out    [latent_dim][width] */
+typedef struct {
+  const void *w_text, *w_img_in, *w_ref_in, *w_final, *w_out;
+} flux3_io_weights;
+
+/* Workspace bytes flux3_transformer_forward needs for n_tokens tokens: the
+ * block workspace (flux3_workspace_bytes) plus the fp32 residual stream,
+ * the bf16 input staging, the modulation vectors and their workspace; 0 if
+ * dims are unsupported. */
+size_t flux3_transformer_workspace_bytes(const flux3_dims *dims, const flux3_io_dims *io_dims,
+                                         int64_t n_tokens);
+
+/* One transformer call; writes the velocity of the image tokens.
+ *   mod_w   : host [2]: stage 1 and stage 2 modulation weights (see
+ *             flux3_modulation_weights); the output layer uses stage 2's
+ *             embedder (w1, w2 and, with a target, w1_tgt, w2_tgt).
+ *   per_mode, n_pm, joint, n_joint: the blocks, as for flux3_stack_forward.
+ *   text    : device bf16 [n_text][text_dim] (the rows of the mode-0
+ *             segment; NULL if there is none).
+ *   image   : device fp32 [n_image][latent_dim], the noisy latent tokens.
+ *   refs    : device fp32 [n_ref][latent_dim], the reference tokens of all
+ *             mode-2 segments in order (NULL if there are none).
+ *   segs    : host; at most one text segment, exactly one image segment,
+ *             then any reference segments, tiling [0, n_tokens).
+ *   t       : the image timestep (sigma in [0, 1]); t_target < 0 for the
+ *             base model, else the flow-map target timestep.
+ *   rope    : device fp32 [n_tokens][64][2] for the call's layout.
+ *   velocity: device fp32 [n_image][latent_dim] out.
+ *   workspace: device, >= flux3_transformer_workspace_bytes, 256-byte
+ *             aligned.
+ * Errors as for flux3_stack_forward and flux3_modulation_forward; on error
+ * nothing is enqueued. */
+flux3_status flux3_transformer_forward(const flux3_dims *dims, const flux3_io_dims *io_dims,
+                                       const flux3_io_weights *io,
+                                       const flux3_modulation_weights *mod_w,
+                                       const flux3_block_weights *per_mode, int32_t n_pm,
+                                       const flux3_block_weights *joint, int32_t n_joint,
+                                       const void *text, const float *image, const float *refs,
+                                       const flux3_segment *segs, int32_t n_segs, float t,
+                                       float t_target, const float *rope, float *velocity,
+                                       void *workspace, size_t workspace_bytes, void *stream);
+
 /* Kernel timing, for benchmarks and profiling.  While enabled, every kernel
  * launch is bracketed by a pair of HIP events recorded on the launch stream,
  * so the durations are those of the kernels themselves on the stream they
@@ -293,7 +368,8 @@ enum {
   FLUX3_K_ATTENTION = 3,
   FLUX3_K_GEMM_OUT = 4,
   FLUX3_K_MODULATION = 5,   /* one record per flux3_modulation_forward call */
-  FLUX3_K_COUNT = 6
+  FLUX3_K_IO_LINEARS = 6,   /* each input / output linear of a transformer call */
+  FLUX3_K_COUNT = 7
 };
 typedef struct {
   int64_t launches;

@@ -10,7 +10,8 @@ from ._lib import (Flux3Error, Dims, Segment, BlockWeights, RopeLayout, Workspac
                    LIB_PATH, KERNELS, profile_enable, profile_reset, profile_read,
                    device_query, modulation_workspace_bytes, modulation_forward,
                    ModulationWeights, weights_packed_bytes, weights_pack, WEIGHTS_LINEAR,
-                   WEIGHTS_PACKED)
+                   WEIGHTS_PACKED, IoDims, IoWeights, transformer_workspace_bytes,
+                   transformer_forward)
 
 __all__ = ["Flux3Error", "Dims", "Segment", "BlockWeights", "RopeLayout", "WorkspaceLayout",
            "load", "layout_tokens", "rope_tables_build", "workspace_bytes", "workspace_layout",
@@ -18,4 +19,5 @@ __all__ = ["Flux3Error", "Dims", "Segment", "BlockWeights", "RopeLayout", "Works
            "LIB_PATH", "KERNELS", "profile_enable", "profile_reset", "profile_read",
            "device_query", "modulation_workspace_bytes", "modulation_forward",
            "ModulationWeights", "weights_packed_bytes", "weights_pack", "WEIGHTS_LINEAR",
-           "WEIGHTS_PACKED"]
+           "WEIGHTS_PACKED", "IoDims", "IoWeights", "transformer_workspace_bytes",
+           "transformer_forward"]

@@ -22,11 +22,13 @@ MAX_REFS = 15
 EXPORTS = ("flux3_layout_tokens", "flux3_rope_tables_build", "flux3_workspace_bytes",
            "flux3_workspace_layout_get", "flux3_block_forward", "flux3_stack_forward",
            "flux3_weights_packed_bytes", "flux3_weights_pack",
+           "flux3_transformer_workspace_bytes", "flux3_transformer_forward",
            "flux3_modulation_workspace_bytes", "flux3_modulation_forward",
            "flux3_profile_enable", "flux3_profile_reset", "flux3_profile_read",
            "flux3_device_query", "flux3_set_debug_sync", "flux3_status_string",
            "flux3_last_error_detail")
-KERNELS = ("rope_tables", "ln_modulate", "gemm_proj", "attention", "gemm_out", "modulation")
+KERNELS = ("rope_tables", "ln_modulate", "gemm_proj", "attention", "gemm_out", "modulation",
+           "io_linears")
 
 
 class Flux3Error(RuntimeError):
@@ -57,6 +59,14 @@ class BlockWeights(ctypes.Structure):
 class ModulationWeights(ctypes.Structure):
     _fields_ = [("w1", ctypes.c_void_p), ("w2", ctypes.c_void_p), ("w1_tgt", ctypes.c_void_p),
                 ("w2_tgt", ctypes.c_void_p), ("w_mod", ctypes.c_void_p * 3)]
+
+
+class IoDims(ctypes.Structure):
+    _fields_ = [("text_dim", ctypes.c_int32), ("latent_dim", ctypes.c_int32)]
+
+
+class IoWeights(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in ("w_text", "w_img_in", "w_ref_in", "w_final", "w_out")]
 
 
 class RopeLayout(ctypes.Structure):
@@ -114,6 +124,13 @@ def load(path=LIB_PATH):
     lib.flux3_weights_packed_bytes.restype = sz
     lib.flux3_weights_pack.argtypes = [P(Dims), P(BlockWeights), vp, sz, P(BlockWeights), vp]
     lib.flux3_weights_pack.restype = i32
+    lib.flux3_transformer_workspace_bytes.argtypes = [P(Dims), P(IoDims), i64]
+    lib.flux3_transformer_workspace_bytes.restype = sz
+    lib.flux3_transformer_forward.argtypes = [P(Dims), P(IoDims), P(IoWeights),
+                                              P(ModulationWeights), P(BlockWeights), i32,
+                                              P(BlockWeights), i32, vp, vp, vp, P(Segment), i32,
+                                              ctypes.c_float, ctypes.c_float, vp, vp, vp, sz, vp]
+    lib.flux3_transformer_forward.restype = i32
     lib.flux3_modulation_workspace_bytes.argtypes = [P(Dims)]
     lib.flux3_modulation_workspace_bytes.restype = sz
     lib.flux3_modulation_forward.argtypes = [P(Dims), P(ModulationWeights), P(ctypes.c_float),
@@ -309,6 +326,61 @@ def modulation_forward(dims, w, t_by_mode, segs, mod, workspace, t_target=None,
                                            -1.0 if t_target is None else float(t_target),
                                            seg_arr, n_segs, _ptr(mod), _ptr(workspace),
                                            workspace_nbytes, _stream_handle(stream)))
+
+
+def _modulation_weights(w):
+    wm = w.get("w_mod", {})
+    mods = [wm.get(m) if isinstance(wm, dict) else wm[m] for m in range(3)]
+    return ModulationWeights(_ptr(w.get("w1")), _ptr(w.get("w2")), _ptr(w.get("w1_tgt")),
+                             _ptr(w.get("w2_tgt")), (ctypes.c_void_p * 3)(*[_ptr(t) for t in mods]))
+
+
+def make_io_dims(d):
+    if isinstance(d, IoDims):
+        return d
+    return IoDims(d.text_dim, d.latent_dim)
+
+
+def transformer_workspace_bytes(dims, io_dims, n_tokens):
+    return load().flux3_transformer_workspace_bytes(ctypes.byref(make_dims(dims)),
+                                                    ctypes.byref(make_io_dims(io_dims)), n_tokens)
+
+
+def _block_arrays(per_mode, joint):
+    if isinstance(per_mode, dict):
+        n_pm = max((len(v) for v in per_mode.values()), default=0)
+        flat = []
+        for m in range(3):
+            blocks = per_mode.get(m, [])
+            for b in range(n_pm):
+                flat.append(make_weights(blocks[b]) if b < len(blocks) else BlockWeights())
+    else:
+        flat = [make_weights(w) for w in per_mode]
+        n_pm = len(flat) // 3
+    pm_arr = (BlockWeights * max(len(flat), 1))(*flat)
+    jt = [make_weights(w) for w in joint]
+    jt_arr = (BlockWeights * max(len(jt), 1))(*jt)
+    return pm_arr, n_pm, jt_arr, len(jt)
+
+
+def transformer_forward(dims, io_dims, io_w, mod_w, per_mode, joint, text, image, refs, segs, t,
+                        rope, velocity, workspace, t_target=None, workspace_nbytes=None,
+                        stream=None):
+    """flux3_transformer_forward.  io_w: dict with w_text, w_img_in, w_ref_in,
+    w_final, w_out; mod_w: two modulation weight dicts (stage 1, stage 2) as
+    for modulation_forward; per_mode / joint as for stack_forward."""
+    io = IoWeights(*[_ptr(io_w.get(k)) for k in ("w_text", "w_img_in", "w_ref_in", "w_final",
+                                                  "w_out")])
+    mw = (ModulationWeights * 2)(_modulation_weights(mod_w[0]), _modulation_weights(mod_w[1]))
+    pm_arr, n_pm, jt_arr, n_joint = _block_arrays(per_mode, joint)
+    seg_arr, n_segs = make_segments(segs)
+    if workspace_nbytes is None:
+        workspace_nbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(load().flux3_transformer_forward(
+        ctypes.byref(make_dims(dims)), ctypes.byref(make_io_dims(io_dims)), ctypes.byref(io), mw,
+        pm_arr, n_pm, jt_arr, n_joint, _ptr(text), _ptr(image), _ptr(refs), seg_arr, n_segs,
+        float(t), -1.0 if t_target is None else float(t_target), _ptr(rope), _ptr(velocity),
+        _ptr(workspace), workspace_nbytes, _stream_handle(stream)))
 
 
 def profile_enable(on):

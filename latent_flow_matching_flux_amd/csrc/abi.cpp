@@ -7,6 +7,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <algorithm>
 #include <cmath>
 
 #include <vector>
@@ -228,6 +229,185 @@ flux3_status run_block(const flux3_dims* d, const flux3_block_weights& w, float*
   return FLUX3_OK;
 }
 
+
+// Validates one stage's modulation inputs for the segments (already
+// checked) and fills the launch description.  Nothing is enqueued.
+flux3_status prepare_modulation(const flux3_dims* dims, const flux3_modulation_weights* w,
+                                const float* t_by_mode, float t_target,
+                                const flux3_segment* segs, int32_t n_segs,
+                                flux3::ModulationShape* ms, flux3::ModulationWeightsDev* wd,
+                                int32_t* seg_mode) {
+  const int D = dims->width;
+  if (D > 4096) return fail(FLUX3_E_UNSUPPORTED, "modulation supports width <= 4096, got %d", D);
+  if (!w) return fail(FLUX3_E_INVALID, "modulation weights struct is NULL");
+  if (!t_by_mode) return fail(FLUX3_E_INVALID, "t_by_mode is NULL");
+  const void* mats[4] = {w->w1, w->w2, w->w1_tgt, w->w2_tgt};
+  static const char* names[4] = {"w1", "w2", "w1_tgt", "w2_tgt"};
+  if (t_target != t_target) return fail(FLUX3_E_INVALID, "t_target is NaN");
+  const bool target = t_target >= 0.f;
+  for (int i = 0; i < (target ? 4 : 2); ++i) {
+    if (!mats[i]) return fail(FLUX3_E_INVALID, "%s is NULL", names[i]);
+    if (!aligned16(mats[i])) return fail(FLUX3_E_ALIGN, "%s is not 16-byte aligned", names[i]);
+  }
+  if (target && !std::isfinite(t_target)) return fail(FLUX3_E_INVALID, "t_target is not finite");
+  // distinct timesteps of the modes in use, in mode order; the target last
+  memset(ms, 0, sizeof *ms);
+  ms->D = D;
+  bool used[3] = {false, false, false};
+  for (int i = 0; i < n_segs; ++i) {
+    seg_mode[i] = segs[i].mode;
+    used[segs[i].mode] = true;
+  }
+  for (int m = 0; m < 3; ++m) {
+    if (!used[m]) continue;
+    if (!w->w_mod[m]) return fail(FLUX3_E_INVALID, "w_mod[%d] is NULL but a segment uses mode %d", m, m);
+    if (!aligned16(w->w_mod[m])) return fail(FLUX3_E_ALIGN, "w_mod[%d] is not 16-byte aligned", m);
+    const float t = t_by_mode[m];
+    if (!std::isfinite(t)) return fail(FLUX3_E_INVALID, "t_by_mode[%d] is not finite", m);
+    int j = 0;
+    while (j < ms->n_t && ms->t[j] != t) ++j;
+    if (j == ms->n_t) ms->t[ms->n_t++] = t;
+    ms->t_index[m] = j;
+  }
+  if (target) {
+    ms->has_target = 1;
+    ms->t[ms->n_t] = t_target;
+  }
+  wd->w1 = w->w1;
+  wd->w2 = w->w2;
+  wd->w1_tgt = w->w1_tgt;
+  wd->w2_tgt = w->w2_tgt;
+  for (int m = 0; m < 3; ++m) wd->w_mod[m] = w->w_mod[m];
+  wd->w_final = nullptr;
+  return FLUX3_OK;
+}
+
+// Weight checks of a stack's blocks for the segments in use.
+flux3_status check_stack_weights(const flux3_block_weights* per_mode, int32_t n_pm,
+                                 const flux3_block_weights* joint, int32_t n_joint,
+                                 const flux3_segment* segs, int32_t n_segs) {
+  flux3_status r;
+  if (n_pm > 0) {
+    if (!per_mode) return fail(FLUX3_E_INVALID, "per_mode is NULL");
+    for (int s = 0; s < n_segs; ++s)
+      for (int b = 0; b < n_pm; ++b)
+        if ((r = check_weights(&per_mode[segs[s].mode * n_pm + b], "per_mode",
+                               segs[s].mode * n_pm + b)) != FLUX3_OK)
+          return r;
+  }
+  if (n_joint > 0) {
+    if (!joint) return fail(FLUX3_E_INVALID, "joint is NULL");
+    for (int b = 0; b < n_joint; ++b)
+      if ((r = check_weights(&joint[b], "joint", b)) != FLUX3_OK) return r;
+  }
+  return FLUX3_OK;
+}
+
+// Enqueues the two stages on validated arguments.
+flux3_status run_stack(const flux3_dims* dims, const flux3_block_weights* per_mode, int32_t n_pm,
+                       const flux3_block_weights* joint, int32_t n_joint, float* x,
+                       int64_t n_tokens, const flux3_segment* segs, int32_t n_segs,
+                       const flux3::SegTableHost& st, const float* mod_stage1,
+                       const float* mod_stage2, int64_t mod_block_stride, const float* rope,
+                       void* workspace, hipStream_t s) {
+  flux3_status r;
+  const size_t D = (size_t)dims->width;
+  // stage 1: each segment runs its own mode's blocks on its rows alone
+  for (int sg = 0; sg < n_segs && n_pm > 0; ++sg) {
+    flux3::SegTableHost one;
+    memset(&one, 0, sizeof one);
+    one.n = 1;
+    const int64_t start = segs[sg].start, cnt = segs[sg].count;
+    for (int b = 0; b < n_pm; ++b) {
+      const float* m1 = mod_stage1 + (size_t)b * mod_block_stride + (size_t)sg * 3 * D;
+      r = run_block(dims, per_mode[segs[sg].mode * n_pm + b], x + start * D, cnt, one, m1,
+                    rope + start * 128, workspace, s);
+      if (r != FLUX3_OK) return r;
+    }
+  }
+  // stage 2: joint blocks over the whole sequence
+  for (int b = 0; b < n_joint; ++b) {
+    r = run_block(dims, joint[b], x, n_tokens, st, mod_stage2 + (size_t)b * mod_block_stride,
+                  rope, workspace, s);
+    if (r != FLUX3_OK) return r;
+  }
+  return FLUX3_OK;
+}
+
+// Byte layout of flux3_transformer_forward's workspace.
+struct TransformerLayout {
+  size_t block, x, stage, w_out, mod1, mod2, mod_final, mod_ws, total;
+  int64_t text_pad, img_pad, ref_pad;
+};
+
+int64_t pad256(int64_t v) { return (v + 255) / 256 * 256; }
+
+void transformer_layout(const flux3_dims* d, const flux3_io_dims* io, int64_t n, int n_segs,
+                        int64_t n_text, int64_t n_img, int64_t n_ref, TransformerLayout* L) {
+  const size_t D = (size_t)d->width;
+  L->text_pad = pad256(n_text);
+  L->img_pad = pad256(n_img);
+  L->ref_pad = pad256(n_ref);
+  size_t off = 0;
+  L->block = off;
+  flux3_workspace_layout wl;
+  layout_of(d, n, &wl);
+  off = align_up(wl.total, kBufAlign);
+  L->x = off;
+  off = align_up(off + (size_t)n * D * 4, kBufAlign);
+  L->stage = off;
+  size_t stage = std::max((size_t)L->text_pad * io->text_dim,
+                          (size_t)std::max(L->img_pad, L->ref_pad) * io->latent_dim) * 2;
+  off = align_up(off + stage, kBufAlign);
+  L->w_out = off;
+  off = align_up(off + 256 * D * 2, kBufAlign);
+  L->mod1 = off;
+  off = align_up(off + (size_t)n_segs * 3 * D * 4, kBufAlign);
+  L->mod2 = off;
+  off = align_up(off + (size_t)n_segs * 3 * D * 4, kBufAlign);
+  L->mod_final = off;
+  off = align_up(off + 3 * D * 4, kBufAlign);
+  L->mod_ws = off;
+  off = align_up(off + flux3::modulation_workspace_floats((int)D) * 4, kBufAlign);
+  L->total = off;
+}
+
+// Pieces per tile for a split linear: enough workgroups to cover the CUs,
+// at least 4 k slices per piece, partials within the block workspace's
+// split-partial region.
+int split_pieces(int64_t m_pad, int64_t n_pad, int K) {
+  const int64_t tiles = (m_pad / 256) * (n_pad / 256);
+  const int nk = K / 64;
+  int S = (int)std::max<int64_t>(1, (256 + tiles - 1) / tiles);
+  S = std::min(S, std::max(1, nk / 4));
+  const size_t budget = 2 * (size_t)flux3::kMaxSplitGroups * flux3::kSplitSlotBytes;
+  while (S > 1 && (size_t)S * m_pad * n_pad * 4 > budget) --S;
+  return S;
+}
+
+// One input or output linear through the split GEMM.
+flux3_status io_linear(const void* a_packed, const void* w, bool w_packed, int64_t M,
+                       int64_t m_pad, int N, int n_pad, int K, float* out, int ldo, float* part,
+                       hipStream_t s) {
+  flux3::SplitGemm g;
+  g.a = a_packed;
+  g.w = w;
+  g.w_packed = w_packed;
+  g.part = part;
+  g.out = out;
+  g.M = (int)M;
+  g.m_pad = (int)m_pad;
+  g.N = N;
+  g.n_pad = n_pad;
+  g.K = K;
+  g.S = split_pieces(m_pad, n_pad, K);
+  g.ldo = ldo;
+  const int pi = prof_begin(FLUX3_K_IO_LINEARS, (double)M, s);
+  hipError_t e = flux3::launch_gemm_split(g, s);
+  prof_end(pi, s);
+  return after_launch(e, "io_linear", s);
+}
+
 }  // namespace
 
 extern "C" {
@@ -384,48 +564,22 @@ flux3_status flux3_stack_forward(const flux3_dims* dims, const flux3_block_weigh
   flux3::SegTableHost st;
   if ((r = check_segments(segs, n_segs, n_tokens, &st)) != FLUX3_OK) return r;
   if (n_pm > 0) {
-    if (!per_mode) return fail(FLUX3_E_INVALID, "per_mode is NULL");
     if (!mod_stage1) return fail(FLUX3_E_INVALID, "mod_stage1 is NULL");
     if (!aligned16(mod_stage1)) return fail(FLUX3_E_ALIGN, "mod_stage1 is not 16-byte aligned");
-    for (int s = 0; s < n_segs; ++s)
-      for (int b = 0; b < n_pm; ++b)
-        if ((r = check_weights(&per_mode[segs[s].mode * n_pm + b], "per_mode",
-                               segs[s].mode * n_pm + b)) != FLUX3_OK)
-          return r;
   }
   if (n_joint > 0) {
-    if (!joint) return fail(FLUX3_E_INVALID, "joint is NULL");
     if (!mod_stage2) return fail(FLUX3_E_INVALID, "mod_stage2 is NULL");
     if (!aligned16(mod_stage2)) return fail(FLUX3_E_ALIGN, "mod_stage2 is not 16-byte aligned");
-    for (int b = 0; b < n_joint; ++b)
-      if ((r = check_weights(&joint[b], "joint", b)) != FLUX3_OK) return r;
   }
+  if ((r = check_stack_weights(per_mode, n_pm, joint, n_joint, segs, n_segs)) != FLUX3_OK) return r;
   if (mod_block_stride % 4 != 0)
     return fail(FLUX3_E_ALIGN, "mod_block_stride must be a multiple of 4 floats");
   flux3_workspace_layout L;
   if ((r = check_ws(dims, n_tokens, workspace, workspace_bytes, &L)) != FLUX3_OK) return r;
-
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  const size_t D = (size_t)dims->width;
-  // stage 1: each segment runs its own mode's blocks on its rows alone
-  for (int sg = 0; sg < n_segs && n_pm > 0; ++sg) {
-    flux3::SegTableHost one;
-    memset(&one, 0, sizeof one);
-    one.n = 1;
-    const int64_t start = segs[sg].start, cnt = segs[sg].count;
-    for (int b = 0; b < n_pm; ++b) {
-      const float* m1 = mod_stage1 + (size_t)b * mod_block_stride + (size_t)sg * 3 * D;
-      r = run_block(dims, per_mode[segs[sg].mode * n_pm + b], x + start * D, cnt, one, m1,
-                    rope + start * 128, workspace, s);
-      if (r != FLUX3_OK) return r;
-    }
-  }
-  // stage 2: joint blocks over the whole sequence
-  for (int b = 0; b < n_joint; ++b) {
-    r = run_block(dims, joint[b], x, n_tokens, st, mod_stage2 + (size_t)b * mod_block_stride,
-                  rope, workspace, s);
-    if (r != FLUX3_OK) return r;
-  }
+  if ((r = run_stack(dims, per_mode, n_pm, joint, n_joint, x, n_tokens, segs, n_segs, st,
+                     mod_stage1, mod_stage2, mod_block_stride, rope, workspace,
+                     static_cast<hipStream_t>(stream))) != FLUX3_OK)
+    return r;
   return ok();
 }
 
@@ -434,55 +588,26 @@ size_t flux3_modulation_workspace_bytes(const flux3_dims* dims) {
   return align_up(flux3::modulation_workspace_floats(dims->width) * sizeof(float), kBufAlign);
 }
 
+
+
 flux3_status flux3_modulation_forward(const flux3_dims* dims, const flux3_modulation_weights* w,
                                       const float* t_by_mode, float t_target,
                                       const flux3_segment* segs, int32_t n_segs, float* mod,
                                       void* workspace, size_t workspace_bytes, void* stream) {
   flux3_status r = check_dims(dims);
   if (r != FLUX3_OK) return r;
-  const int D = dims->width;
-  if (D > 4096) return fail(FLUX3_E_UNSUPPORTED, "modulation supports width <= 4096, got %d", D);
-  if (!w) return fail(FLUX3_E_INVALID, "weights struct is NULL");
-  if (!t_by_mode) return fail(FLUX3_E_INVALID, "t_by_mode is NULL");
   if (!segs || n_segs < 1) return fail(FLUX3_E_SHAPE, "n_segs %d (need >= 1) or segs NULL", n_segs);
+  if (n_segs > FLUX3_MAX_SEGMENTS) return fail(FLUX3_E_SHAPE, "n_segs %d > %d", n_segs, FLUX3_MAX_SEGMENTS);
   const int64_t n = (int64_t)segs[n_segs - 1].start + segs[n_segs - 1].count;
   if (n < 1 || n > kMaxTokens) return fail(FLUX3_E_SHAPE, "segments cover %lld tokens", (long long)n);
   flux3::SegTableHost st;
   if ((r = check_segments(segs, n_segs, n, &st)) != FLUX3_OK) return r;
-  const void* mats[4] = {w->w1, w->w2, w->w1_tgt, w->w2_tgt};
-  static const char* names[4] = {"w1", "w2", "w1_tgt", "w2_tgt"};
-  if (t_target != t_target) return fail(FLUX3_E_INVALID, "t_target is NaN");
-  const bool target = t_target >= 0.f;
-  for (int i = 0; i < (target ? 4 : 2); ++i) {
-    if (!mats[i]) return fail(FLUX3_E_INVALID, "%s is NULL", names[i]);
-    if (!aligned16(mats[i])) return fail(FLUX3_E_ALIGN, "%s is not 16-byte aligned", names[i]);
-  }
-  if (target && !std::isfinite(t_target)) return fail(FLUX3_E_INVALID, "t_target is not finite");
-  // distinct timesteps of the modes in use, in mode order; the target last
   flux3::ModulationShape ms;
-  memset(&ms, 0, sizeof ms);
-  ms.D = D;
+  flux3::ModulationWeightsDev wd;
   int32_t seg_mode[FLUX3_MAX_SEGMENTS];
-  bool used[3] = {false, false, false};
-  for (int i = 0; i < n_segs; ++i) {
-    seg_mode[i] = segs[i].mode;
-    used[segs[i].mode] = true;
-  }
-  for (int m = 0; m < 3; ++m) {
-    if (!used[m]) continue;
-    if (!w->w_mod[m]) return fail(FLUX3_E_INVALID, "w_mod[%d] is NULL but a segment uses mode %d", m, m);
-    if (!aligned16(w->w_mod[m])) return fail(FLUX3_E_ALIGN, "w_mod[%d] is not 16-byte aligned", m);
-    const float t = t_by_mode[m];
-    if (!std::isfinite(t)) return fail(FLUX3_E_INVALID, "t_by_mode[%d] is not finite", m);
-    int j = 0;
-    while (j < ms.n_t && ms.t[j] != t) ++j;
-    if (j == ms.n_t) ms.t[ms.n_t++] = t;
-    ms.t_index[m] = j;
-  }
-  if (target) {
-    ms.has_target = 1;
-    ms.t[ms.n_t] = t_target;
-  }
+  if ((r = prepare_modulation(dims, w, t_by_mode, t_target, segs, n_segs, &ms, &wd, seg_mode)) !=
+      FLUX3_OK)
+    return r;
   if (!mod) return fail(FLUX3_E_INVALID, "mod is NULL");
   if (!aligned16(mod)) return fail(FLUX3_E_ALIGN, "mod is not 16-byte aligned");
   const size_t need = flux3_modulation_workspace_bytes(dims);
@@ -491,17 +616,155 @@ flux3_status flux3_modulation_forward(const flux3_dims* dims, const flux3_modula
     return fail(FLUX3_E_ALIGN, "workspace is not %zu-byte aligned", kBufAlign);
   if (workspace_bytes < need)
     return fail(FLUX3_E_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, need);
-  flux3::ModulationWeightsDev wd;
-  wd.w1 = w->w1;
-  wd.w2 = w->w2;
-  wd.w1_tgt = w->w1_tgt;
-  wd.w2_tgt = w->w2_tgt;
-  for (int m = 0; m < 3; ++m) wd.w_mod[m] = w->w_mod[m];
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int pi = prof_begin(FLUX3_K_MODULATION, (double)n, s);
   hipError_t e = flux3::launch_modulation(ms, wd, st, seg_mode, mod, static_cast<float*>(workspace), s);
   prof_end(pi, s);
   if ((r = after_launch(e, "modulation", s)) != FLUX3_OK) return r;
+  return ok();
+}
+
+size_t flux3_transformer_workspace_bytes(const flux3_dims* dims, const flux3_io_dims* io_dims,
+                                         int64_t n_tokens) {
+  if (check_dims(dims) != FLUX3_OK || !io_dims || io_dims->text_dim <= 0 ||
+      io_dims->text_dim % 64 != 0 || io_dims->latent_dim <= 0 || io_dims->latent_dim % 64 != 0 ||
+      io_dims->latent_dim > 256 || n_tokens < 0 || n_tokens > kMaxTokens)
+    return 0;
+  TransformerLayout L;
+  // sized for the worst split of n_tokens between text, image and references
+  transformer_layout(dims, io_dims, n_tokens, FLUX3_MAX_SEGMENTS, n_tokens, n_tokens, n_tokens, &L);
+  return L.total;
+}
+
+flux3_status flux3_transformer_forward(const flux3_dims* dims, const flux3_io_dims* io_dims,
+                                       const flux3_io_weights* io,
+                                       const flux3_modulation_weights* mod_w,
+                                       const flux3_block_weights* per_mode, int32_t n_pm,
+                                       const flux3_block_weights* joint, int32_t n_joint,
+                                       const void* text, const float* image, const float* refs,
+                                       const flux3_segment* segs, int32_t n_segs, float t,
+                                       float t_target, const float* rope, float* velocity,
+                                       void* workspace, size_t workspace_bytes, void* stream) {
+  flux3_status r = check_dims(dims);
+  if (r != FLUX3_OK) return r;
+  if (!io_dims) return fail(FLUX3_E_INVALID, "io_dims is NULL");
+  const int TD = io_dims->text_dim, LD = io_dims->latent_dim;
+  if (TD <= 0 || TD % 64 != 0)
+    return fail(FLUX3_E_UNSUPPORTED, "text_dim %d unsupported (positive multiple of 64)", TD);
+  if (LD <= 0 || LD % 64 != 0 || LD > 256)
+    return fail(FLUX3_E_UNSUPPORTED, "latent_dim %d unsupported (multiple of 64, <= 256)", LD);
+  if (!io) return fail(FLUX3_E_INVALID, "io weights struct is NULL");
+  if (!mod_w) return fail(FLUX3_E_INVALID, "mod_w is NULL");
+  if (n_pm < 0 || n_joint < 0) return fail(FLUX3_E_SHAPE, "n_pm %d / n_joint %d negative", n_pm, n_joint);
+  if (!segs || n_segs < 1 || n_segs > FLUX3_MAX_SEGMENTS)
+    return fail(FLUX3_E_SHAPE, "n_segs %d outside [1, %d] or segs NULL", n_segs, FLUX3_MAX_SEGMENTS);
+  const int64_t n = (int64_t)segs[n_segs - 1].start + segs[n_segs - 1].count;
+  if (n < 1 || n > kMaxTokens) return fail(FLUX3_E_SHAPE, "segments cover %lld tokens", (long long)n);
+  flux3::SegTableHost st;
+  if ((r = check_segments(segs, n_segs, n, &st)) != FLUX3_OK) return r;
+  int64_t n_text = 0, n_img = 0, n_ref = 0;
+  int img_seg = -1, text_segs = 0;
+  for (int i = 0; i < n_segs; ++i) {
+    if (segs[i].mode == FLUX3_MODE_TEXT) { n_text += segs[i].count; ++text_segs; }
+    if (segs[i].mode == FLUX3_MODE_IMAGE) {
+      if (img_seg >= 0) return fail(FLUX3_E_SHAPE, "more than one image segment");
+      img_seg = i;
+      n_img = segs[i].count;
+    }
+    if (segs[i].mode == FLUX3_MODE_REF) n_ref += segs[i].count;
+  }
+  if (img_seg < 0) return fail(FLUX3_E_SHAPE, "no image segment");
+  if (text_segs > 1) return fail(FLUX3_E_SHAPE, "more than one text segment");
+  // weights and inputs
+  struct { const void* p; const char* name; bool need; } req[] = {
+      {io->w_text, "w_text", n_text > 0}, {io->w_img_in, "w_img_in", true},
+      {io->w_ref_in, "w_ref_in", n_ref > 0}, {io->w_final, "w_final", true},
+      {io->w_out, "w_out", true},         {text, "text", n_text > 0},
+      {image, "image", true},             {refs, "refs", n_ref > 0},
+      {rope, "rope", true},               {velocity, "velocity", true}};
+  for (const auto& q : req) {
+    if (!q.need) continue;
+    if (!q.p) return fail(FLUX3_E_INVALID, "%s is NULL", q.name);
+    if (!aligned16(q.p)) return fail(FLUX3_E_ALIGN, "%s is not 16-byte aligned", q.name);
+  }
+  if (!std::isfinite(t)) return fail(FLUX3_E_INVALID, "t is not finite");
+  if ((r = check_stack_weights(per_mode, n_pm, joint, n_joint, segs, n_segs)) != FLUX3_OK) return r;
+  flux3::ModulationShape ms[2];
+  flux3::ModulationWeightsDev wd[2];
+  int32_t seg_mode[FLUX3_MAX_SEGMENTS];
+  const float t_by_mode[3] = {0.f, t, 0.f};
+  for (int k = 0; k < 2; ++k)
+    if ((r = prepare_modulation(dims, &mod_w[k], t_by_mode, t_target, segs, n_segs, &ms[k], &wd[k],
+                                seg_mode)) != FLUX3_OK)
+      return r;
+  wd[1].w_final = io->w_final;
+  TransformerLayout L;
+  transformer_layout(dims, io_dims, n, n_segs, n_text, n_img, n_ref, &L);
+  if (!workspace) return fail(FLUX3_E_WORKSPACE, "workspace is NULL");
+  if ((reinterpret_cast<uintptr_t>(workspace) & (kBufAlign - 1)) != 0)
+    return fail(FLUX3_E_ALIGN, "workspace is not %zu-byte aligned", kBufAlign);
+  if (workspace_bytes < L.total)
+    return fail(FLUX3_E_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, L.total);
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* base = static_cast<char*>(workspace);
+  flux3_workspace_layout bl;
+  layout_of(dims, n, &bl);
+  const flux3::WsPtrs wp = carve(base + L.block, bl);
+  float* part = static_cast<float*>(wp.part);
+  float* x = reinterpret_cast<float*>(base + L.x);
+  void* stage = base + L.stage;
+  const int D = dims->width;
+  hipError_t e;
+  // input projections into the residual stream, in sequence order
+  const int64_t img0 = segs[img_seg].start;
+  struct { const void* in; bool f32; int64_t rows, pad, row0; int K; const void* w; } inp[3] = {
+      {text, false, n_text, L.text_pad, 0, TD, io->w_text},
+      {image, true, n_img, L.img_pad, img0, LD, io->w_img_in},
+      {refs, true, n_ref, L.ref_pad, img0 + n_img, LD, io->w_ref_in}};
+  for (const auto& q : inp) {
+    if (q.rows == 0) continue;
+    e = flux3::launch_pack_input(q.in, q.f32, stage, (int)q.rows, (int)q.pad, q.K, s);
+    if ((r = after_launch(e, "pack_input", s)) != FLUX3_OK) return r;
+    if ((r = io_linear(stage, q.w, false, q.rows, q.pad, D, D, q.K, x + q.row0 * D, D, part, s)) !=
+        FLUX3_OK)
+      return r;
+  }
+  // both stages' modulation; stage 2 also gives the output layer's
+  float* mod1 = reinterpret_cast<float*>(base + L.mod1);
+  float* mod2 = reinterpret_cast<float*>(base + L.mod2);
+  float* modf = reinterpret_cast<float*>(base + L.mod_final);
+  float* mws = reinterpret_cast<float*>(base + L.mod_ws);
+  for (int k = 0; k < 2; ++k) {
+    const int pi = prof_begin(FLUX3_K_MODULATION, (double)n, s);
+    e = flux3::launch_modulation(ms[k], wd[k], st, seg_mode, k ? mod2 : mod1, mws, s,
+                                 k ? modf : nullptr);
+    prof_end(pi, s);
+    if ((r = after_launch(e, "modulation", s)) != FLUX3_OK) return r;
+  }
+  if ((r = run_stack(dims, per_mode, n_pm, joint, n_joint, x, n, segs, n_segs, st, mod1, mod2, 0,
+                     rope, base + L.block, s)) != FLUX3_OK)
+    return r;
+  // output layer on the image rows: modulated LayerNorm into h, then W_out
+  flux3::BlockShape bs;
+  bs.M = (int32_t)n_img;
+  bs.n_pad = (int32_t)L.img_pad;
+  bs.D = D;
+  bs.H = dims->heads;
+  bs.F = dims->mlp_hidden;
+  flux3::SegTableHost one;
+  memset(&one, 0, sizeof one);
+  one.n = 1;
+  int pi = prof_begin(FLUX3_K_LN_MODULATE, (double)n_img, s);
+  e = flux3::launch_ln_modulate(bs, x + img0 * D, modf, one, wp.h, kEpsLN, s);
+  prof_end(pi, s);
+  if ((r = after_launch(e, "ln_modulate", s)) != FLUX3_OK) return r;
+  void* w_out = base + L.w_out;   // W_out packed, zero rows up to 256
+  e = flux3::launch_pack_input(io->w_out, false, w_out, LD, 256, D, s);
+  if ((r = after_launch(e, "pack_input", s)) != FLUX3_OK) return r;
+  if ((r = io_linear(wp.h, w_out, true, n_img, L.img_pad, LD, 256, D, velocity, LD, part, s)) !=
+      FLUX3_OK)
+    return r;
   return ok();
 }
 

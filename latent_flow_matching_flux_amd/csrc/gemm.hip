@@ -853,6 +853,111 @@ __global__ __launch_bounds__(256) void k_pack_rows(const bf16* __restrict__ in,
       *reinterpret_cast<const u32x4*>(in + r * K + k);
 }
 
+// ---------------------------------------------------------------------------
+// Linears around the block stack (input projections, output projection):
+// C[M][N] = A[M][K] W[N][K]^T with A in the packed layout (rows up to m_pad,
+// the padding zero) and W Linear or packed (rows up to n_pad).  A tile's k
+// slices may be cut into S equal pieces, each its own workgroup, when the
+// tiles alone would leave most CUs idle (the 240 x 20480 text projection
+// has 12 tiles); pieces store fp32 partial tiles and k_split_reduce adds them
+// in piece order.  With S = 1 the tile is stored straight to C.
+struct SplitArgs {
+  const bf16* a;
+  const bf16* w;
+  float* part;    // [S][m_pad][n_pad] when S > 1
+  float* out;     // C rows m < M, columns n < N, row stride ldo, when S == 1
+  int M, m_pad, N, n_pad, K, S, ldo;
+};
+
+template <bool PB>
+__global__ __launch_bounds__(NTHREADS, 1) void k_gemm_split(SplitArgs p) {
+  __shared__ __attribute__((aligned(1024))) unsigned char smem_raw[LDS_BYTES];
+  lds_u8* smem = (lds_u8*)smem_raw;
+  const int t = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6), lane = t & 63;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int n_m = p.m_pad / BM, n_n = p.n_pad / BN, tiles = n_m * n_n;
+  const int piece = blockIdx.x / tiles;
+  int mt, nt;
+  tile_coords(blockIdx.x - piece * tiles, n_m, n_n, mt, nt);
+  const int m0 = mt * BM, n0 = nt * BN;
+  const int nk = p.K / BK;
+  const int kb = (int)((int64_t)nk * piece / p.S), ke = (int)((int64_t)nk * (piece + 1) / p.S);
+  Src A, B;
+  A.lo = p.a + (size_t)(m0 + 64 * wave) * p.K;
+  A.hi = A.lo;
+  A.ld = 8 * p.K;
+  B.lo = p.w + (size_t)(n0 + 64 * wave) * p.K;
+  B.hi = B.lo + (size_t)32 * p.K;
+  B.ld = PB ? 8 * p.K : p.K;
+  Acc acc;
+  gemm_mainloop<true, PB, true>(smem, acc, A, B, nk, B, kb, ke);
+  const int nb = n0 + wn * 128 + (lane & 31);
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int m = m0 + wm * 128 + i * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+      if (p.S == 1) {
+        if (m >= p.M) continue;
+        float* row = p.out + (size_t)m * p.ldo;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          if (nb + 32 * j < p.N) row[nb + 32 * j] = acc.c[i][j][e];
+      } else {
+        float* row = p.part + ((size_t)piece * p.m_pad + m) * p.n_pad;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) row[nb + 32 * j] = acc.c[i][j][e];
+      }
+    }
+}
+
+// C[m][n] = sum over pieces, in piece order; one thread per float4 of C.
+__global__ __launch_bounds__(256) void k_split_reduce(SplitArgs p) {
+  const int n4 = p.N / 4;
+  const int64_t id = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (id >= (int64_t)p.M * n4) return;
+  const int m = (int)(id / n4), n = (int)(id - (int64_t)m * n4) * 4;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int s = 0; s < p.S; ++s) {
+    const float4 v =
+        *reinterpret_cast<const float4*>(p.part + ((size_t)s * p.m_pad + m) * p.n_pad + n);
+    acc.x += v.x;
+    acc.y += v.y;
+    acc.z += v.z;
+    acc.w += v.w;
+  }
+  *reinterpret_cast<float4*>(p.out + (size_t)m * p.ldo + n) = acc;
+}
+
+// Rows [0, M) of a row-major [M][K] fp32 or bf16 matrix -> packed bf16
+// [m_pad][K] (fp32 rounded to nearest even), rows [M, m_pad) zero; one
+// thread per 8-value chunk.
+template <bool F32>
+__global__ __launch_bounds__(256) void k_pack_input(const void* __restrict__ in,
+                                                    bf16* __restrict__ out, int M, int m_pad,
+                                                    int K) {
+  const int64_t cpr = K / 8;
+  const int64_t id = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (id >= (int64_t)m_pad * cpr) return;
+  const int64_t r = id / cpr;
+  const int k = (int)(id - r * cpr) * 8;
+  u32x4 v = {0u, 0u, 0u, 0u};
+  if (r < M) {
+    if constexpr (F32) {
+      const float4* src = reinterpret_cast<const float4*>(static_cast<const float*>(in) + r * K + k);
+      const float4 a = src[0], b = src[1];
+      bf16x8 h;
+      h[0] = f2bf(a.x); h[1] = f2bf(a.y); h[2] = f2bf(a.z); h[3] = f2bf(a.w);
+      h[4] = f2bf(b.x); h[5] = f2bf(b.y); h[6] = f2bf(b.z); h[7] = f2bf(b.w);
+      v = *reinterpret_cast<const u32x4*>(&h);
+    } else {
+      v = *reinterpret_cast<const u32x4*>(static_cast<const bf16*>(in) + r * K + k);
+    }
+  }
+  *reinterpret_cast<u32x4*>(out + packed_index(r, k, K)) = v;
+}
+
 }  // namespace
 
 hipError_t launch_pack_rows(const void* in, void* out, int R, int K, hipStream_t s) {
@@ -860,6 +965,46 @@ hipError_t launch_pack_rows(const void* in, void* out, int R, int K, hipStream_t
   if (chunks == 0) return hipSuccess;
   hipLaunchKernelGGL(k_pack_rows, dim3((unsigned)((chunks + 255) / 256)), dim3(256), 0, s,
                      static_cast<const bf16*>(in), static_cast<bf16*>(out), R, K);
+  return hipGetLastError();
+}
+
+hipError_t launch_pack_input(const void* in, bool in_fp32, void* out, int M, int m_pad, int K,
+                             hipStream_t s) {
+  const int64_t chunks = (int64_t)m_pad * (K / 8);
+  if (chunks == 0) return hipSuccess;
+  const dim3 grid((unsigned)((chunks + 255) / 256));
+  if (in_fp32)
+    hipLaunchKernelGGL(k_pack_input<true>, grid, dim3(256), 0, s, in, static_cast<bf16*>(out), M,
+                       m_pad, K);
+  else
+    hipLaunchKernelGGL(k_pack_input<false>, grid, dim3(256), 0, s, in, static_cast<bf16*>(out), M,
+                       m_pad, K);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_split(const SplitGemm& g, hipStream_t s) {
+  SplitArgs p;
+  p.a = static_cast<const bf16*>(g.a);
+  p.w = static_cast<const bf16*>(g.w);
+  p.part = g.part;
+  p.out = g.out;
+  p.M = g.M;
+  p.m_pad = g.m_pad;
+  p.N = g.N;
+  p.n_pad = g.n_pad;
+  p.K = g.K;
+  p.S = g.S;
+  p.ldo = g.ldo;
+  if (g.M == 0) return hipSuccess;
+  const unsigned grid = (unsigned)((g.m_pad / BM) * (g.n_pad / BN) * g.S);
+  if (g.w_packed)
+    hipLaunchKernelGGL(k_gemm_split<true>, dim3(grid), dim3(NTHREADS), 0, s, p);
+  else
+    hipLaunchKernelGGL(k_gemm_split<false>, dim3(grid), dim3(NTHREADS), 0, s, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || g.S == 1) return e;
+  const int64_t n = (int64_t)g.M * (g.N / 4);
+  hipLaunchKernelGGL(k_split_reduce, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 

@@ -48,6 +48,25 @@ struct BlockWeightsDev {
 // Linear-layout [R][K] bf16 (R % 8 == 0, K % 64 == 0) -> packed operand layout.
 hipError_t launch_pack_rows(const void* in, void* out, int R, int K, hipStream_t s);
 
+// Rows [0, M) of a row-major fp32 (in_fp32) or bf16 [M][K] matrix -> packed
+// bf16 [m_pad][K], padding rows zero (M <= m_pad, m_pad % 8 == 0, K % 64 == 0).
+hipError_t launch_pack_input(const void* in, bool in_fp32, void* out, int M, int m_pad, int K,
+                             hipStream_t s);
+
+// C[M][N] (fp32, row stride ldo) = A W^T: A packed bf16 [m_pad][K], W bf16
+// [n_pad][K] (packed or Linear), m_pad and n_pad multiples of 256, K of 64,
+// N of 4.  S > 1 cuts each tile's k slices into S pieces summed through part
+// ([S][m_pad][n_pad] fp32) in piece order.
+struct SplitGemm {
+  const void* a;
+  const void* w;
+  bool w_packed;
+  float* part;
+  float* out;
+  int M, m_pad, N, n_pad, K, S, ldo;
+};
+hipError_t launch_gemm_split(const SplitGemm& g, hipStream_t s);
+
 // Timestep path (NEXT-1): distinct timesteps of the used modes first, the
 // flow-map target last when present; t_index[mode] indexes t.
 struct ModulationShape {
@@ -61,12 +80,15 @@ struct ModulationShape {
 struct ModulationWeightsDev {
   const void *w1, *w2, *w1_tgt, *w2_tgt;
   const void* w_mod[3];
+  const void* w_final;   // output layer's (shift, scale) linear [2D][D], with final_mod
 };
 
 size_t modulation_workspace_floats(int D);
+// mod[segment] = (shift, scale, gate) of the segment's mode; with final_mod
+// (image mode in use) also the output layer's (shift, scale) from w.w_final.
 hipError_t launch_modulation(const ModulationShape& ms, const ModulationWeightsDev& w,
                              const SegTableHost& segs, const int32_t* seg_mode, float* mod,
-                             float* ws, hipStream_t s);
+                             float* ws, hipStream_t s, float* final_mod = nullptr);
 
 hipError_t launch_rope_tables(const RopeLayoutDev& lay, float* rope, int64_t n,
                               hipStream_t s);

@@ -274,7 +274,7 @@ size_t modulation_workspace_floats(int D) {
 // vectors), e [4][D] (E per timestep, E' of the target last).
 hipError_t launch_modulation(const ModulationShape& ms, const ModulationWeightsDev& w,
                              const SegTableHost& segs, const int32_t* seg_mode, float* mod,
-                             float* ws, hipStream_t s) {
+                             float* ws, hipStream_t s, float* final_mod) {
   const int D = ms.D;
   const int nt = ms.n_t;
   float* emb = ws;                        // [4][256]
@@ -322,7 +322,13 @@ hipError_t launch_modulation(const ModulationShape& ms, const ModulationWeightsD
     }
     if (jb.nv) p.job[nj++] = jb;
   }
-  return launch_gemv(p, nj, D, 1, s);
+  if ((r = launch_gemv(p, nj, D, 1, s)) != hipSuccess) return r;
+  if (!final_mod) return hipSuccess;
+  // output layer: final_mod = W_final silu(e[t_index[image]] + e[nt]), 2 D rows
+  p.y = final_mod;
+  p.job[0] = job(w.w_final, 2 * D, 1, ms.t_index[1] * D, 0, 0);
+  p.job[0].x_add_off = ms.has_target ? nt * D : -1;
+  return launch_gemv(p, 1, D, 1, s);
 }
 
 }  // namespace flux3

@@ -7,8 +7,10 @@ share any of the computation they are compared on.
 """
 from .configs import DIMS, Dims, Segment, RopeLayout, WORKLOADS, workload
 from .gen import (bf16_round_bits, bf16_bits_to_f32, block_weights, tokens,
-                  modulation, modulation_weights, WEIGHT_STD, MOD_STD)
+                  modulation, modulation_weights, io_weights, edge_inputs, TEXT_DIM,
+                  LATENT_DIM, WEIGHT_STD, MOD_STD)
 
 __all__ = ["DIMS", "Dims", "Segment", "RopeLayout", "WORKLOADS", "workload",
            "bf16_round_bits", "bf16_bits_to_f32", "block_weights", "tokens",
-           "modulation", "modulation_weights", "WEIGHT_STD", "MOD_STD"]
+           "modulation", "modulation_weights", "io_weights", "edge_inputs", "TEXT_DIM",
+           "LATENT_DIM", "WEIGHT_STD", "MOD_STD"]

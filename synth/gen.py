@@ -104,3 +104,34 @@ def modulation(seed, stream, n_segs, width, std=MOD_STD):
     a = _rng(seed, _MOD_STREAM, stream, n_segs, width).standard_normal(
         (n_segs, 3, width), dtype=np.float32)
     return a * np.float32(std)
+
+
+# the linears around the stack and the call's edge inputs
+_IO_STREAM = 4_000_000
+T_IO_TEXT, T_IO_IMG, T_IO_REF, T_IO_FINAL, T_IO_OUT = range(5)
+_EDGE_STREAM = 5_000_000
+T_IN_TEXT, T_IN_IMAGE, T_IN_REFS = range(3)
+TEXT_DIM, LATENT_DIM = 20480, 128
+
+
+def io_weights(seed, width, text_dim=TEXT_DIM, latent_dim=LATENT_DIM, std=WEIGHT_STD):
+    """The transformer call's own linears as bf16 bits, torch-Linear layout:
+    w_text [width][text_dim], w_img_in and w_ref_in [width][latent_dim],
+    w_final [2*width][width], w_out [latent_dim][width]; N(0, std^2)."""
+    D = width
+    return {"w_text": _normal_bf16((D, text_dim), std, seed, _IO_STREAM, T_IO_TEXT),
+            "w_img_in": _normal_bf16((D, latent_dim), std, seed, _IO_STREAM, T_IO_IMG),
+            "w_ref_in": _normal_bf16((D, latent_dim), std, seed, _IO_STREAM, T_IO_REF),
+            "w_final": _normal_bf16((2 * D, D), std, seed, _IO_STREAM, T_IO_FINAL),
+            "w_out": _normal_bf16((latent_dim, D), std, seed, _IO_STREAM, T_IO_OUT)}
+
+
+def edge_inputs(seed, n_text, n_image, n_ref, text_dim=TEXT_DIM, latent_dim=LATENT_DIM):
+    """Inputs of one transformer call: text-encoder vectors as bf16 bits
+    [n_text][text_dim] ~ N(0, 1); noisy-image and reference latent tokens
+    [n][latent_dim] ~ N(0, 1) in fp32, rounded to bf16-representable values
+    (the call rounds them to bf16 on the device, exactly, then)."""
+    text = _normal_bf16((n_text, text_dim), 1.0, seed, _EDGE_STREAM, T_IN_TEXT)
+    img = bf16_bits_to_f32(_normal_bf16((n_image, latent_dim), 1.0, seed, _EDGE_STREAM, T_IN_IMAGE))
+    refs = bf16_bits_to_f32(_normal_bf16((n_ref, latent_dim), 1.0, seed, _EDGE_STREAM, T_IN_REFS))
+    return text, img, refs

@@ -266,3 +266,56 @@ def test_weights_pack_sizes_and_validation():
     bad.layout = 7
     assert _call_block(w=bad) == E_INVALID
     assert b"layout" in lib.flux3_last_error_detail()
+
+
+def test_transformer_workspace_and_validation():
+    lib = F.load()
+    d = _dims()
+    io_dims = L.IoDims(20480, 128)
+    n = 336
+    need = F.transformer_workspace_bytes(synth.DIMS, io_dims, n)
+    assert need >= F.workspace_bytes(synth.DIMS, n) + n * 3072 * 4
+    for bad in (L.IoDims(20480, 100), L.IoDims(20480, 512), L.IoDims(100, 128)):
+        assert F.transformer_workspace_bytes(synth.DIMS, bad, n) == 0
+    io = L.IoWeights(*[FAKE + 4096 * i for i in range(5)])
+    mw = (L.ModulationWeights * 2)()
+    for k in range(2):
+        mw[k].w1, mw[k].w2 = FAKE, FAKE + 256
+        for m in range(3):
+            mw[k].w_mod[m] = FAKE + 512 * (m + 1)
+    pm = (L.BlockWeights * 3)(_w(), _w(), _w())
+    jt = (L.BlockWeights * 1)(_w())
+    segs3 = ((0, 80, 0), (80, 128, 1), (208, 128, 2))
+
+    def call(dims=d, iod=io_dims, iow=io, m=mw, text=FAKE, image=FAKE, refs=FAKE,
+             segs=segs3, t=0.5, tt=-1.0, rope=FAKE, vel=FAKE, ws=FAKE, ws_bytes=None):
+        seg_arr, n_segs = L.make_segments(list(segs))
+        nn = sum(c for _s, c, _m in segs)
+        if ws_bytes is None:
+            ws_bytes = F.transformer_workspace_bytes(synth.DIMS, io_dims, nn)
+        return lib.flux3_transformer_forward(
+            ctypes.byref(dims), None if iod is None else ctypes.byref(iod),
+            None if iow is None else ctypes.byref(iow), m, pm, 1, jt, 1, text, image, refs,
+            seg_arr, n_segs, t, tt, rope, vel, ws, ws_bytes, 0)
+
+    assert call(iod=None) == E_INVALID
+    assert call(iod=L.IoDims(20480, 96)) == E_UNSUPPORTED
+    assert call(iow=None) == E_INVALID
+    assert call(m=None) == E_INVALID
+    assert call(segs=((0, 80, 0), (80, 128, 2))) == E_SHAPE                 # no image
+    assert call(segs=((0, 80, 0), (80, 64, 1), (144, 64, 1))) == E_SHAPE    # two images
+    assert call(image=None) == E_INVALID
+    assert call(text=None) == E_INVALID                                      # text segment present
+    assert call(refs=FAKE + 8) == E_ALIGN
+    assert call(vel=None) == E_INVALID
+    assert call(t=float("nan")) == E_INVALID
+    assert call(tt=float("nan")) == E_INVALID
+    assert call(tt=0.25) == E_INVALID                                        # no target embedder
+    assert call(ws=None) == E_WORKSPACE
+    assert call(ws_bytes=1 << 20) == E_WORKSPACE
+    w_final_null = L.IoWeights(FAKE, FAKE, FAKE, None, FAKE)
+    assert call(iow=w_final_null) == E_INVALID
+    assert b"w_final" in lib.flux3_last_error_detail()
+    # text and references are optional when no segment holds them
+    no_ref = L.IoWeights(FAKE, FAKE, None, FAKE, FAKE)
+    assert call(iow=no_ref, refs=None, segs=((0, 80, 0), (80, 128, 1)), ws=None) == E_WORKSPACE
