@@ -39,8 +39,9 @@ Parity status per function (pins live in tests/test_oracle_pins.py):
   token_positions, rope_tables, apply_rope, layer_norm, modulate,
   rms_norm_heads, attention, silu, swiglu_mlp, block_forward,
   block_forward_rows, stack_forward, timestep_embedding,
-  modulation_from_t, shifted_sigmas, euler_step, input_projection,
-  final_modulation, output_layer, transformer_forward: all pinned.
+  modulation_from_t, shifted_sigmas, euler_step, x0_preview, sample,
+  input_projection, final_modulation, output_layer, transformer_forward:
+  all pinned.
 """
 import numpy as np
 
@@ -431,3 +432,27 @@ def shifted_sigmas(steps, shift=6.93):
 def euler_step(sample, v, sigma, sigma_next):
     """Flow-matching Euler update: sample + (sigma_next - sigma) * v."""
     return sample + (sigma_next - sigma) * v
+
+
+def x0_preview(sample, v, sigma):
+    """The model's current guess of the clean latent: sample - sigma * v
+    [P4 "The denoise loop"; the preview step of the Diffusers post]."""
+    return sample - sigma * v
+
+
+def sample(noise, text, refs, segs, io_w, emb_w, w_mod, per_mode, joint, rope, steps=16,
+           shift=6.93, distilled=True, dtype=np.float64):
+    """The denoise loop [P4 "The denoise loop", "What step distillation
+    removed"]: start from pure noise at sigma = 1, and at each step call the
+    transformer at the current sigma (the distilled flow map is also told the
+    sigma it jumps to) and move the latent by (sigma_next - sigma) v.
+    Returns the final latent and the x0 preview of every step."""
+    sig = shifted_sigmas(steps, shift)
+    x = np.array(noise, dtype=dtype, copy=True)
+    previews = []
+    for i in range(steps):
+        v = transformer_forward(text, x, refs, segs, io_w, emb_w, w_mod, per_mode, joint, rope,
+                                sig[i], t_target=sig[i + 1] if distilled else None, dtype=dtype)
+        previews.append(x0_preview(x, v, sig[i]))
+        x = euler_step(x, v, sig[i], sig[i + 1])
+    return x, previews

@@ -629,3 +629,27 @@ def test_transformer_stage_structure():
     assert not np.allclose(b, run(text + 1.0, refs, joint))
     assert not np.allclose(b, run(text, refs * 2.0, joint))
     assert a.shape == (4, 32)
+
+
+def test_sample_loop_structure():
+    """The loop calls the transformer at sigma_i (target sigma_{i+1} for the
+    flow map), moves by (sigma_{i+1} - sigma_i) v, and its last x0 preview is
+    the final latent (the last step lands on sigma = 0)."""
+    D, per_mode, joint, segs, tab, io, emb, w_mod, text, image, refs = _transformer_case(1, 1)
+    out, prev = O.sample(image, text, refs, segs, io, emb, w_mod, per_mode, joint, tab, steps=4)
+    assert len(prev) == 4 and out.shape == image.shape
+    np.testing.assert_allclose(prev[-1], out, rtol=1e-13, atol=1e-13)
+    # step by step against explicit calls at the printed-schedule sigmas
+    sig = O.shifted_sigmas(4)
+    assert round(sig[3], 3) == 0.698           # "ends at 0.698 before the final jump"
+    x = image.copy()
+    for i in range(4):
+        v = O.transformer_forward(text, x, refs, segs, io, emb, w_mod, per_mode, joint, tab,
+                                  sig[i], t_target=sig[i + 1])
+        np.testing.assert_array_equal(prev[i], x - sig[i] * v)
+        x = x + (sig[i + 1] - sig[i]) * v
+    np.testing.assert_array_equal(out, x)
+    # the base model ignores the target embedder
+    base, _ = O.sample(image, text, refs, segs, io, {k: emb[k] for k in ("w1", "w2")}, w_mod,
+                       per_mode, joint, tab, steps=2, distilled=False)
+    assert base.shape == image.shape and np.all(np.isfinite(base))
