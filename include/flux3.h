@@ -352,6 +352,51 @@ flux3_status flux3_transformer_forward(const flux3_dims *dims, const flux3_io_di
                                        float t_target, const float *rope, float *velocity,
                                        void *workspace, size_t workspace_bytes, void *stream);
 
+/* ---------------------------------------------------------------------------
+ * The denoise loop ("The denoise loop" and "What step distillation removed",
+ * rohitghumare.com guide): steps noise levels evenly spaced from 1 down to
+ * 1/steps, each shifted as sigma' = shift sigma / (1 + (shift - 1) sigma)
+ * (shift 6.93 in the pipeline), then a final 0.  Each step calls the
+ * transformer at sigma_i (the distilled flow map is also told sigma_{i+1})
+ * and moves the latent by (sigma_{i+1} - sigma_i) v; latent - sigma_i v is
+ * the step's preview of the clean latent.
+ * ------------------------------------------------------------------------- */
+
+/* The schedule into host sigmas[steps + 1] (computed in double, stored as
+ * float).  Errors: FLUX3_E_SHAPE (steps < 1), FLUX3_E_INVALID (null or a
+ * shift that is not positive and finite). */
+flux3_status flux3_sigmas(int32_t steps, double shift, float *sigmas);
+
+/* One step on n fp32 values (n % 4 == 0, device pointers 16-byte aligned):
+ * x0_preview (optional, may be NULL) = latent - sigma v, then latent +=
+ * (sigma_next - sigma) v.  Asynchronous on stream. */
+flux3_status flux3_euler_step(const float *v, float *latent, float *x0_preview, int64_t n,
+                              float sigma, float sigma_next, void *stream);
+
+/* Workspace bytes flux3_sample needs: flux3_transformer_workspace_bytes
+ * plus one velocity buffer; 0 if dims are unsupported. */
+size_t flux3_sample_workspace_bytes(const flux3_dims *dims, const flux3_io_dims *io_dims,
+                                    int64_t n_tokens);
+
+/* The whole loop: steps transformer calls and Euler steps, all enqueued on
+ * stream (no host synchronisation).
+ *   latent   : device fp32 [n_image][latent_dim]: the starting noise in, the
+ *              final latent out.
+ *   distilled: non-zero to pass sigma_{i+1} as the target timestep (needs
+ *              the target embedders in mod_w).
+ *   previews : device fp32 [steps][n_image][latent_dim] out, or NULL.
+ *   Other arguments as for flux3_transformer_forward (image is latent).
+ * Errors as for flux3_transformer_forward and flux3_sigmas; on error
+ * nothing is enqueued. */
+flux3_status flux3_sample(const flux3_dims *dims, const flux3_io_dims *io_dims,
+                          const flux3_io_weights *io, const flux3_modulation_weights *mod_w,
+                          const flux3_block_weights *per_mode, int32_t n_pm,
+                          const flux3_block_weights *joint, int32_t n_joint, const void *text,
+                          float *latent, const float *refs, const flux3_segment *segs,
+                          int32_t n_segs, int32_t steps, double shift, int32_t distilled,
+                          const float *rope, float *previews, void *workspace,
+                          size_t workspace_bytes, void *stream);
+
 /* Kernel timing, for benchmarks and profiling.  While enabled, every kernel
  * launch is bracketed by a pair of HIP events recorded on the launch stream,
  * so the durations are those of the kernels themselves on the stream they
@@ -369,7 +414,8 @@ enum {
   FLUX3_K_GEMM_OUT = 4,
   FLUX3_K_MODULATION = 5,   /* one record per flux3_modulation_forward call */
   FLUX3_K_IO_LINEARS = 6,   /* each input / output linear of a transformer call */
-  FLUX3_K_COUNT = 7
+  FLUX3_K_EULER = 7,        /* each flux3_euler_step (and sampler step update) */
+  FLUX3_K_COUNT = 8
 };
 typedef struct {
   int64_t launches;

@@ -11,7 +11,7 @@ from ._lib import (Flux3Error, Dims, Segment, BlockWeights, RopeLayout, Workspac
                    device_query, modulation_workspace_bytes, modulation_forward,
                    ModulationWeights, weights_packed_bytes, weights_pack, WEIGHTS_LINEAR,
                    WEIGHTS_PACKED, IoDims, IoWeights, transformer_workspace_bytes,
-                   transformer_forward)
+                   transformer_forward, sigmas, euler_step, sample_workspace_bytes, sample)
 
 __all__ = ["Flux3Error", "Dims", "Segment", "BlockWeights", "RopeLayout", "WorkspaceLayout",
            "load", "layout_tokens", "rope_tables_build", "workspace_bytes", "workspace_layout",
@@ -20,4 +20,4 @@ __all__ = ["Flux3Error", "Dims", "Segment", "BlockWeights", "RopeLayout", "Works
            "device_query", "modulation_workspace_bytes", "modulation_forward",
            "ModulationWeights", "weights_packed_bytes", "weights_pack", "WEIGHTS_LINEAR",
            "WEIGHTS_PACKED", "IoDims", "IoWeights", "transformer_workspace_bytes",
-           "transformer_forward"]
+           "transformer_forward", "sigmas", "euler_step", "sample_workspace_bytes", "sample"]

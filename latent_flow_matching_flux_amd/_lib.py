@@ -23,12 +23,13 @@ EXPORTS = ("flux3_layout_tokens", "flux3_rope_tables_build", "flux3_workspace_by
            "flux3_workspace_layout_get", "flux3_block_forward", "flux3_stack_forward",
            "flux3_weights_packed_bytes", "flux3_weights_pack",
            "flux3_transformer_workspace_bytes", "flux3_transformer_forward",
+           "flux3_sigmas", "flux3_euler_step", "flux3_sample_workspace_bytes", "flux3_sample",
            "flux3_modulation_workspace_bytes", "flux3_modulation_forward",
            "flux3_profile_enable", "flux3_profile_reset", "flux3_profile_read",
            "flux3_device_query", "flux3_set_debug_sync", "flux3_status_string",
            "flux3_last_error_detail")
 KERNELS = ("rope_tables", "ln_modulate", "gemm_proj", "attention", "gemm_out", "modulation",
-           "io_linears")
+           "io_linears", "euler")
 
 
 class Flux3Error(RuntimeError):
@@ -131,6 +132,16 @@ def load(path=LIB_PATH):
                                               P(BlockWeights), i32, vp, vp, vp, P(Segment), i32,
                                               ctypes.c_float, ctypes.c_float, vp, vp, vp, sz, vp]
     lib.flux3_transformer_forward.restype = i32
+    lib.flux3_sigmas.argtypes = [i32, ctypes.c_double, P(ctypes.c_float)]
+    lib.flux3_sigmas.restype = i32
+    lib.flux3_euler_step.argtypes = [vp, vp, vp, i64, ctypes.c_float, ctypes.c_float, vp]
+    lib.flux3_euler_step.restype = i32
+    lib.flux3_sample_workspace_bytes.argtypes = [P(Dims), P(IoDims), i64]
+    lib.flux3_sample_workspace_bytes.restype = sz
+    lib.flux3_sample.argtypes = [P(Dims), P(IoDims), P(IoWeights), P(ModulationWeights),
+                                 P(BlockWeights), i32, P(BlockWeights), i32, vp, vp, vp,
+                                 P(Segment), i32, i32, ctypes.c_double, i32, vp, vp, vp, sz, vp]
+    lib.flux3_sample.restype = i32
     lib.flux3_modulation_workspace_bytes.argtypes = [P(Dims)]
     lib.flux3_modulation_workspace_bytes.restype = sz
     lib.flux3_modulation_forward.argtypes = [P(Dims), P(ModulationWeights), P(ctypes.c_float),
@@ -380,6 +391,42 @@ def transformer_forward(dims, io_dims, io_w, mod_w, per_mode, joint, text, image
         ctypes.byref(make_dims(dims)), ctypes.byref(make_io_dims(io_dims)), ctypes.byref(io), mw,
         pm_arr, n_pm, jt_arr, n_joint, _ptr(text), _ptr(image), _ptr(refs), seg_arr, n_segs,
         float(t), -1.0 if t_target is None else float(t_target), _ptr(rope), _ptr(velocity),
+        _ptr(workspace), workspace_nbytes, _stream_handle(stream)))
+
+
+def sigmas(steps, shift=6.93):
+    """flux3_sigmas: the shifted schedule, a list of steps + 1 floats."""
+    out = (ctypes.c_float * (steps + 1))()
+    _check(load().flux3_sigmas(int(steps), float(shift), out))
+    return list(out)
+
+
+def euler_step(v, latent, sigma, sigma_next, x0_preview=None, stream=None):
+    """flux3_euler_step on fp32 device tensors (in place on latent)."""
+    _check(load().flux3_euler_step(_ptr(v), _ptr(latent), _ptr(x0_preview), latent.numel(),
+                                   float(sigma), float(sigma_next), _stream_handle(stream)))
+
+
+def sample_workspace_bytes(dims, io_dims, n_tokens):
+    return load().flux3_sample_workspace_bytes(ctypes.byref(make_dims(dims)),
+                                               ctypes.byref(make_io_dims(io_dims)), n_tokens)
+
+
+def sample(dims, io_dims, io_w, mod_w, per_mode, joint, text, latent, refs, segs, steps, rope,
+           workspace, shift=6.93, distilled=True, previews=None, workspace_nbytes=None,
+           stream=None):
+    """flux3_sample: the whole denoise loop, in place on latent."""
+    io = IoWeights(*[_ptr(io_w.get(k)) for k in ("w_text", "w_img_in", "w_ref_in", "w_final",
+                                                  "w_out")])
+    mw = (ModulationWeights * 2)(_modulation_weights(mod_w[0]), _modulation_weights(mod_w[1]))
+    pm_arr, n_pm, jt_arr, n_joint = _block_arrays(per_mode, joint)
+    seg_arr, n_segs = make_segments(segs)
+    if workspace_nbytes is None:
+        workspace_nbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(load().flux3_sample(
+        ctypes.byref(make_dims(dims)), ctypes.byref(make_io_dims(io_dims)), ctypes.byref(io), mw,
+        pm_arr, n_pm, jt_arr, n_joint, _ptr(text), _ptr(latent), _ptr(refs), seg_arr, n_segs,
+        int(steps), float(shift), 1 if distilled else 0, _ptr(rope), _ptr(previews),
         _ptr(workspace), workspace_nbytes, _stream_handle(stream)))
 
 

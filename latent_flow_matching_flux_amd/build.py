@@ -18,7 +18,8 @@ COMMON = [
     "-Wall", "-Wno-unused-function", "-Wno-unknown-pragmas",
 ]
 
-SOURCES = ["rope.hip", "ln_modulate.hip", "gemm.hip", "attention.hip", "modulation.hip", "abi.cpp"]
+SOURCES = ["rope.hip", "ln_modulate.hip", "gemm.hip", "attention.hip", "modulation.hip",
+           "sampler.hip", "abi.cpp"]
 
 
 def _compile(src, defines=(), build_dir=BUILD):

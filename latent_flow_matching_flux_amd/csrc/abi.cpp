@@ -768,6 +768,87 @@ flux3_status flux3_transformer_forward(const flux3_dims* dims, const flux3_io_di
   return ok();
 }
 
+flux3_status flux3_sigmas(int32_t steps, double shift, float* sigmas) {
+  if (steps < 1) return fail(FLUX3_E_SHAPE, "steps %d < 1", steps);
+  if (!sigmas) return fail(FLUX3_E_INVALID, "sigmas is NULL");
+  if (!(shift > 0.0) || !std::isfinite(shift)) return fail(FLUX3_E_INVALID, "shift must be positive");
+  for (int i = 0; i < steps; ++i) {
+    // evenly spaced from 1 down to 1/steps
+    const double sg = steps == 1 ? 1.0 : 1.0 + i * ((1.0 / steps - 1.0) / (steps - 1));
+    sigmas[i] = (float)(shift * sg / (1.0 + (shift - 1.0) * sg));
+  }
+  sigmas[steps] = 0.f;
+  return ok();
+}
+
+flux3_status flux3_euler_step(const float* v, float* latent, float* x0_preview, int64_t n,
+                              float sigma, float sigma_next, void* stream) {
+  if (!v || !latent) return fail(FLUX3_E_INVALID, "v or latent is NULL");
+  if (!aligned16(v) || !aligned16(latent) || (x0_preview && !aligned16(x0_preview)))
+    return fail(FLUX3_E_ALIGN, "v, latent or x0_preview is not 16-byte aligned");
+  if (n < 0 || n % 4 != 0) return fail(FLUX3_E_SHAPE, "n %lld must be a non-negative multiple of 4", (long long)n);
+  if (!std::isfinite(sigma) || !std::isfinite(sigma_next))
+    return fail(FLUX3_E_INVALID, "sigma or sigma_next is not finite");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int pi = prof_begin(FLUX3_K_EULER, (double)n, s);
+  hipError_t e = flux3::launch_euler(v, latent, x0_preview, n, sigma, sigma_next, s);
+  prof_end(pi, s);
+  flux3_status r = after_launch(e, "euler", s);
+  return r != FLUX3_OK ? r : ok();
+}
+
+size_t flux3_sample_workspace_bytes(const flux3_dims* dims, const flux3_io_dims* io_dims,
+                                    int64_t n_tokens) {
+  const size_t t = flux3_transformer_workspace_bytes(dims, io_dims, n_tokens);
+  if (t == 0) return 0;
+  return t + align_up((size_t)n_tokens * io_dims->latent_dim * 4, kBufAlign);
+}
+
+flux3_status flux3_sample(const flux3_dims* dims, const flux3_io_dims* io_dims,
+                          const flux3_io_weights* io, const flux3_modulation_weights* mod_w,
+                          const flux3_block_weights* per_mode, int32_t n_pm,
+                          const flux3_block_weights* joint, int32_t n_joint, const void* text,
+                          float* latent, const float* refs, const flux3_segment* segs,
+                          int32_t n_segs, int32_t steps, double shift, int32_t distilled,
+                          const float* rope, float* previews, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  if (steps < 1 || steps > 1000) return fail(FLUX3_E_SHAPE, "steps %d outside [1, 1000]", steps);
+  std::vector<float> sig(steps + 1);
+  flux3_status r = flux3_sigmas(steps, shift, sig.data());
+  if (r != FLUX3_OK) return r;
+  if (!dims || !io_dims) return fail(FLUX3_E_INVALID, "dims or io_dims is NULL");
+  if (!segs || n_segs < 1 || n_segs > FLUX3_MAX_SEGMENTS)
+    return fail(FLUX3_E_SHAPE, "n_segs %d outside [1, %d] or segs NULL", n_segs, FLUX3_MAX_SEGMENTS);
+  const int64_t n = (int64_t)segs[n_segs - 1].start + segs[n_segs - 1].count;
+  int64_t n_img = 0;
+  for (int i = 0; i < n_segs; ++i)
+    if (segs[i].mode == FLUX3_MODE_IMAGE) n_img += segs[i].count;
+  if (previews && !aligned16(previews)) return fail(FLUX3_E_ALIGN, "previews is not 16-byte aligned");
+  const size_t need = flux3_sample_workspace_bytes(dims, io_dims, n);
+  if (need == 0) return fail(FLUX3_E_UNSUPPORTED, "dims or io_dims unsupported");
+  if (!workspace) return fail(FLUX3_E_WORKSPACE, "workspace is NULL");
+  if (workspace_bytes < need)
+    return fail(FLUX3_E_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, need);
+  const size_t tbytes = flux3_transformer_workspace_bytes(dims, io_dims, n);
+  float* vel = reinterpret_cast<float*>(static_cast<char*>(workspace) + tbytes);
+  const int64_t nv = n_img * io_dims->latent_dim;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  for (int i = 0; i < steps; ++i) {
+    // the first call validates every argument before anything is enqueued
+    r = flux3_transformer_forward(dims, io_dims, io, mod_w, per_mode, n_pm, joint, n_joint, text,
+                                  latent, refs, segs, n_segs, sig[i],
+                                  distilled ? sig[i + 1] : -1.f, rope, vel, workspace, tbytes,
+                                  stream);
+    if (r != FLUX3_OK) return r;
+    const int pi = prof_begin(FLUX3_K_EULER, (double)nv, s);
+    hipError_t e = flux3::launch_euler(vel, latent, previews ? previews + (size_t)i * nv : nullptr,
+                                       nv, sig[i], sig[i + 1], s);
+    prof_end(pi, s);
+    if ((r = after_launch(e, "euler", s)) != FLUX3_OK) return r;
+  }
+  return ok();
+}
+
 flux3_status flux3_device_query(int32_t device, flux3_device_info* out) {
   if (!out) return fail(FLUX3_E_INVALID, "out is NULL");
   memset(out, 0, sizeof *out);

@@ -90,6 +90,11 @@ hipError_t launch_modulation(const ModulationShape& ms, const ModulationWeightsD
                              const SegTableHost& segs, const int32_t* seg_mode, float* mod,
                              float* ws, hipStream_t s, float* final_mod = nullptr);
 
+// latent += (sigma_next - sigma) v over n fp32 values (n % 4 == 0), with the
+// preview x0 = latent - sigma v first when x0 is not null.
+hipError_t launch_euler(const float* v, float* latent, float* x0, int64_t n, float sigma,
+                        float sigma_next, hipStream_t s);
+
 hipError_t launch_rope_tables(const RopeLayoutDev& lay, float* rope, int64_t n,
                               hipStream_t s);
 hipError_t launch_ln_modulate(const BlockShape& bs, const float* x,

@@ -319,3 +319,43 @@ def test_transformer_workspace_and_validation():
     # text and references are optional when no segment holds them
     no_ref = L.IoWeights(FAKE, FAKE, None, FAKE, FAKE)
     assert call(iow=no_ref, refs=None, segs=((0, 80, 0), (80, 128, 1)), ws=None) == E_WORKSPACE
+
+
+def test_sigmas_schedule_and_validation():
+    from oracle import flux3_oracle as O
+    for steps in (1, 4, 16, 50):
+        got = np.array(F.sigmas(steps), np.float32)
+        want = O.shifted_sigmas(steps).astype(np.float32)
+        assert got.shape == want.shape and got[-1] == 0.0
+        np.testing.assert_array_max_ulp(got, want, maxulp=1)
+    s16 = F.sigmas(16)
+    assert [round(v, 3) for v in s16[:3]] == [1.0, 0.99, 0.98]
+    assert [round(v, 3) for v in s16[13:16]] == [0.615, 0.497, 0.316]
+    lib = F.load()
+    buf = (ctypes.c_float * 4)()
+    assert lib.flux3_sigmas(0, 6.93, buf) == E_SHAPE
+    assert lib.flux3_sigmas(3, 0.0, buf) == E_INVALID
+    assert lib.flux3_sigmas(3, float("nan"), buf) == E_INVALID
+    assert lib.flux3_sigmas(3, 6.93, None) == E_INVALID
+
+
+def test_euler_and_sample_validation():
+    lib = F.load()
+    assert lib.flux3_euler_step(None, FAKE, None, 128, 1.0, 0.9, 0) == E_INVALID
+    assert lib.flux3_euler_step(FAKE, FAKE, None, 126, 1.0, 0.9, 0) == E_SHAPE
+    assert lib.flux3_euler_step(FAKE, FAKE + 4, None, 128, 1.0, 0.9, 0) == E_ALIGN
+    assert lib.flux3_euler_step(FAKE, FAKE, None, 128, float("inf"), 0.9, 0) == E_INVALID
+    io_dims = L.IoDims(20480, 128)
+    need = F.sample_workspace_bytes(synth.DIMS, io_dims, 336)
+    assert need >= F.transformer_workspace_bytes(synth.DIMS, io_dims, 336) + 336 * 128 * 4
+    seg_arr, n_segs = L.make_segments([(0, 80, 0), (80, 256, 1)])
+    io = L.IoWeights(*[FAKE + 4096 * i for i in range(5)])
+    mw = (L.ModulationWeights * 2)()
+    args = lambda steps, ws, nbytes: (ctypes.byref(_dims()), ctypes.byref(io_dims),
+                                      ctypes.byref(io), mw, None, 0, None, 0, FAKE, FAKE, None,
+                                      seg_arr, n_segs, steps, 6.93, 1, FAKE, None, ws, nbytes, 0)
+    assert lib.flux3_sample(*args(0, FAKE, need)) == E_SHAPE
+    assert lib.flux3_sample(*args(16, FAKE, need - 1)) == E_WORKSPACE
+    assert lib.flux3_sample(*args(16, None, need)) == E_WORKSPACE
+    # reaches the transformer call's own checks (no modulation weights)
+    assert lib.flux3_sample(*args(16, FAKE, need)) == E_INVALID

@@ -93,6 +93,14 @@ CASES = [
      0.3),
     ("model_t2i4336_io_only", synth.DIMS, synth.workload("t2i4336").layout, synth.TEXT_DIM, 0, 0,
      0.8, None),
+    # the 1360 x 768 edit layout (48 x 85 grid and a same-size reference) and
+    # ten references, the layouts of "Inside the transformer" / the ten-image
+    # reference limit
+    ("small_1360x768_edit", SMALL, synth.RopeLayout(240, 48, 85, ((48, 85),)), 256, 1, 1, 0.5,
+     0.35),
+    ("small_ten_refs", SMALL, synth.RopeLayout(80, 16, 16, tuple((8 + k, 12 - k % 3)
+                                                                  for k in range(10))), 256, 1, 1,
+     0.65, None),
 ]
 
 
