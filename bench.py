@@ -25,7 +25,10 @@ apart from the step loop: 5 warm-up and 20 timed calls, each bracketed by
 HIP events on the launch stream, rotating 4 weight copies (980 MB) so that
 no call finds its weights in the 256 MB Infinity Cache; median and minimum,
 block tokens/s = N / t_block, and GEMM / attention TFLOP/s from the
-library's per-kernel events over those calls.  Peak: the 2516.6 TFLOP/s of
+library's per-kernel events over those calls.  "whole_call" times one
+flux3_transformer_forward (input linears from 20,480-value text vectors and
+128-value latent tokens, both stages' modulation, the 5+28 blocks, the
+output layer) and one 16-step distilled flux3_sample over the same blocks.  Peak: the 2516.6 TFLOP/s of
 AMD's MI355X spec, next to CUs x clock x 4096 from the device query.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
@@ -128,6 +131,78 @@ def time_joint_block(F, dims, lay, segs, n, rand, rand_block, reps=20, warmup=5,
             "kernel_ms": {k: v["total_ms"] / reps for k, v in stats.items()}}
 
 
+def time_whole_calls(F, dims, lay, segs, n, rand, per_mode, joint, emb_w, mod_w, steps=16,
+                     reps=3):
+    """One whole transformer call (input linears, both stages' modulation,
+    the stack, the output layer) and one full denoise loop of `steps`
+    distilled steps, on the same workload and blocks: event-timed, mean of
+    `reps` calls after one warm-up, and one loop after a warm-up loop."""
+    import torch
+    import synth
+    dev = torch.device("cuda:0")
+    D = dims.width
+    TD, LD = synth.TEXT_DIM, synth.LATENT_DIM
+    n_text = sum(s.count for s in segs if s.mode == 0)
+    n_img = sum(s.count for s in segs if s.mode == 1)
+    n_ref = sum(s.count for s in segs if s.mode == 2)
+    io = {"w_text": rand(D, TD, std=0.02), "w_img_in": rand(D, LD, std=0.02),
+          "w_ref_in": rand(D, LD, std=0.02), "w_final": rand(2 * D, D, std=0.02),
+          "w_out": rand(LD, D, std=0.02)}
+    tgt = {"w1_tgt": rand(D, 256, std=0.02), "w2_tgt": rand(D, D, std=0.02)}
+    mw = [dict(m, **tgt) for m in mod_w]
+    text = rand(n_text, TD) if n_text else None
+    image = rand(n_img, LD, dtype=torch.float32)
+    refs = rand(n_ref, LD, dtype=torch.float32) if n_ref else None
+    rope = torch.empty((n, 64, 2), dtype=torch.float32, device=dev)
+    F.rope_tables_build(lay, rope)
+    io_dims = F.IoDims(TD, LD)
+    vel = torch.empty((n_img, LD), dtype=torch.float32, device=dev)
+    ws = torch.empty(F.sample_workspace_bytes(dims, io_dims, n), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def call():
+        F.transformer_forward(dims, io_dims, io, mw, per_mode, joint, text, image, refs, segs,
+                              0.75, rope, vel, ws, t_target=0.7, stream=stream)
+
+    call()
+    torch.cuda.synchronize()
+    F.profile_reset()
+    F.profile_enable(True)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        call()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    F.profile_enable(False)
+    io_stats = F.profile_read("io_linears")
+    F.profile_reset()
+    call_ms = e0.elapsed_time(e1) / reps
+    assert torch.isfinite(vel).all(), "non-finite velocity"
+    lat = torch.empty_like(image)
+
+    def loop():
+        lat.copy_(image)
+        F.sample(dims, io_dims, io, mw, per_mode, joint, text, lat, refs, segs, steps, rope, ws,
+                 stream=stream)
+
+    loop()
+    torch.cuda.synchronize()
+    e0.record(stream)
+    loop()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    loop_ms = e0.elapsed_time(e1)
+    assert torch.isfinite(lat).all(), "non-finite latent"
+    return {"transformer_call_ms": call_ms, "transformer_call_tokens_per_s": n / (call_ms * 1e-3),
+            "io_linears_ms_per_call": io_stats["total_ms"] / reps,
+            "sample_steps": steps, "sample_ms": loop_ms,
+            "images_per_s": 1e3 / loop_ms, "reps": reps,
+            "what": "transformer call = text/image/reference input linears + both stages' "
+                    "modulation from (t, t_target) + 5+28 blocks + output layer; sample = "
+                    f"{steps} distilled steps (call + Euler step each), shift 6.93"}
+
+
 def cpu_baseline(workload_name):
     """The oracle, as it stands (NumPy float64), on one joint block of the
     same workload; value in block tokens/s."""
@@ -162,7 +237,8 @@ def main():
     ap.add_argument("--linear-weights", action="store_true",
                     help="keep the weights in Linear layout instead of packing them at load")
     ap.add_argument("--no-block", action="store_true",
-                    help="skip the single-block timing (profiling runs of the step alone)")
+                    help="skip the single-block, whole-call and denoise-loop timings "
+                         "(profiling runs of the step alone)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path; run with --gpus 1",
@@ -287,12 +363,14 @@ def main():
                 "traffic": measured_traffic(n),
                 "work_per_launch": f"{proj_fpt / 1e6:.2f} MFLOP/token x {gp['tokens'] / max(gp['launches'], 1):.0f} tokens (mean over stage-1 and stage-2 launches)"}
 
-    # single joint block over all tokens (the same segments and layout)
-    block = None
+    # single joint block over all tokens (the same segments and layout), and
+    # the whole transformer call and denoise loop around the same blocks
+    block = whole = None
     if not args.no_block:
         block = time_joint_block(F, dims, lay, segs, n, rand, rand_block)
         block["gemm_frac_peak"] = block["gemm_tflops"] / PEAK_BF16_TFLOPS
         block["attention_frac_peak"] = block["attention_tflops"] / PEAK_BF16_TFLOPS
+        whole = time_whole_calls(F, dims, lay, segs, n, rand, per_mode, joint, emb_w, mod_w)
     devinfo = F.device_query(0)
     peak = {"spec_tflops": PEAK_BF16_TFLOPS, "derived_tflops": devinfo["bf16_dense_tflops"],
             "compute_units": devinfo["compute_units"], "clock_mhz": devinfo["clock_khz"] / 1e3,
@@ -328,6 +406,7 @@ def main():
         "stack_tokens_per_s": n / (ms_per_step / 1e3),
         "kernels": kern,
         "block": block,
+        "whole_call": whole,
         "peak": peak,
         "roofline": roofline,
         "cpu_baseline": cpu,
