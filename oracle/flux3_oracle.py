@@ -389,7 +389,7 @@ def output_layer(x_img, shift, scale, w_out, dtype=np.float64, eps=EPS_LN):
 
 
 def transformer_forward(text, image, refs, segs, io_w, emb_w, w_mod, per_mode, joint, rope,
-                        t, t_target=None, dtype=np.float64):
+                        t, t_target=None, dtype=np.float64, keep=False):
     """One transformer call: input projections, the two stages' modulation
     from the timesteps (image tokens t, text and references 0), the two-stage
     stack, then the output layer on the image rows.
@@ -397,7 +397,8 @@ def transformer_forward(text, image, refs, segs, io_w, emb_w, w_mod, per_mode, j
     io_w: {w_text, w_img_in, w_ref_in, w_final, w_out}; emb_w: {w1, w2} and,
     for the distilled model, {w1_tgt, w2_tgt}; w_mod[stage][mode] the
     per-(stage, mode) modulation linears.  segs: (start, count, mode) in the
-    order text, image, references.  Returns the velocity of the image tokens.
+    order text, image, references.  Returns the velocity of the image tokens
+    (and, with keep, the residual stream after the stack).
     """
     x = input_projection(text, image, refs, io_w["w_text"], io_w["w_img_in"],
                          io_w["w_ref_in"], dtype)
@@ -414,7 +415,8 @@ def transformer_forward(text, image, refs, segs, io_w, emb_w, w_mod, per_mode, j
                                     **tgt)
     img = [(st, c) for st, c, m in segs if m == MODE_IMAGE]
     rows = np.concatenate([np.arange(st, st + c) for st, c in img])
-    return output_layer(x[rows], shift, scale, io_w["w_out"], dtype)
+    v = output_layer(x[rows], shift, scale, io_w["w_out"], dtype)
+    return (v, x) if keep else v
 
 
 # --------------------------------------------------------------------------

@@ -653,3 +653,29 @@ def test_sample_loop_structure():
     base, _ = O.sample(image, text, refs, segs, io, {k: emb[k] for k in ("w1", "w2")}, w_mod,
                        per_mode, joint, tab, steps=2, distilled=False)
     assert base.shape == image.shape and np.all(np.isfinite(base))
+
+
+def test_transformer_text_and_reference_modulation_ignore_t():
+    """Text and reference tokens are modulated at t = 0 whatever the image
+    timestep [P1]: after a stack of per-mode blocks only, their rows of the
+    residual stream are bit-identical for any t, while the image rows move."""
+    D, per_mode, _joint, segs, tab, io, emb, w_mod, text, image, refs = _transformer_case(2, 0)
+    run = lambda t: O.transformer_forward(text, image, refs, segs, io, emb, w_mod, per_mode, [],
+                                          tab, t, keep=True)[1]
+    a, b = run(0.2), run(0.9)
+    np.testing.assert_array_equal(a[:3], b[:3])     # text rows
+    np.testing.assert_array_equal(a[7:], b[7:])     # reference rows
+    assert not np.allclose(a[3:7], b[3:7])          # image rows
+
+
+def test_transformer_stage_modulation_goes_to_its_stage():
+    """Stage-1 blocks take the stage-1 modulation linears: without joint
+    blocks the stage-2 linears do not change the velocity."""
+    D, per_mode, _joint, segs, tab, io, emb, w_mod, text, image, refs = _transformer_case(1, 0)
+    a = O.transformer_forward(text, image, refs, segs, io, emb, w_mod, per_mode, [], tab, 0.4)
+    w_mod2 = [w_mod[0], {m: w * 3.0 for m, w in w_mod[1].items()}]
+    b = O.transformer_forward(text, image, refs, segs, io, emb, w_mod2, per_mode, [], tab, 0.4)
+    np.testing.assert_array_equal(a, b)
+    w_mod3 = [{m: w * 3.0 for m, w in w_mod[0].items()}, w_mod[1]]
+    c = O.transformer_forward(text, image, refs, segs, io, emb, w_mod3, per_mode, [], tab, 0.4)
+    assert not np.allclose(a, c)
