@@ -236,6 +236,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--linear-weights", action="store_true",
                     help="keep the weights in Linear layout instead of packing them at load")
+    ap.add_argument("--no-sample", action="store_true",
+                    help="skip the whole-call and denoise-loop timings")
     ap.add_argument("--no-block", action="store_true",
                     help="skip the single-block, whole-call and denoise-loop timings "
                          "(profiling runs of the step alone)")
@@ -370,7 +372,8 @@ def main():
         block = time_joint_block(F, dims, lay, segs, n, rand, rand_block)
         block["gemm_frac_peak"] = block["gemm_tflops"] / PEAK_BF16_TFLOPS
         block["attention_frac_peak"] = block["attention_tflops"] / PEAK_BF16_TFLOPS
-        whole = time_whole_calls(F, dims, lay, segs, n, rand, per_mode, joint, emb_w, mod_w)
+        if not args.no_sample:
+            whole = time_whole_calls(F, dims, lay, segs, n, rand, per_mode, joint, emb_w, mod_w)
     devinfo = F.device_query(0)
     peak = {"spec_tflops": PEAK_BF16_TFLOPS, "derived_tflops": devinfo["bf16_dense_tflops"],
             "compute_units": devinfo["compute_units"], "clock_mhz": devinfo["clock_khz"] / 1e3,
