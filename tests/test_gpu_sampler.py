@@ -61,7 +61,8 @@ def _setup(dims, layout, text_dim, n_pm, n_joint, target, seed=9):
     return segs, io, mw, per_mode, joint, text, noise, refs
 
 
-@pytest.mark.parametrize("steps,distilled", [(4, True), (3, False)], ids=["distilled4", "base3"])
+@pytest.mark.parametrize("steps,distilled", [(4, True), (3, False), (1, True)],
+                         ids=["distilled4", "base3", "one_step"])
 def test_sample_matches_oracle(steps, distilled):
     dims, text_dim = SMALL, 256
     layout = synth.RopeLayout(80, 8, 8, ((8, 8),))

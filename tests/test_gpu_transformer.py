@@ -101,6 +101,9 @@ CASES = [
     ("small_ten_refs", SMALL, synth.RopeLayout(80, 16, 16, tuple((8 + k, 12 - k % 3)
                                                                   for k in range(10))), 256, 1, 1,
      0.65, None),
+    # references without text; a ragged grid; t at both ends of the schedule
+    ("small_refs_no_text_t1", SMALL, synth.RopeLayout(0, 7, 9, ((5, 3),)), 256, 1, 1, 1.0, 0.99),
+    ("small_ragged_t0", SMALL, synth.RopeLayout(13, 5, 11, ()), 256, 1, 1, 0.0, None),
 ]
 
 
