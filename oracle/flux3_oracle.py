@@ -9,13 +9,14 @@ their host code.
 Sources (the release pages; cited by page title and section):
 
 * [P1]  "FLUX.3 Image Klein Is Now Available in Diffusers" (15jq.com),
-        section "Speed, architecture, and how the tokens move".
+        sections "Speed, architecture, and how the tokens move" and
+        "Smaller GPUs, single files, and custom LoRA training" (rowwise FP8).
 * [P3]  The Chinese translation of the Diffusers release post (everytik.com):
         the `block(x, shift, scale, gate)` listing and the RoPE position
         table under the model walk-through.
 * [P4]  "How to Run FLUX 3 Image Klein Locally" (rohitghumare.com), sections
         "Inside the transformer", "The latent space and the VAE",
-        "What step distillation removed".
+        "What step distillation removed", "What Black Forest Labs released".
 * [P5]  The ifeeling.app summary, architecture paragraphs (reference offset
         runs negatively along l).
 
@@ -40,8 +41,10 @@ Parity status per function (pins live in tests/test_oracle_pins.py):
   rms_norm_heads, attention, silu, swiglu_mlp, block_forward,
   block_forward_rows, stack_forward, timestep_embedding,
   modulation_from_t, shifted_sigmas, euler_step, x0_preview, sample,
-  input_projection, final_modulation, output_layer, transformer_forward:
-  all pinned.
+  input_projection, final_modulation, output_layer, transformer_forward,
+  e4m3_values, e4m3_encode, quantize_rowwise, dequantize_rowwise,
+  fake_quantize_rows, fused_block_matrices, quantize_block_weights,
+  block_forward_quantized, block_forward_fp8: all pinned.
 """
 import numpy as np
 
@@ -458,3 +461,154 @@ def sample(noise, text, refs, segs, io_w, emb_w, w_mod, per_mode, joint, rope, s
         previews.append(x0_preview(x, v, sig[i]))
         x = euler_step(x, v, sig[i], sig[i + 1])
     return x, previews
+
+
+# --------------------------------------------------------------------------
+# rowwise FP8 ("fp8r") block linears
+#   [P1 "Smaller GPUs, single files, and custom LoRA training": the
+#   transformer also ships as a rowwise-FP8 single file]; [P4 "What Black
+#   Forest Labs released": FP8 files and the GPUs that have FP8 kernels];
+#   [P5 architecture notes: fp8r is row-level FP8].
+# Readings: the 8-bit format is e4m3 in the OCP 8-bit floating-point form
+# (sign, 4 exponent bits with bias 7, 3 mantissa bits; exponent field 15
+# with mantissa 7 is NaN, there are no infinities, the largest finite value
+# is 448).  A weight matrix [out][in] keeps one scale per output row; the
+# input of each quantised linear is quantised the same way per token row
+# when the linear runs.  A row with largest magnitude a gets the scale
+# s = a / 448 and the codes round(v * (448 / a)), nearest with ties to the
+# even code, clamped to +-448; the decision is taken in fp32 (the scale, the
+# multiplier and the product are fp32 operations).  An all-zero row gets
+# s = 0 and zero codes.  The quantised linears are the block's two fused
+# GEMMs: h -> [q | k | v | gate | up] and [o | act] -> out.
+# --------------------------------------------------------------------------
+E4M3_MAX = 448.0
+
+
+def e4m3_values():
+    """Value of each of the 256 e4m3 codes (NaN for the two NaN codes)."""
+    code = np.arange(256)
+    sign = np.where(code >> 7, -1.0, 1.0)
+    e = (code >> 3) & 15
+    m = (code & 7).astype(np.float64)
+    mag = np.where(e == 0, m / 8.0 * 2.0 ** -6, (1.0 + m / 8.0) * 2.0 ** (e - 7.0))
+    val = sign * mag
+    val[(e == 15) & (code & 7 == 7)] = np.nan
+    return val
+
+
+E4M3 = e4m3_values()
+
+
+def e4m3_encode(y):
+    """Codes of y rounded to e4m3: nearest value, ties to the even code,
+    magnitudes above 448 saturated to 448, the sign kept (also on zero)."""
+    y = np.asarray(y, dtype=np.float64)
+    a = np.minimum(np.abs(y), E4M3_MAX)
+    # spacing of the values around a: 2^(e - 3) in binade [2^e, 2^(e+1)),
+    # e >= -6 (below 2^-6 the subnormals keep the spacing 2^-9)
+    e = np.floor(np.log2(np.where(a > 0, a, 1.0)))
+    e = np.maximum(e, -6.0)
+    step = 2.0 ** (e - 3.0)
+    n = np.round(a / step)                     # half to even
+    mag = n * step                             # exact: n < 2^5
+    # code of the magnitude: field from its binade, mantissa from the step
+    ef = np.floor(np.log2(np.where(mag > 0, mag, 1.0)))
+    normal = mag >= 2.0 ** -6
+    exp_field = np.where(normal, ef + 7.0, 0.0)
+    mant = np.where(normal, mag / 2.0 ** ef * 8.0 - 8.0, mag / 2.0 ** -9)
+    code = (exp_field.astype(np.int64) << 3) | mant.astype(np.int64)
+    code = np.where(np.signbit(y), code | 0x80, code)
+    return code.astype(np.uint8)
+
+
+def quantize_rowwise(a):
+    """Rowwise e4m3 quantisation of a 2-D array (read as fp32): returns
+    (codes uint8 [R][K], scales fp32 [R]) with a ~= E4M3[codes] * scale."""
+    a32 = np.asarray(a, dtype=np.float32)
+    amax = np.max(np.abs(a32), axis=1) if a32.shape[1] else np.zeros(a32.shape[0], np.float32)
+    pos = amax > 0
+    mult = np.zeros_like(amax)
+    mult[pos] = np.float32(E4M3_MAX) / amax[pos]
+    y = a32 * mult[:, None]                    # fp32 product
+    codes = e4m3_encode(y)
+    scale = (amax / np.float32(E4M3_MAX)).astype(np.float32)
+    return codes, scale
+
+
+def dequantize_rowwise(codes, scale, dtype=np.float64):
+    """E4M3[codes] * scale per row (exact in float64)."""
+    return (E4M3[np.asarray(codes)] * np.asarray(scale, np.float64)[:, None]).astype(dtype)
+
+
+def fake_quantize_rows(a, dtype=np.float64):
+    """The values a rowwise-quantised operand stands for."""
+    codes, scale = quantize_rowwise(a)
+    return dequantize_rowwise(codes, scale, dtype)
+
+
+def fused_block_matrices(w):
+    """The block's two fused linears as plain matrices (bf16 values):
+    W1 = [wq; wk; wv; w_gate; w_up] [3D + 2F][D] and W2 = [wo | w_down]
+    [D][D + F]."""
+    f = _weights(w, np.float64)
+    w1 = np.concatenate([f["wq"], f["wk"], f["wv"], f["w_gate"], f["w_up"]], axis=0)
+    w2 = np.concatenate([f["wo"], f["w_down"]], axis=1)
+    return w1, w2
+
+
+def quantize_block_weights(w):
+    """Rowwise-FP8 form of one block's weights: {"w1": (codes, scales),
+    "w2": (codes, scales), "q_norm", "k_norm"} with W1, W2 as in
+    fused_block_matrices."""
+    w1, w2 = fused_block_matrices(w)
+    return {"w1": quantize_rowwise(w1), "w2": quantize_rowwise(w2),
+            "q_norm": np.asarray(w["q_norm"]), "k_norm": np.asarray(w["k_norm"])}
+
+
+def block_forward_quantized(x, w1, w2, norms, segs, mod, rope, act_quant, heads=None,
+                            dtype=np.float64, eps_ln=EPS_LN, eps_rms=EPS_RMS, keep=False,
+                            rows=None, attn_chunk=None):
+    """block_forward with the weights given as the fused W1 [3D + 2F][D] and
+    W2 [D][D + F] (any values, e.g. dequantised codes) and with act_quant
+    applied to the input of each fused linear, the modulated h and the
+    concatenation [o | act].  norms = (q_norm, k_norm).  rows: evaluate the
+    output only at these rows (keys and values still come from every
+    token).  keep=True also returns {h, y1, o, act, cat, out}."""
+    x = np.asarray(x, dtype=dtype)
+    n, width = x.shape
+    q_norm, k_norm = (as_float(v, dtype) for v in norms)
+    hd = q_norm.shape[0]
+    if heads is None:
+        heads = width // hd
+    f = (w1.shape[0] - 3 * width) // 2
+    shift, scale, gate = _row_modulation(segs, mod, n, dtype)
+    h = modulate(layer_norm(x, eps_ln), shift, scale)
+    hq = np.asarray(act_quant(h), dtype=dtype)
+    w1 = as_float(w1, dtype)
+    k = (hq @ w1[width:2 * width].T).reshape(n, heads, hd)
+    v = (hq @ w1[2 * width:3 * width].T).reshape(n, heads, hd)
+    k = apply_rope(rms_norm_heads(k, k_norm, eps_rms), rope)
+    sel = np.arange(n) if rows is None else np.asarray(rows, dtype=np.int64)
+    y1 = hq[sel] @ w1[np.r_[0:width, 3 * width:3 * width + 2 * f]].T
+    q = y1[:, :width].reshape(len(sel), heads, hd)
+    q = apply_rope(rms_norm_heads(q, q_norm, eps_rms), rope[sel])
+    o = attention(q, k, v, chunk=attn_chunk).reshape(len(sel), width)
+    act = silu(y1[:, width:width + f]) * y1[:, width + f:]
+    cat = np.concatenate([o, act], axis=1)
+    out = np.asarray(act_quant(cat), dtype=dtype) @ as_float(w2, dtype).T
+    x_new = x[sel] + gate[sel] * out
+    if keep:
+        return x_new, {"h": h, "y1": y1, "o": o, "act": act, "cat": cat, "out": out}
+    return x_new
+
+
+def block_forward_fp8(x, w8, segs, mod, rope, heads=None, dtype=np.float64, rows=None,
+                      keep=False, attn_chunk=None):
+    """One block with rowwise-FP8 linears: the weights of
+    quantize_block_weights, and h and [o | act] quantised per token row
+    (the linear itself is exact on the dequantised values)."""
+    w1 = dequantize_rowwise(*w8["w1"])
+    w2 = dequantize_rowwise(*w8["w2"])
+    return block_forward_quantized(x, w1, w2, (w8["q_norm"], w8["k_norm"]), segs, mod, rope,
+                                   fake_quantize_rows, heads=heads, dtype=dtype, rows=rows,
+                                   keep=keep, attn_chunk=attn_chunk)

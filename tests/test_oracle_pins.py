@@ -679,3 +679,180 @@ def test_transformer_stage_modulation_goes_to_its_stage():
     w_mod3 = [{m: w * 3.0 for m, w in w_mod[0].items()}, w_mod[1]]
     c = O.transformer_forward(text, image, refs, segs, io, emb, w_mod3, per_mode, [], tab, 0.4)
     assert not np.allclose(a, c)
+
+
+# --------------------------------------------------------------------------
+# rowwise FP8 (e4m3) quantisation and the block with FP8 linears
+# --------------------------------------------------------------------------
+def test_e4m3_format_constants():
+    """The OCP e4m3 format: bias 7, 3 mantissa bits, subnormals 2^-9 apart,
+    largest finite 448, the all-ones codes NaN, codes ordered by value."""
+    v = O.E4M3
+    assert v[0x00] == 0.0 and np.signbit(v[0x80])
+    assert v[0x01] == 2.0 ** -9 and v[0x07] == 7 * 2.0 ** -9
+    assert v[0x08] == 2.0 ** -6 and v[0x38] == 1.0 and v[0x39] == 1.125
+    assert v[0x7E] == 448.0 and v[0x77] == 240.0
+    assert np.isnan(v[0x7F]) and np.isnan(v[0xFF])
+    pos = v[:0x7F]
+    assert np.all(np.diff(pos) > 0)                       # monotone in the code
+    np.testing.assert_array_equal(v[0x80:0xFF], -pos)     # sign-magnitude
+
+
+def _e4m3_brute(y):
+    """Nearest of the 127 non-negative values by search, ties to the even
+    code, saturating; sign copied."""
+    table = [(c, O.E4M3[c]) for c in range(0x7F)]
+    out = []
+    for t in np.asarray(y, np.float64).ravel():
+        a = min(abs(t), 448.0)
+        best = None
+        for c, val in table:
+            d = abs(val - a)
+            if best is None or d < best[1] or (d == best[1] and c % 2 == 0):
+                best = (c, d)
+        out.append(best[0] | (0x80 if np.signbit(t) else 0))
+    return np.array(out, np.uint8).reshape(np.shape(y))
+
+
+def test_e4m3_encode_vs_brute_force():
+    """Round to nearest, ties to even, on every value, every midpoint and its
+    neighbours, random magnitudes over the whole range, and beyond 448."""
+    vals = O.E4M3[:0x7F]
+    mids = (vals[:-1] + vals[1:]) / 2
+    rng = np.random.default_rng(5)
+    rand = rng.standard_normal(3000) * np.exp2(rng.uniform(-12, 10, 3000))
+    y = np.concatenate([vals, -vals, mids, -mids, np.nextafter(mids, 0), np.nextafter(mids, 1e9),
+                        rand, [448.0, 449.0, 463.9, 464.0, 465.0, 1e6, -1e6, 2.0 ** -10,
+                               1.5 * 2.0 ** -10, -2.0 ** -11, 0.0, -0.0]])
+    y = y.astype(np.float32).astype(np.float64)            # the inputs are fp32
+    np.testing.assert_array_equal(O.e4m3_encode(y), _e4m3_brute(y))
+
+
+def test_e4m3_ties_go_to_even_codes():
+    vals = O.E4M3[:0x7F]
+    mids = (vals[:-1] + vals[1:]) / 2
+    codes = O.e4m3_encode(mids)
+    assert np.all(codes % 2 == 0)
+    assert np.all((codes == np.arange(0x7E)) | (codes == np.arange(1, 0x7F)))
+
+
+def test_quantize_rowwise_scale_and_error_bound():
+    """Scale = row max / 448; the row maximum maps to +-448; every element
+    within half a step of its value (2^-4 relative for normals, 2^-10 s in
+    the subnormal range)."""
+    rng = np.random.default_rng(6)
+    a = (rng.standard_normal((40, 300)) * np.exp2(rng.uniform(-20, 20, (40, 1)))).astype(np.float32)
+    codes, s = O.quantize_rowwise(a)
+    amax = np.abs(a).max(axis=1)
+    np.testing.assert_array_equal(s, (amax / np.float32(448)).astype(np.float32))
+    arg = np.abs(a).argmax(axis=1)
+    assert np.all(np.abs(O.E4M3[codes[np.arange(40), arg]]) == 448.0)
+    deq = O.dequantize_rowwise(codes, s)
+    y = np.abs(a.astype(np.float64)) / s[:, None].astype(np.float64)   # position on the grid
+    err = np.abs(deq - a) / s[:, None]
+    bound = np.where(y >= 2.0 ** -6, y * 2.0 ** -4, 2.0 ** -10) * (1 + 1e-6)
+    assert np.all(err <= bound)
+    assert np.all(np.sign(deq) * np.sign(a) >= 0)
+
+
+def test_quantize_rowwise_special_rows():
+    """A zero row gives scale 0 and zero codes; a row already on the e4m3
+    grid with maximum 448 is returned as is (scale 1); scaling a row by a
+    power of two scales only its scale."""
+    rng = np.random.default_rng(7)
+    on_grid = O.E4M3[rng.integers(0, 0x7E, (3, 64))] * rng.choice([-1, 1], (3, 64))
+    on_grid[:, 5] = 448.0
+    rows = np.vstack([np.zeros((1, 64)), on_grid])
+    codes, s = O.quantize_rowwise(rows)
+    assert s[0] == 0 and np.all(O.E4M3[codes[0]] == 0)
+    np.testing.assert_array_equal(s[1:], 1.0)
+    np.testing.assert_array_equal(O.E4M3[codes[1:]], on_grid)
+    b = rng.standard_normal((4, 50)).astype(np.float32)
+    c1, s1 = O.quantize_rowwise(b)
+    c2, s2 = O.quantize_rowwise(b * np.float32(2.0 ** -7))
+    np.testing.assert_array_equal(c1, c2)
+    np.testing.assert_array_equal(s2, s1 * np.float32(2.0 ** -7))
+
+
+def test_fused_matrices_split_back_into_the_linears():
+    D, F = 128, 48
+    w = _tiny_weights(D, F)
+    w1, w2 = O.fused_block_matrices(w)
+    assert w1.shape == (3 * D + 2 * F, D) and w2.shape == (D, D + F)
+    h = _rand(5, D)
+    y = h @ w1.T
+    for name, lo, hi in [("wq", 0, D), ("wk", D, 2 * D), ("wv", 2 * D, 3 * D),
+                         ("w_gate", 3 * D, 3 * D + F), ("w_up", 3 * D + F, 3 * D + 2 * F)]:
+        np.testing.assert_allclose(y[:, lo:hi], h @ w[name].T, rtol=1e-12, atol=1e-12)
+    o, act = _rand(5, D), _rand(5, F)
+    np.testing.assert_allclose(np.hstack([o, act]) @ w2.T, o @ w["wo"].T + act @ w["w_down"].T,
+                               rtol=1e-12, atol=1e-12)
+
+
+def _fp8_case(D=256, F=64, n=9):
+    w = _tiny_weights(D, F)
+    x = _rand(n, D)
+    segs = [(0, 3, 0), (3, n - 3, 1)]
+    mod = _rand(2, 3, D) * 0.2
+    tab = O.rope_tables(O.token_positions(3, 2, (n - 3) // 2))
+    return w, x, segs, mod, tab
+
+
+def test_quantized_block_with_identity_quantiser_is_the_block():
+    """With the unquantised fused weights and no activation quantisation the
+    FP8 block's structure reduces to block_forward (pinned by brute force)."""
+    w, x, segs, mod, tab = _fp8_case()
+    w1, w2 = O.fused_block_matrices(w)
+    got = O.block_forward_quantized(x, w1, w2, (w["q_norm"], w["k_norm"]), segs, mod, tab,
+                                    lambda a: a)
+    np.testing.assert_allclose(got, O.block_forward(x, w, segs, mod, tab), rtol=1e-12, atol=1e-12)
+    rows = [0, 4, 8]
+    got_r = O.block_forward_quantized(x, w1, w2, (w["q_norm"], w["k_norm"]), segs, mod, tab,
+                                      lambda a: a, rows=rows)
+    np.testing.assert_allclose(got_r, got[rows], rtol=1e-12, atol=1e-12)
+
+
+def test_quantized_block_quantises_h_then_the_concatenation():
+    """The activation quantiser sees exactly the two GEMM inputs: the
+    modulated h [n][D], then [o | act] [n][D + F]."""
+    w, x, segs, mod, tab = _fp8_case()
+    _, inter = O.block_forward(x, w, segs, mod, tab, keep=True)
+    seen = []
+
+    def record(a):
+        seen.append(np.array(a))
+        return a
+
+    w1, w2 = O.fused_block_matrices(w)
+    O.block_forward_quantized(x, w1, w2, (w["q_norm"], w["k_norm"]), segs, mod, tab, record)
+    assert len(seen) == 2
+    np.testing.assert_allclose(seen[0], inter["h"], rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(seen[1], np.hstack([inter["o"], inter["act"]]), rtol=1e-10,
+                               atol=1e-12)
+
+
+def test_fp8_block_is_the_block_on_dequantised_operands():
+    """block_forward_fp8 uses the dequantised codes of quantize_block_weights
+    and rowwise-quantised activations; its change against the bf16-weight
+    block is of the size 3-bit mantissas give (a few percent of the block
+    delta), and is not zero."""
+    w, x, segs, mod, tab = _fp8_case(n=13)
+    w8 = O.quantize_block_weights(w)
+    w1, w2 = O.fused_block_matrices(w)
+    c1, s1 = w8["w1"]
+    c1_want, s1_want = O.quantize_rowwise(w1)
+    np.testing.assert_array_equal(c1, c1_want)
+    np.testing.assert_array_equal(s1, s1_want)
+    got = O.block_forward_fp8(x, w8, segs, mod, tab)
+    ref = O.block_forward(x, w, segs, mod, tab)
+    d_got, d_ref = got - x, ref - x
+    rel = np.linalg.norm(d_got - d_ref) / np.linalg.norm(d_ref)
+    assert 1e-3 < rel < 0.1, rel
+    deq = O.block_forward_quantized(x, O.dequantize_rowwise(*w8["w1"]),
+                                    O.dequantize_rowwise(*w8["w2"]),
+                                    (w["q_norm"], w["k_norm"]), segs, mod, tab,
+                                    O.fake_quantize_rows)
+    np.testing.assert_array_equal(got, deq)
+    rows = [1, 6, 12]
+    np.testing.assert_allclose(O.block_forward_fp8(x, w8, segs, mod, tab, rows=rows), got[rows],
+                               rtol=1e-12, atol=1e-12)
