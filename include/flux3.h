@@ -78,21 +78,28 @@ typedef struct {
 } flux3_segment;
 
 /* Layouts of a block's weight matrices (flux3_block_weights.layout). */
-enum { FLUX3_WEIGHTS_LINEAR = 0, FLUX3_WEIGHTS_PACKED = 1 };
+enum { FLUX3_WEIGHTS_LINEAR = 0, FLUX3_WEIGHTS_PACKED = 1, FLUX3_WEIGHTS_FP8R = 2 };
 
 /* One block's weights, all device pointers.  Matrices are bf16, no biases
  * [P3 block listing; P4], in torch Linear layout [out][in] row-major
  * (layout = FLUX3_WEIGHTS_LINEAR, the zero value) or in the packed operand
- * layout that flux3_weights_pack writes (FLUX3_WEIGHTS_PACKED):
+ * layout that flux3_weights_pack writes (FLUX3_WEIGHTS_PACKED), or rowwise
+ * e4m3 codes that flux3_weights_quantize_fp8r writes (FLUX3_WEIGHTS_FP8R):
  *   wq, wk, wv, wo : [width][width]
  *   w_gate, w_up   : [mlp_hidden][width]   (silu acts on the w_gate branch)
  *   w_down         : [width][mlp_hidden]
- *   q_norm, k_norm : fp32 [head_dim] RMSNorm scales for queries and keys. */
+ *   q_norm, k_norm : fp32 [head_dim] RMSNorm scales for queries and keys.
+ *   s_proj, s_out  : FLUX3_WEIGHTS_FP8R only (ignored otherwise): fp32
+ *                    dequantisation scale of each output row, s_proj
+ *                    [3 width + 2 mlp_hidden] for the rows of wq, wk, wv,
+ *                    w_gate, w_up in that order, s_out [width] for the rows
+ *                    of the output linear [wo | w_down]. */
 typedef struct {
   const void *wq, *wk, *wv, *wo;
   const void *w_gate, *w_up, *w_down;
   const float *q_norm, *k_norm;
   int32_t layout;
+  const float *s_proj, *s_out;
 } flux3_block_weights;
 
 /* Bytes of one block's seven matrices in the packed operand layout (each
@@ -117,6 +124,43 @@ size_t flux3_weights_packed_bytes(const flux3_dims *dims);
 flux3_status flux3_weights_pack(const flux3_dims *dims, const flux3_block_weights *in,
                                 void *buffer, size_t buffer_bytes, flux3_block_weights *out,
                                 void *stream);
+
+/* Bytes of one block's weights in the rowwise-FP8 form: the seven code
+ * matrices (one byte per value) and the two scale arrays, each on a
+ * 256-byte boundary; 0 if dims are unsupported. */
+size_t flux3_weights_fp8r_bytes(const flux3_dims *dims);
+
+/* The rowwise-FP8 ("fp8r") form of one block's weights [P1 "Smaller GPUs,
+ * single files, and custom LoRA training": the rowwise-FP8 single file;
+ * P4 "What Black Forest Labs released": FP8 files and FP8 kernels].
+ * Each output row of the block's two fused linears, [wq; wk; wv; w_gate;
+ * w_up] (over width inputs) and [wo | w_down] (over width + mlp_hidden
+ * inputs), with largest magnitude a gets the scale s = a / 448 and the
+ * e4m3 codes (OCP 8-bit float: bias 7, 3 mantissa bits, largest 448) of
+ * its values times 448 / a: nearest, ties to the even code, clamped to
+ * +-448, every step in fp32; an all-zero row gets s = 0 and zero codes.
+ * A block run with these weights quantises its two GEMM inputs, the
+ * modulated h and [o | act], the same way per token row and runs both
+ * GEMMs on the fp8 matrix cores with fp32 accumulation; the rest of the
+ * block is unchanged.  Done once per weight set.
+ *   in     : layout FLUX3_WEIGHTS_LINEAR, all pointers valid and aligned.
+ *   buffer : device, >= flux3_weights_fp8r_bytes(dims), 256-byte aligned;
+ *            owned by the caller and must outlive every use of *out.
+ *   out    : host struct with the code matrices and scales in buffer, the
+ *            norm pointers of in, and layout FLUX3_WEIGHTS_FP8R.  A code
+ *            matrix [R][K] is stored in the packed fp8 layout: 1-KiB blocks
+ *            of 8 rows x 128 codes, block (row / 8, k / 128) at block index
+ *            (row / 8) (K / 128) + k / 128, row row % 8 taking 128 bytes of
+ *            it, its 16-byte chunk c (codes 16c .. 16c + 15) in slot
+ *            c ^ ((row / 2) % 8).
+ * Asynchronous on stream.  Errors: FLUX3_E_INVALID (null or not Linear
+ * in), FLUX3_E_UNSUPPORTED (dims; also width + mlp_hidden > 16384 or
+ * mlp_hidden >= 7 width, where the per-token codes of [o | act] would not
+ * fit the block workspace), FLUX3_E_ALIGN, FLUX3_E_WORKSPACE (buffer too
+ * small), FLUX3_E_HIP. */
+flux3_status flux3_weights_quantize_fp8r(const flux3_dims *dims, const flux3_block_weights *in,
+                                         void *buffer, size_t buffer_bytes,
+                                         flux3_block_weights *out, void *stream);
 
 /* Token layout of one call: n_text text tokens, a grid_h x grid_w noisy
  * image grid (raster order), then n_refs reference grids ref_h[k] x ref_w[k]
@@ -415,7 +459,8 @@ enum {
   FLUX3_K_MODULATION = 5,   /* one record per flux3_modulation_forward call */
   FLUX3_K_IO_LINEARS = 6,   /* each input / output linear of a transformer call */
   FLUX3_K_EULER = 7,        /* each flux3_euler_step (and sampler step update) */
-  FLUX3_K_COUNT = 8
+  FLUX3_K_QUANT = 8,        /* per-token e4m3 quantisation of [o | act] (FP8R blocks) */
+  FLUX3_K_COUNT = 9
 };
 typedef struct {
   int64_t launches;

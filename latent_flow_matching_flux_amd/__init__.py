@@ -10,7 +10,8 @@ from ._lib import (Flux3Error, Dims, Segment, BlockWeights, RopeLayout, Workspac
                    LIB_PATH, KERNELS, profile_enable, profile_reset, profile_read,
                    device_query, modulation_workspace_bytes, modulation_forward,
                    ModulationWeights, weights_packed_bytes, weights_pack, WEIGHTS_LINEAR,
-                   WEIGHTS_PACKED, IoDims, IoWeights, transformer_workspace_bytes,
+                   WEIGHTS_PACKED, WEIGHTS_FP8R, weights_fp8r_bytes, weights_quantize_fp8r,
+                   IoDims, IoWeights, transformer_workspace_bytes,
                    transformer_forward, sigmas, euler_step, sample_workspace_bytes, sample)
 
 __all__ = ["Flux3Error", "Dims", "Segment", "BlockWeights", "RopeLayout", "WorkspaceLayout",
@@ -19,5 +20,6 @@ __all__ = ["Flux3Error", "Dims", "Segment", "BlockWeights", "RopeLayout", "Works
            "LIB_PATH", "KERNELS", "profile_enable", "profile_reset", "profile_read",
            "device_query", "modulation_workspace_bytes", "modulation_forward",
            "ModulationWeights", "weights_packed_bytes", "weights_pack", "WEIGHTS_LINEAR",
-           "WEIGHTS_PACKED", "IoDims", "IoWeights", "transformer_workspace_bytes",
+           "WEIGHTS_PACKED", "WEIGHTS_FP8R", "weights_fp8r_bytes", "weights_quantize_fp8r",
+           "IoDims", "IoWeights", "transformer_workspace_bytes",
            "transformer_forward", "sigmas", "euler_step", "sample_workspace_bytes", "sample"]

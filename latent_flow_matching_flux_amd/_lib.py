@@ -22,6 +22,7 @@ MAX_REFS = 15
 EXPORTS = ("flux3_layout_tokens", "flux3_rope_tables_build", "flux3_workspace_bytes",
            "flux3_workspace_layout_get", "flux3_block_forward", "flux3_stack_forward",
            "flux3_weights_packed_bytes", "flux3_weights_pack",
+           "flux3_weights_fp8r_bytes", "flux3_weights_quantize_fp8r",
            "flux3_transformer_workspace_bytes", "flux3_transformer_forward",
            "flux3_sigmas", "flux3_euler_step", "flux3_sample_workspace_bytes", "flux3_sample",
            "flux3_modulation_workspace_bytes", "flux3_modulation_forward",
@@ -29,7 +30,7 @@ EXPORTS = ("flux3_layout_tokens", "flux3_rope_tables_build", "flux3_workspace_by
            "flux3_device_query", "flux3_set_debug_sync", "flux3_status_string",
            "flux3_last_error_detail")
 KERNELS = ("rope_tables", "ln_modulate", "gemm_proj", "attention", "gemm_out", "modulation",
-           "io_linears", "euler")
+           "io_linears", "euler", "quant")
 
 
 class Flux3Error(RuntimeError):
@@ -48,13 +49,14 @@ class Segment(ctypes.Structure):
     _fields_ = [("start", ctypes.c_int32), ("count", ctypes.c_int32), ("mode", ctypes.c_int32)]
 
 
-WEIGHTS_LINEAR, WEIGHTS_PACKED = 0, 1
+WEIGHTS_LINEAR, WEIGHTS_PACKED, WEIGHTS_FP8R = 0, 1, 2
 MATRICES = ("wq", "wk", "wv", "wo", "w_gate", "w_up", "w_down")
 
 
 class BlockWeights(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in MATRICES + ("q_norm", "k_norm")] + \
-               [("layout", ctypes.c_int32)]
+               [("layout", ctypes.c_int32), ("s_proj", ctypes.c_void_p),
+                ("s_out", ctypes.c_void_p)]
 
 
 class ModulationWeights(ctypes.Structure):
@@ -125,6 +127,11 @@ def load(path=LIB_PATH):
     lib.flux3_weights_packed_bytes.restype = sz
     lib.flux3_weights_pack.argtypes = [P(Dims), P(BlockWeights), vp, sz, P(BlockWeights), vp]
     lib.flux3_weights_pack.restype = i32
+    lib.flux3_weights_fp8r_bytes.argtypes = [P(Dims)]
+    lib.flux3_weights_fp8r_bytes.restype = sz
+    lib.flux3_weights_quantize_fp8r.argtypes = [P(Dims), P(BlockWeights), vp, sz,
+                                                P(BlockWeights), vp]
+    lib.flux3_weights_quantize_fp8r.restype = i32
     lib.flux3_transformer_workspace_bytes.argtypes = [P(Dims), P(IoDims), i64]
     lib.flux3_transformer_workspace_bytes.restype = sz
     lib.flux3_transformer_forward.argtypes = [P(Dims), P(IoDims), P(IoWeights),
@@ -208,11 +215,13 @@ def make_segments(segs):
 
 def make_weights(w):
     """BlockWeights from a dict of tensors (keys as in the header struct; an
-    optional "layout" entry, default WEIGHTS_LINEAR)."""
+    optional "layout" entry, default WEIGHTS_LINEAR; "s_proj" and "s_out"
+    for WEIGHTS_FP8R)."""
     if isinstance(w, BlockWeights):
         return w
     return BlockWeights(*[_ptr(w.get(k)) for k in MATRICES + ("q_norm", "k_norm")],
-                        int(w.get("layout", WEIGHTS_LINEAR)))
+                        int(w.get("layout", WEIGHTS_LINEAR)), _ptr(w.get("s_proj")),
+                        _ptr(w.get("s_out")))
 
 
 def weights_packed_bytes(dims):
@@ -230,6 +239,24 @@ def weights_pack(dims, w, buffer, stream=None):
                                      if hasattr(buffer, "numel") else 0,
                                      ctypes.byref(out), _stream_handle(stream)))
     # the struct points into buffer and at the caller's norm vectors
+    out._keep = (buffer, w.get("q_norm"), w.get("k_norm")) if isinstance(w, dict) else (buffer, w)
+    return out
+
+
+def weights_fp8r_bytes(dims):
+    return load().flux3_weights_fp8r_bytes(ctypes.byref(make_dims(dims)))
+
+
+def weights_quantize_fp8r(dims, w, buffer, stream=None):
+    """flux3_weights_quantize_fp8r: the rowwise-FP8 form of a block's
+    Linear-layout weights, written into buffer (device, >=
+    weights_fp8r_bytes(dims) bytes).  Returns the BlockWeights pointing into
+    buffer (layout WEIGHTS_FP8R); buffer must stay alive while it is used."""
+    out = BlockWeights()
+    _check(load().flux3_weights_quantize_fp8r(
+        ctypes.byref(make_dims(dims)), ctypes.byref(make_weights(w)), _ptr(buffer),
+        buffer.numel() * buffer.element_size() if hasattr(buffer, "numel") else 0,
+        ctypes.byref(out), _stream_handle(stream)))
     out._keep = (buffer, w.get("q_norm"), w.get("k_norm")) if isinstance(w, dict) else (buffer, w)
     return out
 

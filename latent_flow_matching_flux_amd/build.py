@@ -18,7 +18,7 @@ COMMON = [
     "-Wall", "-Wno-unused-function", "-Wno-unknown-pragmas",
 ]
 
-SOURCES = ["rope.hip", "ln_modulate.hip", "gemm.hip", "attention.hip", "modulation.hip",
+SOURCES = ["rope.hip", "ln_modulate.hip", "gemm.hip", "attention.hip", "modulation.hip", "quant.hip",
            "sampler.hip", "abi.cpp"]
 
 

@@ -107,7 +107,21 @@ bool layout_of(const flux3_dims* d, int64_t n, flux3_workspace_layout* L) {
   return true;
 }
 
-flux3_status check_weights(const flux3_block_weights* w, const char* what, int idx) {
+// What a rowwise-fp8 block needs of the dims: the quantiser's row length,
+// and the codes and scales of [o | act] within the workspace's h, q, k and vt
+// buffers (8 width bytes per padded row).
+flux3_status check_fp8_dims(const flux3_dims* d) {
+  const int D = d->width, F = d->mlp_hidden;
+  if (D + F > flux3::kQuantMaxK)
+    return fail(FLUX3_E_UNSUPPORTED, "fp8r weights: width + mlp_hidden %d > %d", D + F,
+                flux3::kQuantMaxK);
+  if (F >= 7 * D)
+    return fail(FLUX3_E_UNSUPPORTED, "fp8r weights: mlp_hidden %d >= 7 width", F);
+  return FLUX3_OK;
+}
+
+flux3_status check_weights(const flux3_block_weights* w, const char* what, int idx,
+                           const flux3_dims* d) {
   if (!w) return fail(FLUX3_E_INVALID, "%s[%d] weights struct is NULL", what, idx);
   const void* ptrs[9] = {w->wq, w->wk, w->wv, w->wo, w->w_gate, w->w_up, w->w_down,
                          w->q_norm, w->k_norm};
@@ -118,9 +132,18 @@ flux3_status check_weights(const flux3_block_weights* w, const char* what, int i
     if (!aligned16(ptrs[i]))
       return fail(FLUX3_E_ALIGN, "%s[%d].%s is not 16-byte aligned", what, idx, names[i]);
   }
-  if (w->layout != FLUX3_WEIGHTS_LINEAR && w->layout != FLUX3_WEIGHTS_PACKED)
+  if (w->layout != FLUX3_WEIGHTS_LINEAR && w->layout != FLUX3_WEIGHTS_PACKED &&
+      w->layout != FLUX3_WEIGHTS_FP8R)
     return fail(FLUX3_E_INVALID, "%s[%d].layout %d is not a FLUX3_WEIGHTS_* value", what, idx,
                 w->layout);
+  if (w->layout == FLUX3_WEIGHTS_FP8R) {
+    if (!w->s_proj || !w->s_out)
+      return fail(FLUX3_E_INVALID, "%s[%d]: fp8r weights need s_proj and s_out", what, idx);
+    if (!aligned16(w->s_proj) || !aligned16(w->s_out))
+      return fail(FLUX3_E_ALIGN, "%s[%d]: s_proj or s_out is not 16-byte aligned", what, idx);
+    flux3_status r = check_fp8_dims(d);
+    if (r != FLUX3_OK) return r;
+  }
   return FLUX3_OK;
 }
 
@@ -181,7 +204,10 @@ flux3::BlockWeightsDev dev_weights(const flux3_block_weights& w) {
   d.wq = w.wq; d.wk = w.wk; d.wv = w.wv; d.wo = w.wo;
   d.w_gate = w.w_gate; d.w_up = w.w_up; d.w_down = w.w_down;
   d.q_norm = w.q_norm; d.k_norm = w.k_norm;
-  d.packed = w.layout == FLUX3_WEIGHTS_PACKED;
+  d.packed = w.layout == FLUX3_WEIGHTS_PACKED || w.layout == FLUX3_WEIGHTS_FP8R;
+  d.fp8 = w.layout == FLUX3_WEIGHTS_FP8R;
+  d.s_proj = d.fp8 ? w.s_proj : nullptr;
+  d.s_out = d.fp8 ? w.s_out : nullptr;
   return d;
 }
 
@@ -200,18 +226,31 @@ flux3_status run_block(const flux3_dims* d, const flux3_block_weights& w, float*
                        void* ws, hipStream_t s) {
   flux3_workspace_layout L;
   layout_of(d, n, &L);
-  const flux3::WsPtrs wp = carve(ws, L);
+  flux3::WsPtrs wp = carve(ws, L);
+  const flux3::BlockWeightsDev wd = dev_weights(w);
+  if (wd.fp8) {
+    // h's codes and scales in h's buffer (dead until the next block's K1);
+    // those of [o | act] from the start of h over q, k and vt, which nothing
+    // reads once attention is done (check_fp8_dims keeps them below cat)
+    char* base = static_cast<char*>(wp.h);
+    const size_t n_pad = (size_t)L.n_pad;
+    wp.h8 = base;
+    wp.sh = reinterpret_cast<float*>(base + n_pad * (size_t)d->width);
+    wp.cat8 = base;
+    wp.scat = reinterpret_cast<float*>(
+        base + align_up(n_pad * (size_t)(d->width + d->mlp_hidden), kBufAlign));
+  }
   flux3::BlockShape bs;
   bs.M = (int32_t)n;
   bs.n_pad = (int32_t)L.n_pad;
   bs.D = d->width;
   bs.H = d->heads;
   bs.F = d->mlp_hidden;
-  const flux3::BlockWeightsDev wd = dev_weights(w);
   flux3_status r;
   const double m = (double)n;
   int pi = prof_begin(FLUX3_K_LN_MODULATE, m, s);
-  hipError_t e = flux3::launch_ln_modulate(bs, x, mod, st, wp.h, kEpsLN, s);
+  hipError_t e = wd.fp8 ? flux3::launch_ln_modulate_f8(bs, x, mod, st, wp.h8, wp.sh, kEpsLN, s)
+                        : flux3::launch_ln_modulate(bs, x, mod, st, wp.h, kEpsLN, s);
   prof_end(pi, s);
   if ((r = after_launch(e, "ln_modulate", s)) != FLUX3_OK) return r;
   pi = prof_begin(FLUX3_K_GEMM_PROJ, m, s);
@@ -222,6 +261,12 @@ flux3_status run_block(const flux3_dims* d, const flux3_block_weights& w, float*
   e = flux3::launch_attention(bs, wp, s);
   prof_end(pi, s);
   if ((r = after_launch(e, "attention", s)) != FLUX3_OK) return r;
+  if (wd.fp8) {
+    pi = prof_begin(FLUX3_K_QUANT, m, s);
+    e = flux3::launch_quant_packed_rows(wp.cat, wp.cat8, wp.scat, bs.M, bs.D + bs.F, s);
+    prof_end(pi, s);
+    if ((r = after_launch(e, "quant_cat", s)) != FLUX3_OK) return r;
+  }
   pi = prof_begin(FLUX3_K_GEMM_OUT, m, s);
   e = flux3::launch_gemm_out(bs, wd, wp, x, mod, st, s);
   prof_end(pi, s);
@@ -283,22 +328,22 @@ flux3_status prepare_modulation(const flux3_dims* dims, const flux3_modulation_w
 }
 
 // Weight checks of a stack's blocks for the segments in use.
-flux3_status check_stack_weights(const flux3_block_weights* per_mode, int32_t n_pm,
-                                 const flux3_block_weights* joint, int32_t n_joint,
-                                 const flux3_segment* segs, int32_t n_segs) {
+flux3_status check_stack_weights(const flux3_dims* d, const flux3_block_weights* per_mode,
+                                 int32_t n_pm, const flux3_block_weights* joint,
+                                 int32_t n_joint, const flux3_segment* segs, int32_t n_segs) {
   flux3_status r;
   if (n_pm > 0) {
     if (!per_mode) return fail(FLUX3_E_INVALID, "per_mode is NULL");
     for (int s = 0; s < n_segs; ++s)
       for (int b = 0; b < n_pm; ++b)
         if ((r = check_weights(&per_mode[segs[s].mode * n_pm + b], "per_mode",
-                               segs[s].mode * n_pm + b)) != FLUX3_OK)
+                               segs[s].mode * n_pm + b, d)) != FLUX3_OK)
           return r;
   }
   if (n_joint > 0) {
     if (!joint) return fail(FLUX3_E_INVALID, "joint is NULL");
     for (int b = 0; b < n_joint; ++b)
-      if ((r = check_weights(&joint[b], "joint", b)) != FLUX3_OK) return r;
+      if ((r = check_weights(&joint[b], "joint", b, d)) != FLUX3_OK) return r;
   }
   return FLUX3_OK;
 }
@@ -488,7 +533,7 @@ flux3_status flux3_weights_pack(const flux3_dims* dims, const flux3_block_weight
                                 void* stream) {
   flux3_status r = check_dims(dims);
   if (r != FLUX3_OK) return r;
-  if ((r = check_weights(in, "in", 0)) != FLUX3_OK) return r;
+  if ((r = check_weights(in, "in", 0, dims)) != FLUX3_OK) return r;
   if (in->layout != FLUX3_WEIGHTS_LINEAR)
     return fail(FLUX3_E_INVALID, "in is already packed");
   if (!out) return fail(FLUX3_E_INVALID, "out is NULL");
@@ -519,6 +564,74 @@ flux3_status flux3_weights_pack(const flux3_dims* dims, const flux3_block_weight
   return ok();
 }
 
+size_t flux3_weights_fp8r_bytes(const flux3_dims* dims) {
+  if (check_dims(dims) != FLUX3_OK) return 0;
+  const size_t D = (size_t)dims->width, F = (size_t)dims->mlp_hidden;
+  return 4 * align_up(D * D, kBufAlign) + 3 * align_up(D * F, kBufAlign) +
+         align_up((3 * D + 2 * F) * 4, kBufAlign) + align_up(D * 4, kBufAlign);
+}
+
+flux3_status flux3_weights_quantize_fp8r(const flux3_dims* dims, const flux3_block_weights* in,
+                                         void* buffer, size_t buffer_bytes,
+                                         flux3_block_weights* out, void* stream) {
+  flux3_status r = check_dims(dims);
+  if (r != FLUX3_OK) return r;
+  if ((r = check_fp8_dims(dims)) != FLUX3_OK) return r;
+  if ((r = check_weights(in, "in", 0, dims)) != FLUX3_OK) return r;
+  if (in->layout != FLUX3_WEIGHTS_LINEAR)
+    return fail(FLUX3_E_INVALID, "in must be in Linear layout");
+  if (!out) return fail(FLUX3_E_INVALID, "out is NULL");
+  if (!buffer) return fail(FLUX3_E_WORKSPACE, "buffer is NULL");
+  if ((reinterpret_cast<uintptr_t>(buffer) & (kBufAlign - 1)) != 0)
+    return fail(FLUX3_E_ALIGN, "buffer is not %zu-byte aligned", kBufAlign);
+  const size_t need = flux3_weights_fp8r_bytes(dims);
+  if (buffer_bytes < need)
+    return fail(FLUX3_E_WORKSPACE, "buffer has %zu bytes, needs %zu", buffer_bytes, need);
+  const int D = dims->width, F = dims->mlp_hidden;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  // code matrices wq wk wv wo w_gate w_up w_down, then s_proj and s_out
+  const size_t bytes[7] = {(size_t)D * D, (size_t)D * D, (size_t)D * D, (size_t)D * D,
+                           (size_t)F * D, (size_t)F * D, (size_t)D * F};
+  void* dst[7];
+  char* b = static_cast<char*>(buffer);
+  for (int i = 0; i < 7; ++i) {
+    dst[i] = b;
+    b += align_up(bytes[i], kBufAlign);
+  }
+  float* s_proj = reinterpret_cast<float*>(b);
+  b += align_up((size_t)(3 * D + 2 * F) * 4, kBufAlign);
+  float* s_out = reinterpret_cast<float*>(b);
+  // the rows of [wq; wk; wv; w_gate; w_up], one matrix at a time
+  struct Job {
+    const void* w;
+    void* out;
+    int rows;
+    size_t s_off;
+    const char* name;
+  };
+  const Job jobs[5] = {{in->wq, dst[0], D, 0, "wq"},
+                       {in->wk, dst[1], D, (size_t)D, "wk"},
+                       {in->wv, dst[2], D, (size_t)2 * D, "wv"},
+                       {in->w_gate, dst[4], F, (size_t)3 * D, "w_gate"},
+                       {in->w_up, dst[5], F, (size_t)3 * D + F, "w_up"}};
+  for (const Job& j : jobs) {
+    hipError_t e = flux3::launch_quant_weight_rows(j.w, D, nullptr, 0, j.out, nullptr,
+                                                   s_proj + j.s_off, j.rows, s);
+    if ((r = after_launch(e, j.name, s)) != FLUX3_OK) return r;
+  }
+  // [wo | w_down]: one scale per output row over both matrices
+  hipError_t e = flux3::launch_quant_weight_rows(in->wo, D, in->w_down, F, dst[3], dst[6], s_out,
+                                                 D, s);
+  if ((r = after_launch(e, "wo_w_down", s)) != FLUX3_OK) return r;
+  *out = *in;
+  out->wq = dst[0]; out->wk = dst[1]; out->wv = dst[2]; out->wo = dst[3];
+  out->w_gate = dst[4]; out->w_up = dst[5]; out->w_down = dst[6];
+  out->s_proj = s_proj;
+  out->s_out = s_out;
+  out->layout = FLUX3_WEIGHTS_FP8R;
+  return ok();
+}
+
 flux3_status flux3_block_forward(const flux3_dims* dims, const flux3_block_weights* w, float* x,
                                  int64_t n_tokens, const flux3_segment* segs, int32_t n_segs,
                                  const float* mod, const float* rope, void* workspace,
@@ -531,7 +644,7 @@ flux3_status flux3_block_forward(const flux3_dims* dims, const flux3_block_weigh
     if (n_segs != 0) return fail(FLUX3_E_SHAPE, "n_tokens is 0 but n_segs is %d", n_segs);
     return ok();
   }
-  if ((r = check_weights(w, "w", 0)) != FLUX3_OK) return r;
+  if ((r = check_weights(w, "w", 0, dims)) != FLUX3_OK) return r;
   if (!x || !mod || !rope) return fail(FLUX3_E_INVALID, "x, mod or rope is NULL");
   if (!aligned16(x) || !aligned16(mod) || !aligned16(rope))
     return fail(FLUX3_E_ALIGN, "x, mod or rope is not 16-byte aligned");
@@ -571,7 +684,8 @@ flux3_status flux3_stack_forward(const flux3_dims* dims, const flux3_block_weigh
     if (!mod_stage2) return fail(FLUX3_E_INVALID, "mod_stage2 is NULL");
     if (!aligned16(mod_stage2)) return fail(FLUX3_E_ALIGN, "mod_stage2 is not 16-byte aligned");
   }
-  if ((r = check_stack_weights(per_mode, n_pm, joint, n_joint, segs, n_segs)) != FLUX3_OK) return r;
+  if ((r = check_stack_weights(dims, per_mode, n_pm, joint, n_joint, segs, n_segs)) != FLUX3_OK)
+    return r;
   if (mod_block_stride % 4 != 0)
     return fail(FLUX3_E_ALIGN, "mod_block_stride must be a multiple of 4 floats");
   flux3_workspace_layout L;
@@ -688,7 +802,8 @@ flux3_status flux3_transformer_forward(const flux3_dims* dims, const flux3_io_di
     if (!aligned16(q.p)) return fail(FLUX3_E_ALIGN, "%s is not 16-byte aligned", q.name);
   }
   if (!std::isfinite(t)) return fail(FLUX3_E_INVALID, "t is not finite");
-  if ((r = check_stack_weights(per_mode, n_pm, joint, n_joint, segs, n_segs)) != FLUX3_OK) return r;
+  if ((r = check_stack_weights(dims, per_mode, n_pm, joint, n_joint, segs, n_segs)) != FLUX3_OK)
+    return r;
   flux3::ModulationShape ms[2];
   flux3::ModulationWeightsDev wd[2];
   int32_t seg_mode[FLUX3_MAX_SEGMENTS];

@@ -12,6 +12,13 @@
 //   K4  out = [o | act] . [Wo | Wd]^T                            (K = D + F)
 //       epilogue: x += gate_s * out on the fp32 residual.
 //
+// A rowwise-FP8 variant of both (the rowwise-FP8 single file of the
+// release post, section on smaller GPUs and single files) reads e4m3 codes
+// of h / [o | act] (one scale per token row) and of the weights (one scale
+// per output row) through the same pipeline: a 128-byte LDS slice row then
+// holds 128 codes, consumed by two 32x32x64 fp8 MFMA steps, and the row
+// scales multiply each finished product tile.
+//
 // Both operands are K-contiguous ("NT"): C[m][n] = sum_k A[m][k] * B[n][k],
 // with B in torch Linear layout [out][in].  Tile 256 x 256 x 64, 4 waves in
 // a 2 x 2 arrangement, each wave 128 x 128 = 4 x 4 blocks of the 32x32x16
@@ -60,11 +67,15 @@ constexpr int OP_BYTES = BM * ROW_BYTES;               // one operand's slice: 3
 constexpr int DEEP_STAGES = 3, SHALLOW_STAGES = 2;
 constexpr int LDS_BYTES = (DEEP_STAGES + SHALLOW_STAGES) * OP_BYTES;
 constexpr int LOADS_PER_OP = 64 / ROWS_PER_KB;         // 1-KiB blocks per wave per operand slice
-constexpr int KSTEPS = BK / 16;
+// MFMA k-steps per slice: a slice row holds 128 bytes, 64 bf16 values (four
+// 16-deep bf16 steps) or 128 fp8 codes (two 64-deep fp8 steps).
+template <bool F8>
+constexpr int KSTEPS = F8 ? 2 : 4;
 static_assert(LDS_BYTES <= 160 * 1024, "LDS rings too large");
 static_assert(BK == 64 && SWZ_DIV == 2 && CPR == 8,
               "the packed operand layout holds 64-wide k blocks with this swizzle");
-static_assert(LOADS_PER_OP == 8 && KSTEPS == 4, "load schedule: 8 loads in each of k-steps 0 and 1");
+static_assert(LOADS_PER_OP == 8 && KSTEPS<false> == 4 && KSTEPS<true> == 2,
+              "load schedule: 8 loads per operand and slice");
 
 struct Acc {
   f32x16 c[4][4];
@@ -145,21 +156,40 @@ __device__ __forceinline__ int k_offset(int k) {
   return P ? k * 8 : k;
 }
 
+// One k-step's operand fragments of a wave: 4 A and 4 B blocks of 32 rows.
+template <bool F8>
 struct Frags {
   bf16x8 a[4], b[4];
 };
+template <>
+struct Frags<true> {
+  i32x8 a[4], b[4];
+};
 
-// One 16-byte fragment read (Q < 4: A block Q, else B block Q - 4) of k-step kk.
-template <int Q>
-__device__ __forceinline__ void read_frag(Frags& f, const lds_u8* As, const lds_u8* Bs, int wm,
-                                          int wn, int lane, int kk) {
+// The fragment reads of k-step kk for block Q (Q < 4: A block Q, else B
+// block Q - 4).  bf16: one 16-byte chunk per lane (lane half h takes chunk
+// 2 kk + h).  fp8: two chunks per lane, 32 consecutive codes (lane half h
+// takes chunks 4 kk + 2 h and 4 kk + 2 h + 1).
+template <int Q, bool F8>
+__device__ __forceinline__ void read_frag(Frags<F8>& f, const lds_u8* As, const lds_u8* Bs,
+                                          int wm, int wn, int lane, int kk) {
   const int r = lane & 31;
-  const int chunk = ((2 * kk + (lane >> 5)) ^ ((r / SWZ_DIV) % CPR)) << 4;
-  typedef const __attribute__((address_space(3))) bf16x8 lds_frag;
-  if constexpr (Q < 4)
-    f.a[Q] = *reinterpret_cast<lds_frag*>(As + (wm * 128 + Q * 32 + r) * ROW_BYTES + chunk);
-  else
-    f.b[Q - 4] = *reinterpret_cast<lds_frag*>(Bs + (wn * 128 + (Q - 4) * 32 + r) * ROW_BYTES + chunk);
+  const int swz = (r / SWZ_DIV) % CPR;
+  const lds_u8* row = Q < 4 ? As + (wm * 128 + Q * 32 + r) * ROW_BYTES
+                            : Bs + (wn * 128 + (Q - 4) * 32 + r) * ROW_BYTES;
+  if constexpr (!F8) {
+    typedef const __attribute__((address_space(3))) bf16x8 lds_frag;
+    const bf16x8 v = *reinterpret_cast<lds_frag*>(row + (((2 * kk + (lane >> 5)) ^ swz) << 4));
+    if constexpr (Q < 4) f.a[Q] = v; else f.b[Q - 4] = v;
+  } else {
+    typedef const __attribute__((address_space(3))) u32x4 lds_chunk;
+    const int c0 = 4 * kk + 2 * (lane >> 5);
+    const u32x4 lo = *reinterpret_cast<lds_chunk*>(row + ((c0 ^ swz) << 4));
+    const u32x4 hi = *reinterpret_cast<lds_chunk*>(row + (((c0 + 1) ^ swz) << 4));
+    const i32x8 v = {(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                     (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+    if constexpr (Q < 4) f.a[Q] = v; else f.b[Q - 4] = v;
+  }
 }
 
 // Per-workgroup stream state.
@@ -236,32 +266,44 @@ struct Stream {
   }
 };
 
-// MFMA number IDX (block i = IDX/4, j = IDX%4) of a k-step, followed by at
-// most one memory instruction, then a scheduling barrier so that the exact
-// order (one memory op issued in the shadow of each MFMA) is kept.  MFMAs
-// 8..15 of k-step 0 carry the shallow operand's 8 loads of the pending
-// slice, those of k-step 1 the deep operand's.
-template <int KK, int IDX, class ST>
-__device__ __forceinline__ void kstep_op(const ST& st, const Frags& cur, Frags& nxt, Acc& acc,
-                                         const lds_u8* As, const lds_u8* Bs, int kk_next) {
+// MFMA number IDX (block i = IDX/4, j = IDX%4) of a k-step, followed by its
+// share of the memory instructions, then a scheduling barrier so that the
+// exact order is kept.  bf16 (four k-steps): MFMAs 0..7 of an early k-step
+// read the next k-step's fragments, MFMAs 8..15 of k-step 0 carry the
+// shallow operand's 8 loads of the pending slice, those of k-step 1 the deep
+// operand's.  fp8 (two k-steps, each MFMA twice as long): k-step 0 carries
+// all of them -- fragment reads and shallow loads in MFMAs 0..7, deep loads
+// in 8..15.
+template <int KK, int IDX, bool F8, class ST>
+__device__ __forceinline__ void kstep_op(const ST& st, const Frags<F8>& cur, Frags<F8>& nxt,
+                                         Acc& acc, const lds_u8* As, const lds_u8* Bs,
+                                         int kk_next) {
   constexpr int i = IDX / 4, j = IDX % 4;
-  acc.c[i][j] = mfma32(cur.a[i], cur.b[j], acc.c[i][j]);
-  constexpr bool last = KK == KSTEPS - 1;
+  if constexpr (F8)
+    acc.c[i][j] = mfma32_f8(cur.a[i], cur.b[j], acc.c[i][j]);
+  else
+    acc.c[i][j] = mfma32(cur.a[i], cur.b[j], acc.c[i][j]);
+  constexpr bool last = KK == KSTEPS<F8> - 1;
   if constexpr (!last) {
     if constexpr (IDX < 8) read_frag<IDX>(nxt, As, Bs, st.wm, st.wn, st.lane, kk_next);
-    if constexpr (IDX >= 8 && KK == 0) st.template load_shallow<IDX - 8>();
-    if constexpr (IDX >= 8 && KK == 1) st.template load_deep<IDX - 8>();
+    if constexpr (F8) {
+      if constexpr (IDX < 8) st.template load_shallow<IDX>();
+      else st.template load_deep<IDX - 8>();
+    } else {
+      if constexpr (IDX >= 8 && KK == 0) st.template load_shallow<IDX - 8>();
+      if constexpr (IDX >= 8 && KK == 1) st.template load_deep<IDX - 8>();
+    }
   } else {
     if constexpr (IDX >= 8) read_frag<IDX - 8>(nxt, As, Bs, st.wm, st.wn, st.lane, 0);
   }
   __builtin_amdgcn_sched_barrier(0);
 }
 
-template <int KK, class ST, int... IDX>
-__device__ __forceinline__ void kstep_ops(const ST& st, const Frags& cur, Frags& nxt,
+template <int KK, bool F8, class ST, int... IDX>
+__device__ __forceinline__ void kstep_ops(const ST& st, const Frags<F8>& cur, Frags<F8>& nxt,
                                           Acc& acc, const lds_u8* As, const lds_u8* Bs,
                                           int kk_next, std::integer_sequence<int, IDX...>) {
-  (kstep_op<KK, IDX>(st, cur, nxt, acc, As, Bs, kk_next), ...);
+  (kstep_op<KK, IDX, F8>(st, cur, nxt, acc, As, Bs, kk_next), ...);
 }
 
 // k-step KK of slice kt.  Early k-steps read the next k-step's fragments
@@ -272,36 +314,38 @@ __device__ __forceinline__ void kstep_ops(const ST& st, const Frags& cur, Frags&
 // for this wave) and meets the other waves at the workgroup barrier --
 // after which slice kt's buffers are free and slice kt + 1 is complete --
 // then reads slice kt + 1's first fragments during its last 8 MFMAs.
-template <int KK, class ST>
-__device__ __forceinline__ void mma_kstep(ST& st, Frags& cur, Frags& nxt, Acc& acc, int kt) {
-  if constexpr (KK + 1 < KSTEPS) {
-    kstep_ops<KK>(st, cur, nxt, acc, st.a_buf(kt), st.b_buf(kt), KK + 1,
-                  std::make_integer_sequence<int, 16>{});
-    mma_kstep<KK + 1>(st, nxt, cur, acc, kt);
+template <int KK, bool F8, class ST>
+__device__ __forceinline__ void mma_kstep(ST& st, Frags<F8>& cur, Frags<F8>& nxt, Acc& acc,
+                                          int kt) {
+  if constexpr (KK + 1 < KSTEPS<F8>) {
+    kstep_ops<KK, F8>(st, cur, nxt, acc, st.a_buf(kt), st.b_buf(kt), KK + 1,
+                      std::make_integer_sequence<int, 16>{});
+    mma_kstep<KK + 1, F8>(st, nxt, cur, acc, kt);
   } else {
-    kstep_ops<KK>(st, cur, nxt, acc, st.a_buf(kt), st.b_buf(kt), 0,
-                  std::integer_sequence<int, 0, 1, 2, 3, 4, 5, 6, 7>{});
+    kstep_ops<KK, F8>(st, cur, nxt, acc, st.a_buf(kt), st.b_buf(kt), 0,
+                      std::integer_sequence<int, 0, 1, 2, 3, 4, 5, 6, 7>{});
     wait_vm<LOADS_PER_OP>();
     __syncthreads();
     // slice kt's buffers are free from here on
     st.set_load_shallow(kt + SHALLOW_STAGES);
     st.set_load_deep(kt + DEEP_STAGES);
-    kstep_ops<KK>(st, cur, nxt, acc, st.a_buf(kt + 1), st.b_buf(kt + 1), 0,
-                  std::integer_sequence<int, 8, 9, 10, 11, 12, 13, 14, 15>{});
+    kstep_ops<KK, F8>(st, cur, nxt, acc, st.a_buf(kt + 1), st.b_buf(kt + 1), 0,
+                      std::integer_sequence<int, 8, 9, 10, 11, 12, 13, 14, 15>{});
   }
 }
 
 // Main loop over the k slices [k_begin, k_end) of one tile; PA / PB say
 // whether A / B are in the packed operand layout, DEEP_B whether B (else A)
-// is the weight operand with the deeper ring.  Slices below nk0 take their
-// B rows from B0, the others (from slice nk0 on) from B1; A runs straight
-// through.  The caller separates two calls on the same LDS with a workgroup
-// barrier.
-template <bool PA, bool PB, bool DEEP_B>
+// is the weight operand with the deeper ring, F8 whether both hold e4m3
+// codes (packed fp8 layout; Src pointers and strides then count code pairs,
+// so a slice is 128 codes deep).  Slices below nk0 take their B rows from
+// B0, the others (from slice nk0 on) from B1; A runs straight through.  The
+// caller separates two calls on the same LDS with a workgroup barrier.
+template <bool PA, bool PB, bool DEEP_B, bool F8 = false>
 __device__ __forceinline__ void gemm_mainloop(lds_u8* smem, Acc& acc, const Src& A,
                                               const Src& B0, int nk0, const Src& B1,
                                               int k_begin, int k_end) {
-  static_assert(KSTEPS % 2 == 0, "slices start in the first fragment set");
+  static_assert(KSTEPS<F8> % 2 == 0, "slices start in the first fragment set");
   Stream<PA, PB, DEEP_B> st;
   st.smem = smem;
   st.lds0 = (uint32_t)(uintptr_t)smem;
@@ -335,7 +379,7 @@ __device__ __forceinline__ void gemm_mainloop(lds_u8* smem, Acc& acc, const Src&
   st.set_load_deep(2);
   wait_vm<LOADS_PER_OP>();
   __syncthreads();
-  Frags f0, f1;
+  Frags<F8> f0, f1;
   const lds_u8* a0 = st.a_buf(0);
   const lds_u8* b0 = st.b_buf(0);
   read_frag<0>(f0, a0, b0, st.wm, st.wn, st.lane, 0);
@@ -346,15 +390,17 @@ __device__ __forceinline__ void gemm_mainloop(lds_u8* smem, Acc& acc, const Src&
   read_frag<5>(f0, a0, b0, st.wm, st.wn, st.lane, 0);
   read_frag<6>(f0, a0, b0, st.wm, st.wn, st.lane, 0);
   read_frag<7>(f0, a0, b0, st.wm, st.wn, st.lane, 0);
-  for (int kt = 0; kt < st.nk; ++kt) mma_kstep<0>(st, f0, f1, acc, kt);
+  for (int kt = 0; kt < st.nk; ++kt) mma_kstep<0, F8>(st, f0, f1, acc, kt);
   // the re-fetches issued by the last iterations must land before the
   // workgroup can release its LDS
   wait_vm<0>();
 }
 
 struct ProjArgs {
-  const bf16* h;
+  const bf16* h;       // packed bf16 h, or packed e4m3 codes of h (F8)
   const bf16 *wq, *wk, *wv, *wg, *wu;
+  const float* sh;     // F8: dequantisation scale of each h row [n_pad]
+  const float* sw;     // F8: scale of each weight row [3D + 2F], q k v gate up
   const float *qn, *kn;
   const float2* rope;
   bf16 *q, *k, *vt, *cat;
@@ -371,10 +417,38 @@ __device__ __forceinline__ int vt_pos(int m) {
   return (m & ~15) | (gp << 2) | (m & 3);
 }
 
+// acc *= a_scale * b_scale for rowwise-fp8 operands: A row
+// wm 128 + 32 i + 8 (e / 4) + 4 (l / 32) + e % 4 takes a_run[i][8 (e / 4) +
+// 4 (l / 32) + e % 4] (a_run[i]: the scales of the wave's 32-row run i), B
+// row wn 128 + 32 j + l % 32 takes b_scale[32 j + l % 32].
+__device__ __forceinline__ void scale_acc(Acc& acc, const float* const (&a_run)[4],
+                                          const float* b_scale, int lane) {
+  const int hi = lane >> 5, r32 = lane & 31;
+  float cs[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) cs[j] = b_scale[32 * j + r32];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const float4 rs = *reinterpret_cast<const float4*>(a_run[i] + 8 * g + 4 * hi);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        acc.c[i][j][4 * g + 0] *= rs.x * cs[j];
+        acc.c[i][j][4 * g + 1] *= rs.y * cs[j];
+        acc.c[i][j][4 * g + 2] *= rs.z * cs[j];
+        acc.c[i][j][4 * g + 3] *= rs.w * cs[j];
+      }
+    }
+}
+
 // PW: the weights come in the packed operand layout (flux3_weights_pack),
-// else in Linear layout.
-template <bool PW>
+// else in Linear layout.  F8: h and the weights are rowwise e4m3 codes in
+// the packed fp8 layout (flux3_weights_quantize_fp8r), the products are
+// scaled back by the row scales before the epilogue.
+template <bool PW, bool F8>
 __global__ __launch_bounds__(NTHREADS, 1) void k_gemm_proj(ProjArgs p) {
+  static_assert(PW || !F8, "fp8 weights are always packed");
   __shared__ __attribute__((aligned(1024))) unsigned char smem_raw[LDS_BYTES];
   lds_u8* smem = (lds_u8*)smem_raw;
   const int t = threadIdx.x;
@@ -396,25 +470,26 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_gemm_proj(ProjArgs p) {
     hid0 = (nt - 3 * qkv_tiles) * 128;
   }
   const int D = p.D;
-  // first row of 32-row run i of the weight tile (256 output features)
-  auto w_run = [&](int i) -> const bf16* {
-    if (kind < 3) {
-      const bf16* W = kind == 0 ? p.wq : (kind == 1 ? p.wk : p.wv);
-      return W + (size_t)(head0 * 128 + 32 * i) * D;
-    }
+  const int Dk = F8 ? D / 2 : D;   // row length in 2-byte units
+  // first weight row of 32-row run i of the tile (256 output features)
+  auto w_row = [&](int i) -> int {
+    if (kind < 3) return head0 * 128 + 32 * i;
     // SwiGLU tiles: each 128-row half holds 64 gate rows then the 64 up rows
     // of the same hidden units, so gate and up land in one lane's registers
-    const int half = i >> 2, blk = i & 3;
-    const bf16* W = blk < 2 ? p.wg : p.wu;
-    return W + (size_t)(hid0 + 64 * half + 32 * (blk & 1)) * D;
+    return hid0 + 64 * (i >> 2) + 32 * (i & 1);
   };
+  auto w_mat = [&](int i) -> const bf16* {
+    if (kind < 3) return kind == 0 ? p.wq : (kind == 1 ? p.wk : p.wv);
+    return (i & 3) < 2 ? p.wg : p.wu;
+  };
+  auto w_run = [&](int i) -> const bf16* { return w_mat(i) + (size_t)w_row(i) * Dk; };
   Src H, W;   // h is packed, the weights row-major
-  H.lo = p.h + (size_t)(m0 + 64 * wave) * D;
+  H.lo = p.h + (size_t)(m0 + 64 * wave) * Dk;
   H.hi = H.lo;
-  H.ld = 8 * D;
+  H.ld = 8 * Dk;
   W.lo = w_run(2 * wave);
   W.hi = w_run(2 * wave + 1);   // = lo + 32 D: a wave's 64 rows are consecutive rows of one matrix
-  W.ld = PW ? 8 * D : D;
+  W.ld = PW ? 8 * Dk : Dk;
   // Values use C = h . Wv^T (a lane then holds 4 consecutive tokens of one
   // dim, the order of the transposed store).  Queries, keys and SwiGLU use
   // C^T = W . h^T: a lane holds one token and 4 consecutive features per
@@ -422,9 +497,25 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_gemm_proj(ProjArgs p) {
   // exchange with lane ^ 32, and stores are 8 bytes wide.
   Acc acc;
   if (kind == 2)
-    gemm_mainloop<true, PW, true>(smem, acc, H, W, D / BK, W, 0, D / BK);
+    gemm_mainloop<true, PW, true, F8>(smem, acc, H, W, Dk / BK, W, 0, Dk / BK);
   else
-    gemm_mainloop<PW, true, false>(smem, acc, W, H, D / BK, H, 0, D / BK);
+    gemm_mainloop<PW, true, false, F8>(smem, acc, W, H, Dk / BK, H, 0, Dk / BK);
+  if constexpr (F8) {
+    // scale of weight row r of matrix kind (q k v gate up) in p.sw
+    auto w_scale = [&](int i) -> const float* {
+      const int base = kind < 3 ? kind * D : 3 * D + ((i & 3) < 2 ? 0 : p.F);
+      return p.sw + base + w_row(i);
+    };
+    if (kind == 2) {
+      const float* const a_run[4] = {p.sh + m0 + wm * 128, p.sh + m0 + wm * 128 + 32,
+                                     p.sh + m0 + wm * 128 + 64, p.sh + m0 + wm * 128 + 96};
+      scale_acc(acc, a_run, w_scale(4 * wn), lane);
+    } else {
+      const float* const a_run[4] = {w_scale(4 * wm), w_scale(4 * wm + 1), w_scale(4 * wm + 2),
+                                     w_scale(4 * wm + 3)};
+      scale_acc(acc, a_run, p.sh + m0 + wn * 128, lane);
+    }
+  }
 
   const int r32 = lane & 31, hi = lane >> 5;
   // LDS is free once every wave is past the main loop.  Values and SwiGLU
@@ -590,13 +681,16 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_gemm_proj(ProjArgs p) {
 }
 
 struct OutArgs {
-  const bf16* cat;
+  const bf16* cat;     // packed bf16 [o | act], or its packed e4m3 codes (F8)
   const bf16 *wo, *wd;
+  const float* scat;   // F8: scale of each cat row [n_pad]
+  const float* sw;     // F8: scale of each row of [wo | wd] [D]
   float* x;
   const float* mod;
   float* part;       // split-tile partial sums: 2 slots of BM x BN fp32 per workgroup
   SegTable segs;
   int M, n_pad, D, F;
+  int nk, nk0;       // k slices of a tile, of them from wo
   int groups;        // persistent workgroups G
   int dp_rounds;     // whole-tile rounds before the split tail
   int tail;          // tiles left to the stream-K split (0: none)
@@ -685,10 +779,11 @@ __device__ __forceinline__ float4* slot_base(const OutArgs& p, int slot) {
   return reinterpret_cast<float4*>(p.part + (size_t)slot * BM * BN);
 }
 
-template <bool PW>
+template <bool PW, bool F8>
 __device__ __forceinline__ void out_tile_ptrs(const OutArgs& p, int m0, int n0, int wave, Src& A,
                                               Src& B0, Src& B1) {
-  const int D = p.D, F = p.F, ldc = D + F;
+  // row lengths in 2-byte units
+  const int D = F8 ? p.D / 2 : p.D, F = F8 ? p.F / 2 : p.F, ldc = D + F;
   A.lo = p.cat + (size_t)(m0 + 64 * wave) * ldc;   // packed
   A.hi = A.lo;
   A.ld = 8 * ldc;
@@ -700,8 +795,12 @@ __device__ __forceinline__ void out_tile_ptrs(const OutArgs& p, int m0, int n0, 
   B1.ld = PW ? 8 * F : F;
 }
 
-template <bool PW>
+// F8: cat and the weights are rowwise e4m3 codes in the packed fp8 layout;
+// every product tile is scaled back by the row scales as soon as its main
+// loop ends, so whole tiles, partial tiles and the fixup see plain sums.
+template <bool PW, bool F8>
 __global__ __launch_bounds__(NTHREADS, 1) void k_gemm_out(OutArgs p) {
+  static_assert(PW || !F8, "fp8 weights are always packed");
   __shared__ __attribute__((aligned(1024))) unsigned char smem_raw[LDS_BYTES];
   lds_u8* smem = (lds_u8*)smem_raw;
   const int t = threadIdx.x;
@@ -710,7 +809,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_gemm_out(OutArgs p) {
   const int n_n = p.D / BN;
   const int n_m = p.n_pad / BM;
   const int n_tiles = n_m * n_n;
-  const int nk = (p.D + p.F) / BK;
+  const int nk = p.nk;
   const int G = p.groups;
   // this workgroup's tail range (empty without a tail)
   SplitK sk;
@@ -746,11 +845,16 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_gemm_out(OutArgs p) {
       break;
     }
     Src A, B0, B1;
-    out_tile_ptrs<PW>(p, mt * BM, nt * BN, wave, A, B0, B1);
+    out_tile_ptrs<PW, F8>(p, mt * BM, nt * BN, wave, A, B0, B1);
     if (!first) __syncthreads();   // the previous item's LDS reads are done
     first = false;
     Acc acc;
-    gemm_mainloop<true, PW, true>(smem, acc, A, B0, p.D / BK, B1, kb, ke);
+    gemm_mainloop<true, PW, true, F8>(smem, acc, A, B0, p.nk0, B1, kb, ke);
+    if constexpr (F8) {
+      const float* a0 = p.scat + mt * BM + wm * 128;
+      const float* const a_run[4] = {a0, a0 + 32, a0 + 64, a0 + 96};
+      scale_acc(acc, a_run, p.sw + nt * BN + wn * 128, lane);
+    }
     if (kb == 0 && ke == nk) {
       out_epilogue(p, acc, mt * BM, nt * BN, wm, wn, lane);
     } else {
@@ -782,7 +886,7 @@ __global__ __launch_bounds__(NTHREADS) void k_gemm_out_fixup(OutArgs p) {
   const int n_n = p.D / BN;
   const int n_m = p.n_pad / BM;
   SplitK sk;
-  sk.nk = (p.D + p.F) / BK;
+  sk.nk = p.nk;
   sk.G = p.groups;
   sk.total = (int64_t)p.tail * sk.nk;
   const int i = blockIdx.x / FIX_SPLIT, chunk = blockIdx.x % FIX_SPLIT;
@@ -1012,7 +1116,9 @@ hipError_t launch_gemm_proj(const BlockShape& bs, const BlockWeightsDev& w,
                             const float* rope, const WsPtrs& ws, float eps,
                             hipStream_t s) {
   ProjArgs p;
-  p.h = static_cast<const bf16*>(ws.h);
+  p.h = static_cast<const bf16*>(w.fp8 ? ws.h8 : ws.h);
+  p.sh = ws.sh;
+  p.sw = w.s_proj;
   p.wq = static_cast<const bf16*>(w.wq);
   p.wk = static_cast<const bf16*>(w.wk);
   p.wv = static_cast<const bf16*>(w.wv);
@@ -1033,10 +1139,12 @@ hipError_t launch_gemm_proj(const BlockShape& bs, const BlockWeightsDev& w,
   p.eps = eps;
   const int n_n = 3 * (bs.H / 2) + bs.F / 128;
   const int n_m = bs.n_pad / BM;
-  if (w.packed)
-    hipLaunchKernelGGL(k_gemm_proj<true>, dim3(n_m * n_n), dim3(NTHREADS), 0, s, p);
+  if (w.fp8)
+    hipLaunchKernelGGL((k_gemm_proj<true, true>), dim3(n_m * n_n), dim3(NTHREADS), 0, s, p);
+  else if (w.packed)
+    hipLaunchKernelGGL((k_gemm_proj<true, false>), dim3(n_m * n_n), dim3(NTHREADS), 0, s, p);
   else
-    hipLaunchKernelGGL(k_gemm_proj<false>, dim3(n_m * n_n), dim3(NTHREADS), 0, s, p);
+    hipLaunchKernelGGL((k_gemm_proj<false, false>), dim3(n_m * n_n), dim3(NTHREADS), 0, s, p);
   return hipGetLastError();
 }
 
@@ -1056,9 +1164,15 @@ hipError_t launch_gemm_out(const BlockShape& bs, const BlockWeightsDev& w,
                            const WsPtrs& ws, float* x, const float* mod,
                            const SegTableHost& segs, hipStream_t s) {
   OutArgs p;
-  p.cat = static_cast<const bf16*>(ws.cat);
+  p.cat = static_cast<const bf16*>(w.fp8 ? ws.cat8 : ws.cat);
   p.wo = static_cast<const bf16*>(w.wo);
   p.wd = static_cast<const bf16*>(w.w_down);
+  p.scat = ws.scat;
+  p.sw = w.s_out;
+  // a slice is 64 bf16 values or 128 fp8 codes deep
+  const int slice = w.fp8 ? 2 * BK : BK;
+  p.nk = (bs.D + bs.F) / slice;
+  p.nk0 = bs.D / slice;
   p.x = x;
   p.mod = mod;
   p.part = static_cast<float*>(ws.part);
@@ -1080,10 +1194,12 @@ hipError_t launch_gemm_out(const BlockShape& bs, const BlockWeightsDev& w,
     p.dp_rounds += 1;
     p.tail = 0;
   }
-  if (w.packed)
-    hipLaunchKernelGGL(k_gemm_out<true>, dim3(G), dim3(NTHREADS), 0, s, p);
+  if (w.fp8)
+    hipLaunchKernelGGL((k_gemm_out<true, true>), dim3(G), dim3(NTHREADS), 0, s, p);
+  else if (w.packed)
+    hipLaunchKernelGGL((k_gemm_out<true, false>), dim3(G), dim3(NTHREADS), 0, s, p);
   else
-    hipLaunchKernelGGL(k_gemm_out<false>, dim3(G), dim3(NTHREADS), 0, s, p);
+    hipLaunchKernelGGL((k_gemm_out<false, false>), dim3(G), dim3(NTHREADS), 0, s, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.tail == 0 || G < 2) return e;
   hipLaunchKernelGGL(k_gemm_out_fixup, dim3((G - 1) * FIX_SPLIT), dim3(NTHREADS), 0, s, p);

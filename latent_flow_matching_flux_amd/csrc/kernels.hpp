@@ -32,6 +32,13 @@ struct WsPtrs {
   void* vt;   // bf16 [H][128][n_pad]
   void* cat;  // bf16 [n_pad][D + F]
   void* part; // fp32 [2 kMaxSplitGroups][256 * 256]: split-tile partials of K4
+  // rowwise-fp8 blocks only (packed e4m3 codes, fp32 row scales); they live in
+  // buffers that are dead at the time: h8 / sh from K1 to K2, cat8 / scat from
+  // the cat quantisation to K4 (over h, q, k, vt once attention is done)
+  void* h8;    // [n_pad][D]
+  float* sh;   // [n_pad]
+  void* cat8;  // [n_pad][D + F]
+  float* scat; // [n_pad]
 };
 
 // Upper bound on the persistent workgroups of the stream-K output GEMM (one
@@ -43,6 +50,9 @@ struct BlockWeightsDev {
   const void *wq, *wk, *wv, *wo, *w_gate, *w_up, *w_down;
   const float *q_norm, *k_norm;
   bool packed;   // matrices in the packed operand layout
+  bool fp8;      // rowwise e4m3 codes in the packed fp8 layout (packed too)
+  const float* s_proj;  // fp8: row scales of wq, wk, wv, w_gate, w_up [3D + 2F]
+  const float* s_out;   // fp8: row scales of [wo | w_down] [D]
 };
 
 // Linear-layout [R][K] bf16 (R % 8 == 0, K % 64 == 0) -> packed operand layout.
@@ -100,6 +110,24 @@ hipError_t launch_rope_tables(const RopeLayoutDev& lay, float* rope, int64_t n,
 hipError_t launch_ln_modulate(const BlockShape& bs, const float* x,
                               const float* mod, const SegTableHost& segs,
                               void* h, float eps, hipStream_t s);
+// K1 with rowwise-fp8 output: packed e4m3 codes of h [n_pad][D] and the scale
+// of each row (rows < M).
+hipError_t launch_ln_modulate_f8(const BlockShape& bs, const float* x, const float* mod,
+                                 const SegTableHost& segs, void* h8, float* sh, float eps,
+                                 hipStream_t s);
+// Rowwise e4m3 quantisation of the packed bf16 concatenation [o | act]
+// [n_pad][K] into packed fp8 codes and row scales, row blocks of 8 up to
+// rows M (K % 128 == 0, K <= kQuantMaxK).
+constexpr int kQuantMaxK = 16384;
+hipError_t launch_quant_packed_rows(const void* in, void* out, float* scale, int M, int K,
+                                    hipStream_t s);
+// Rowwise e4m3 quantisation of a Linear-layout bf16 matrix given as two
+// column pieces [R][Ka] and [R][Kb] (b may be null with Kb = 0): the codes of
+// piece a go to out_a (packed fp8 [R][Ka]), those of b to out_b ([R][Kb]),
+// one scale per row over both.  R % 8 == 0, Ka and Kb % 128 == 0,
+// Ka + Kb <= kQuantMaxK.
+hipError_t launch_quant_weight_rows(const void* a, int Ka, const void* b, int Kb, void* out_a,
+                                    void* out_b, float* scale, int R, hipStream_t s);
 hipError_t launch_gemm_proj(const BlockShape& bs, const BlockWeightsDev& w,
                             const float* rope, const WsPtrs& ws, float eps,
                             hipStream_t s);

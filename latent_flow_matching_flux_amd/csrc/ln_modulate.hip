@@ -88,6 +88,98 @@ __global__ __launch_bounds__(256) void k_ln_modulate_any(
     h[packed_index(row, c, D)] = f2bf((1.0f + scale[c]) * ((xr[c] - mean) * rstd) + shift[c]);
 }
 
+// Rowwise-fp8 output (blocks with e4m3 weights): the same h values in fp32,
+// then the row's largest magnitude a, the codes of h * (448 / a) in the
+// packed fp8 layout and the row scale a / 448.  One wave per row.  Any width
+// that is a multiple of 256; at 3072 the row stays in registers, otherwise
+// the values are recomputed from x for each pass.
+template <int V>
+__device__ __forceinline__ void ln_row_f8(const float* __restrict__ x, const float* __restrict__ mod,
+                                          const SegTable& segs, uint8_t* __restrict__ h8,
+                                          float* __restrict__ sh, int row, int D, int nv,
+                                          float eps) {
+  const int lane = threadIdx.x & 63;
+  const float4* xr = reinterpret_cast<const float4*>(x + (size_t)row * D);
+  float4 v[V > 0 ? V : 1];
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < (V > 0 ? V : nv); ++i) {
+    const float4 a = xr[lane + 64 * i];
+    if constexpr (V > 0) v[i] = a;
+    s += (a.x + a.y) + (a.z + a.w);
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) s += xor_lane(s, o);
+  const float mean = s * (1.0f / (float)D);
+  float q = 0.f;
+#pragma unroll
+  for (int i = 0; i < (V > 0 ? V : nv); ++i) {
+    const float4 a = V > 0 ? v[i] : xr[lane + 64 * i];
+    const float b0 = a.x - mean, b1 = a.y - mean, b2 = a.z - mean, b3 = a.w - mean;
+    q += (b0 * b0 + b1 * b1) + (b2 * b2 + b3 * b3);
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) q += xor_lane(q, o);
+  const float rstd = 1.0f / sqrtf(q * (1.0f / (float)D) + eps);
+  const int sg = seg_of(segs, row);
+  const float4* shift = reinterpret_cast<const float4*>(mod + (size_t)sg * 3 * D);
+  const float4* scale = shift + D / 4;
+  auto hval = [&](int i) -> float4 {
+    const int c = lane + 64 * i;
+    const float4 a = V > 0 ? v[i] : xr[c];
+    const float4 shv = shift[c], sc = scale[c];
+    return make_float4((1.0f + sc.x) * ((a.x - mean) * rstd) + shv.x,
+                       (1.0f + sc.y) * ((a.y - mean) * rstd) + shv.y,
+                       (1.0f + sc.z) * ((a.z - mean) * rstd) + shv.z,
+                       (1.0f + sc.w) * ((a.w - mean) * rstd) + shv.w);
+  };
+  float amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < (V > 0 ? V : nv); ++i) {
+    const float4 h = hval(i);
+    if constexpr (V > 0) v[i] = h;
+    amax = fmaxf(amax, fmaxf(fmaxf(fabsf(h.x), fabsf(h.y)), fmaxf(fabsf(h.z), fabsf(h.w))));
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) amax = fmaxf(amax, xor_lane(amax, o));
+  float mult, rscale;
+  e4m3_row_scale(amax, mult, rscale);
+#pragma unroll
+  for (int i = 0; i < (V > 0 ? V : nv); ++i) {
+    const float4 h = V > 0 ? v[i] : hval(i);
+    *reinterpret_cast<uint32_t*>(h8 + packed8_index(row, 4 * (lane + 64 * i), D)) =
+        e4m3x4(h.x, h.y, h.z, h.w, mult);
+  }
+  if (lane == 0) sh[row] = rscale;
+}
+
+template <int V>
+__global__ __launch_bounds__(256) void k_ln_modulate_f8(
+    const float* __restrict__ x, const float* __restrict__ mod, SegTable segs,
+    uint8_t* __restrict__ h8, float* __restrict__ sh, int M, int D, float eps) {
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= M) return;
+  ln_row_f8<V>(x, mod, segs, h8, sh, row, D, D / 256, eps);
+}
+
+hipError_t launch_ln_modulate_f8(const BlockShape& bs, const float* x, const float* mod,
+                                 const SegTableHost& segs, void* h8, float* sh, float eps,
+                                 hipStream_t s) {
+  SegTable st;
+  for (int i = 0; i < kMaxSegs; ++i) st.start[i] = segs.start[i];
+  st.n = segs.n;
+  const unsigned blocks = (unsigned)((bs.M + 3) / 4);
+  if (blocks == 0) return hipSuccess;
+  uint8_t* out = static_cast<uint8_t*>(h8);
+  if (bs.D == 3072)
+    hipLaunchKernelGGL(k_ln_modulate_f8<12>, dim3(blocks), dim3(256), 0, s, x, mod, st, out, sh,
+                       bs.M, bs.D, eps);
+  else
+    hipLaunchKernelGGL(k_ln_modulate_f8<0>, dim3(blocks), dim3(256), 0, s, x, mod, st, out, sh,
+                       bs.M, bs.D, eps);
+  return hipGetLastError();
+}
+
 hipError_t launch_ln_modulate(const BlockShape& bs, const float* x,
                               const float* mod, const SegTableHost& segs,
                               void* h, float eps, hipStream_t s) {

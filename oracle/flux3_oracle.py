@@ -285,7 +285,7 @@ def block_forward_rows(x, w, segs, mod, rope, rows, heads=None,
 
 
 def stack_forward(x, per_mode, joint, segs, mod_stage1, mod_stage2, rope,
-                  dtype=np.float64, per_block_mod=False):
+                  dtype=np.float64, per_block_mod=False, block_fn=None):
     """The two-stage stack [P1], [P4 "Inside the transformer"].
 
     Stage 1: every segment (stream) runs the per-mode blocks of its own mode
@@ -296,18 +296,20 @@ def stack_forward(x, per_mode, joint, segs, mod_stage1, mod_stage2, rope,
     per_mode[mode] is a list of block weight dicts (5 each); joint is a list
     (28).  mod_stage1 / mod_stage2: [n_segs][3][D] shared by every block of
     the stage, or, with per_block_mod, [n_blocks][n_segs][3][D].
+    block_fn: the block (block_forward by default; block_forward_fp8 for
+    weights in the form quantize_block_weights gives).
     """
+    block_fn = block_fn or block_forward
     out = np.array(x, dtype=dtype, copy=True)
     for s, (start, count, mode) in enumerate(segs):
         rows = slice(start, start + count)
         for b, wb in enumerate(per_mode[mode]):
             m1 = mod_stage1[b] if per_block_mod else mod_stage1
-            out[rows] = block_forward(out[rows], wb, [(0, count, mode)],
-                                      np.asarray(m1)[s:s + 1], rope[rows],
-                                      dtype=dtype)
+            out[rows] = block_fn(out[rows], wb, [(0, count, mode)],
+                                 np.asarray(m1)[s:s + 1], rope[rows], dtype=dtype)
     for b, wb in enumerate(joint):
         m2 = mod_stage2[b] if per_block_mod else mod_stage2
-        out = block_forward(out, wb, segs, m2, rope, dtype=dtype)
+        out = block_fn(out, wb, segs, m2, rope, dtype=dtype)
     return out
 
 

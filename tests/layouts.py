@@ -20,6 +20,29 @@ def unpack_rows(p, R, K):
     return out.reshape(R, K)
 
 
+def unpack8_rows(p, R, K):
+    """Row-major [R][K] uint8 codes of a packed fp8 matrix given as R*K
+    bytes: its bytes sit where a packed bf16 [R][K / 2] matrix's would."""
+    pairs = np.ascontiguousarray(np.asarray(p, np.uint8)).view(np.uint16)
+    return np.ascontiguousarray(unpack_rows(pairs, R, K // 2)).view(np.uint8).reshape(R, K)
+
+
+def pack8_rows_loops(x):
+    """Packed fp8 layout by explicit loops, from its definition: 1-KiB
+    blocks of 8 rows x 128 codes, block (r / 8, k / 128) at index
+    (r / 8)(K / 128) + k / 128, row r % 8 at byte 128 (r % 8) of it, 16-byte
+    chunk c in slot c ^ ((r / 2) % 8)."""
+    R, K = x.shape
+    out = np.zeros(R * K, dtype=np.uint8)
+    for r in range(R):
+        for k in range(K):
+            blk = (r // 8) * (K // 128) + k // 128
+            c = (k % 128) // 16
+            slot = c ^ ((r // 2) % 8)
+            out[blk * 1024 + (r % 8) * 128 + slot * 16 + k % 16] = x[r, k]
+    return out
+
+
 def pack_rows_loops(x):
     """Reference packer written with explicit loops (small matrices only)."""
     R, K = x.shape

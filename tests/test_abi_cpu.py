@@ -27,7 +27,7 @@ FAKE = 0x7F0000000000          # a 256-byte aligned address that is never derefe
 def header_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(flux3_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(flux3_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_library_exports_every_declared_function():
@@ -205,6 +205,20 @@ def test_packed_layout_reader():
         assert np.array_equal(unpack_rows(p, R, K), x)
 
 
+def test_packed_fp8_layout_reader():
+    """The fp8 code layout read back two ways: by its own definition and as
+    the bytes of the bf16 layout of code pairs."""
+    from layouts import unpack8_rows, pack8_rows_loops
+    rng = np.random.default_rng(1)
+    for R, K in ((8, 128), (16, 256), (24, 384)):
+        x = rng.integers(0, 256, (R, K)).astype(np.uint8)
+        p = pack8_rows_loops(x)
+        blk = p.reshape(-1, 1024)
+        assert blk.shape[0] == (R // 8) * (K // 128)
+        assert np.array_equal(np.sort(blk[0]), np.sort(x[:8, :128].ravel()))
+        assert np.array_equal(unpack8_rows(p, R, K), x)
+
+
 def test_modulation_workspace_and_validation():
     d = _dims()
     assert F.modulation_workspace_bytes(synth.DIMS) == (4 * 256 + 8 * 3072) * 4
@@ -266,6 +280,49 @@ def test_weights_pack_sizes_and_validation():
     bad.layout = 7
     assert _call_block(w=bad) == E_INVALID
     assert b"layout" in lib.flux3_last_error_detail()
+
+
+def test_weights_fp8r_sizes_and_validation():
+    lib = F.load()
+    d = _dims()
+    D, Fh = 3072, 9216
+    # one byte per code, scales fp32, each piece 256-byte aligned
+    assert F.weights_fp8r_bytes(synth.DIMS) == \
+        4 * D * D + 3 * D * Fh + 4 * (3 * D + 2 * Fh) + 4 * D == 122806272
+    assert lib.flux3_weights_fp8r_bytes(ctypes.byref(_dims(head_dim=64))) == 0
+    need = F.weights_fp8r_bytes(synth.DIMS)
+    out = L.BlockWeights()
+
+    def quant(w=None, buf=FAKE + (1 << 32), nbytes=need, o=out, dims=d):
+        return lib.flux3_weights_quantize_fp8r(ctypes.byref(dims), None if w is False else
+                                               ctypes.byref(w if w is not None else _w()), buf,
+                                               nbytes, None if o is None else ctypes.byref(o), 0)
+
+    assert quant(w=False) == E_INVALID
+    packed = _w()
+    packed.layout = L.WEIGHTS_PACKED
+    assert quant(w=packed) == E_INVALID
+    assert b"Linear" in lib.flux3_last_error_detail()
+    assert quant(o=None) == E_INVALID
+    assert quant(buf=None) == E_WORKSPACE
+    assert quant(buf=FAKE + 16) == E_ALIGN
+    assert quant(nbytes=need - 1) == E_WORKSPACE
+    assert quant(dims=_dims(width=3000)) == E_UNSUPPORTED
+    # the per-token quantiser's row limit and the workspace room for [o | act]
+    assert quant(dims=_dims(hidden=13568)) == E_UNSUPPORTED
+    assert b"16384" in lib.flux3_last_error_detail()
+    assert quant(dims=_dims(width=256, heads=2, hidden=7 * 256)) == E_UNSUPPORTED
+    # a block call with fp8r weights needs both scale arrays, aligned
+    w8 = _w()
+    w8.layout = L.WEIGHTS_FP8R
+    assert _call_block(w=w8) == E_INVALID
+    assert b"s_proj" in lib.flux3_last_error_detail()
+    w8.s_proj = FAKE + (1 << 33)
+    w8.s_out = FAKE + (1 << 33) + 8
+    assert _call_block(w=w8) == E_ALIGN
+    w8.s_out = FAKE + (1 << 33) + 65536
+    small = _dims(width=256, heads=2, hidden=7 * 256)
+    assert _call_block(dims=small, w=w8) == E_UNSUPPORTED
 
 
 def test_transformer_workspace_and_validation():

@@ -1,0 +1,247 @@
+"""Rowwise-FP8 blocks (weights of flux3_weights_quantize_fp8r) against the
+oracle's FP8 block.
+
+The weight quantisation and the per-token quantisation of [o | act] take
+every decision in fp32 on bf16 inputs, as the oracle does, so their codes
+and scales are compared bit for bit.  Block and stack outputs are held to
+the bf16 bar (max-abs 3e-2, cosine 0.9995) against block_forward_fp8: the
+oracle quantises its fp64 h and [o | act], the kernels their fp32 h and
+bf16 [o | act], so a code can differ by one step where a value lies next to
+a rounding boundary, and the fp8 matrix cores sum with a narrower adder
+than fp32 (a few 2^-12 of the largest product of a group)."""
+import numpy as np
+import pytest
+import torch
+
+import latent_flow_matching_flux_amd as F
+import synth
+from oracle import flux3_oracle as O
+
+pytestmark = pytest.mark.gpu
+
+from layouts import unpack8_rows, unpack_rows  # noqa: E402
+from gpu_util import (DEV, assert_close, assert_close_stack, rope_dev, seg_tuples,  # noqa: E402
+                      upload_weights, workspace)
+
+SMALL = synth.Dims(width=256, heads=2, head_dim=128, mlp_hidden=384)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    assert torch.cuda.is_available(), "GPU tests need a HIP device"
+    F.load()
+    yield
+    torch.cuda.synchronize()
+
+
+def fp8_weights(dims, w_np):
+    """Device rowwise-FP8 weights of one block: (BlockWeights, buffer)."""
+    w_dev = upload_weights(w_np)
+    buf = torch.empty(F.weights_fp8r_bytes(dims), dtype=torch.uint8, device=DEV)
+    w8 = F.weights_quantize_fp8r(dims, w_dev, buf)
+    w8._keep = (buf, w_dev)
+    return w8, buf
+
+
+_OCACHE = {}
+
+
+def oracle_fp8(w_np):
+    if id(w_np) not in _OCACHE:
+        _OCACHE[id(w_np)] = (w_np, O.quantize_block_weights(w_np))
+    return _OCACHE[id(w_np)][1]
+
+
+def _f32_bits(a):
+    return np.ascontiguousarray(a, np.float32).view(np.uint32)
+
+
+def _planted(dims, seed):
+    """Block weights with rows that exercise the quantiser's edges: an
+    all-zero row, a row of one large value over tiny ones of both signs
+    (they round to signed zeros), a row whose maximum is negative, and
+    exact ties of the e4m3 grid after scaling."""
+    w = {k: np.array(v, copy=True) for k, v in synth.block_weights(seed, 1, dims).items()}
+    D = dims.width
+
+    def bits(a):
+        return synth.bf16_round_bits(np.asarray(a, np.float32))
+
+    w["wq"][0] = 0
+    row = np.full(D, 1e-6, np.float32)
+    row[1::2] = -1e-6
+    row[7] = 3.0
+    w["wq"][1] = bits(row)
+    w["wk"][2] = bits(-np.abs(synth.bf16_bits_to_f32(w["wk"][2])) - 0.01)
+    # 448 times a tie point between e4m3 values 1.0 and 1.125: with the row
+    # maximum 448, the multiplier is exactly 1
+    tie = np.linspace(-1, 1, D).astype(np.float32)
+    tie[0] = 448.0
+    tie[5] = 1.0625
+    tie[6] = -1.0625
+    tie[9] = 1.1875
+    w["w_up"][3] = bits(tie)
+    w["w_down"][4] = 0
+    w["wo"][4] = 0
+    return w
+
+
+@pytest.mark.parametrize("dims,planted", [(SMALL, True), (synth.DIMS, False)],
+                         ids=["small_planted", "model"])
+def test_weight_codes_and_scales_bit_exact(dims, planted):
+    w_np = _planted(dims, 11) if planted else synth.block_weights(0, 2, dims)
+    w8, buf = fp8_weights(dims, w_np)
+    torch.cuda.synchronize()
+    assert w8.layout == F.WEIGHTS_FP8R
+    host = buf.cpu().numpy()
+    base = buf.data_ptr()
+    D, Fh = dims.width, dims.mlp_hidden
+
+    def codes(name, R, K):
+        off = getattr(w8, name) - base
+        assert off % 256 == 0 and off + R * K <= host.size
+        return unpack8_rows(host[off:off + R * K], R, K)
+
+    def floats(ptr, n):
+        off = ptr - base
+        return host[off:off + 4 * n].view(np.float32)
+
+    s_proj = floats(w8.s_proj, 3 * D + 2 * Fh)
+    row0 = 0
+    for name, R in (("wq", D), ("wk", D), ("wv", D), ("w_gate", Fh), ("w_up", Fh)):
+        want_c, want_s = O.quantize_rowwise(O.as_float(w_np[name]))
+        got_c = codes(name, R, D)
+        bad = np.argwhere(got_c != want_c)
+        assert bad.size == 0, f"{name}: {len(bad)} codes differ, first {bad[:4].tolist()}"
+        np.testing.assert_array_equal(_f32_bits(s_proj[row0:row0 + R]), _f32_bits(want_s))
+        row0 += R
+    w2 = np.hstack([O.as_float(w_np["wo"]), O.as_float(w_np["w_down"])])
+    want_c, want_s = O.quantize_rowwise(w2)
+    np.testing.assert_array_equal(codes("wo", D, D), want_c[:, :D])
+    np.testing.assert_array_equal(codes("w_down", D, Fh), want_c[:, D:])
+    np.testing.assert_array_equal(_f32_bits(floats(w8.s_out, D)), _f32_bits(want_s))
+    if planted:
+        assert s_proj[0] == 0 and np.all(codes("wq", D, D)[0] == 0)
+        assert np.any(codes("wq", D, D)[1] == 0x80)        # negative tiny -> -0
+        assert floats(w8.s_out, D)[4] == 0
+
+
+def _case(layout, seed, dims=synth.DIMS):
+    n = layout.n_tokens
+    segs = layout.segments()
+    w = synth.block_weights(seed, 0, dims)
+    x = synth.tokens(seed, n, dims.width)
+    mod = synth.modulation(seed, 0, len(segs), dims.width)
+    return segs, w, x, mod
+
+
+def oracle_rope(layout):
+    return O.rope_tables(O.token_positions(layout.n_text, layout.grid_h, layout.grid_w,
+                                           layout.refs, layout.hw_scale), layout.theta)
+
+
+def run_fp8_block(dims, w_np, x_np, segs, mod_np, layout):
+    n = x_np.shape[0]
+    w8, _ = fp8_weights(dims, w_np)
+    x = torch.from_numpy(x_np).to(DEV)
+    mod = torch.from_numpy(np.ascontiguousarray(mod_np, np.float32)).to(DEV)
+    ws = workspace(dims, n)
+    F.block_forward(dims, w8, x, segs, mod, rope_dev(layout), ws)
+    torch.cuda.synchronize()
+    return x.cpu().numpy(), ws
+
+
+def test_block336_output_and_cat_quantisation():
+    """The 336-token block: output against the oracle, and the per-token
+    codes and scales of [o | act] bit for bit against the oracle's
+    quantisation of the kernels' own bf16 [o | act]."""
+    dims = synth.DIMS
+    layout = synth.workload("block336").layout
+    segs, w, x, mod = _case(layout, 0)
+    got, ws = run_fp8_block(dims, w, x, segs, mod, layout)
+    want = O.block_forward_fp8(x, oracle_fp8(w), seg_tuples(segs), mod, oracle_rope(layout))
+    assert_close(got, want, "x_out fp8 block336")
+    assert_close(got - x, want - x, "delta fp8 block336")
+
+    n = layout.n_tokens
+    L = F.workspace_layout(dims, n)
+    n_pad, K = L.n_pad, dims.width + dims.mlp_hidden
+    host = ws.cpu().numpy()
+    cat = unpack_rows(host[L.cat:L.cat + n_pad * K * 2].view(np.uint16), n_pad, K)[:n]
+    want_c, want_s = O.quantize_rowwise(O.as_float(cat))
+    got_c = unpack8_rows(host[L.h:L.h + n_pad * K], n_pad, K)[:n]
+    bad = np.argwhere(got_c != want_c)
+    assert bad.size == 0, f"{len(bad)} codes of [o | act] differ, first {bad[:4].tolist()}"
+    s_off = L.h + (n_pad * K + 255) // 256 * 256
+    got_s = host[s_off:s_off + 4 * n].view(np.float32)
+    np.testing.assert_array_equal(_f32_bits(got_s), _f32_bits(want_s))
+
+
+@pytest.mark.parametrize("n_text,grid", [(1, (0, 0)), (80, (5, 7)), (240, (16, 16))])
+def test_block_ragged_sizes(n_text, grid):
+    dims = synth.DIMS
+    layout = synth.RopeLayout(n_text, grid[0], grid[1])
+    segs, w, x, mod = _case(layout, 3)
+    got, _ = run_fp8_block(dims, w, x, segs, mod, layout)
+    want = O.block_forward_fp8(x, oracle_fp8(w), seg_tuples(segs), mod, oracle_rope(layout))
+    assert_close(got, want, f"x_out fp8 n={layout.n_tokens}")
+    assert_close(got - x, want - x, "delta fp8")
+
+
+def test_block_small_dims_three_segments():
+    dims = SMALL
+    layout = synth.RopeLayout(40, 6, 7, ((5, 6),))
+    segs, w, x, mod = _case(layout, 5, dims)
+    got, _ = run_fp8_block(dims, w, x, segs, mod, layout)
+    want = O.block_forward_fp8(x, oracle_fp8(w), seg_tuples(segs), mod, oracle_rope(layout))
+    assert_close(got, want, "x_out fp8 small dims")
+    assert_close(got - x, want - x, "delta fp8 small dims")
+
+
+def test_block_edit8432_sampled_rows():
+    """The 8432-token edit block (the bench's workload), on sampled rows."""
+    dims = synth.DIMS
+    layout = synth.workload("edit8432").layout
+    segs, w, x, mod = _case(layout, 0)
+    got, _ = run_fp8_block(dims, w, x, segs, mod, layout)
+    rng = np.random.default_rng(0)
+    rows = np.unique(np.concatenate([[0, 239, 240, 4335, 4336, 8431],
+                                     rng.choice(8432, 58, replace=False)]))
+    want = O.block_forward_fp8(x, oracle_fp8(w), seg_tuples(segs), mod, oracle_rope(layout),
+                               rows=rows, dtype=np.float32)
+    assert_close(got[rows], want, "x_out fp8 rows")
+    assert_close(got[rows] - x[rows], want - x[rows], "delta fp8 rows")
+
+
+def test_stack_small_dims_full_depth():
+    """5 per-mode + 28 joint rowwise-FP8 blocks over [text | image | ref]."""
+    dims = SMALL
+    layout = synth.RopeLayout(48, 8, 10, ((8, 10),))
+    segs = layout.segments()
+    n = layout.n_tokens
+    pm_np = {m: [synth.block_weights(31 + m, b % 2, dims) for b in range(5)] for m in range(3)}
+    jt_np = [synth.block_weights(37, b % 3, dims) for b in range(28)]
+    x_np = synth.tokens(31, n, dims.width)
+    m1 = synth.modulation(31, 1, len(segs), dims.width)
+    m2 = synth.modulation(31, 2, len(segs), dims.width)
+    keep = []
+
+    def dev(w):
+        w8, buf = fp8_weights(dims, w)
+        keep.append((w8, buf))
+        return w8
+
+    pm = {m: [dev(w) for w in ws] for m, ws in pm_np.items()}
+    jt = [dev(w) for w in jt_np]
+    x = torch.from_numpy(x_np).to(DEV)
+    F.stack_forward(dims, pm, jt, x, segs,
+                    torch.from_numpy(np.ascontiguousarray(m1, np.float32)).to(DEV),
+                    torch.from_numpy(np.ascontiguousarray(m2, np.float32)).to(DEV),
+                    rope_dev(layout), workspace(dims, n))
+    torch.cuda.synchronize()
+    got = x.cpu().numpy()
+    pm_o = {m: [oracle_fp8(w) for w in ws] for m, ws in pm_np.items()}
+    jt_o = [oracle_fp8(w) for w in jt_np]
+    want = O.stack_forward(x_np, pm_o, jt_o, seg_tuples(segs), m1, m2, oracle_rope(layout),
+                           block_fn=O.block_forward_fp8)
+    assert_close_stack(got, want, x_np, "fp8 stack")
