@@ -31,6 +31,12 @@ flux3_transformer_forward (input linears from 20,480-value text vectors and
 output layer) and one 16-step distilled flux3_sample over the same blocks.  Peak: the 2516.6 TFLOP/s of
 AMD's MI355X spec, next to CUs x clock x 4096 from the device query.
 
+"fp8r" repeats the joint block and the step loop with the blocks' weights in
+the rowwise-FP8 form (flux3_weights_quantize_fp8r: e4m3 codes, one scale per
+output row; the GEMM inputs quantised per token inside each block), its GEMM
+rates against the 5033 TFLOP/s dense fp8 MFMA peak.  The headline value
+stays the bf16 stack.
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
 """
 import argparse
@@ -44,6 +50,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2516.6      # 256 CU x 2.4 GHz x 4096 dense bf16 FLOP/clk/CU
+PEAK_FP8_TFLOPS = 5033.2       # 256 CU x 2.4 GHz x 8192 dense fp8 FLOP/clk/CU
 PEAK_HBM_GBS = 8000.0
 N_PM, N_JOINT = 5, 28
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_proj_edit8432_traffic.json")
@@ -77,7 +84,8 @@ def measured_traffic(launch_tokens):
     return t.get("bytes_per_launch")
 
 
-def time_joint_block(F, dims, lay, segs, n, rand, rand_block, reps=20, warmup=5, copies=4):
+def time_joint_block(F, dims, lay, segs, n, rand, rand_block, reps=20, warmup=5, copies=4,
+                     peak=PEAK_BF16_TFLOPS):
     """One joint block over all n tokens: median/min of `reps` event-timed
     calls with rotating weight copies, plus per-kernel GEMM and attention
     rates over the same calls."""
@@ -125,7 +133,7 @@ def time_joint_block(F, dims, lay, segs, n, rand, rand_block, reps=20, warmup=5,
             "median_ms": med, "min_ms": ms[0],
             "tokens_per_s": n / (med * 1e-3),
             "tflops": block_flops / (med * 1e-3) / 1e12,
-            "frac_peak": block_flops / (med * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+            "frac_peak": block_flops / (med * 1e-3) / 1e12 / peak,
             "gemm_tflops": gemm_flops / (gemm_ms * 1e-3) / 1e12,
             "attention_tflops": attn_flops / (attn_ms * 1e-3) / 1e12,
             "kernel_ms": {k: v["total_ms"] / reps for k, v in stats.items()}}
@@ -238,6 +246,8 @@ def main():
                     help="keep the weights in Linear layout instead of packing them at load")
     ap.add_argument("--no-sample", action="store_true",
                     help="skip the whole-call and denoise-loop timings")
+    ap.add_argument("--no-fp8", action="store_true",
+                    help="skip the rowwise-FP8 block and step timings")
     ap.add_argument("--no-block", action="store_true",
                     help="skip the single-block, whole-call and denoise-loop timings "
                          "(profiling runs of the step alone)")
@@ -266,11 +276,15 @@ def main():
     def rand(*shape, std=1.0, dtype=torch.bfloat16):
         return (torch.randn(*shape, generator=g, device=dev, dtype=torch.float32) * std).to(dtype)
 
-    def rand_block():
+    def rand_block(fp8=False):
         w = {"wq": rand(D, D, std=0.02), "wk": rand(D, D, std=0.02), "wv": rand(D, D, std=0.02),
              "wo": rand(D, D, std=0.02), "w_gate": rand(Fh, D, std=0.02),
              "w_up": rand(Fh, D, std=0.02), "w_down": rand(D, Fh, std=0.02),
              "q_norm": torch.ones(128, device=dev), "k_norm": torch.ones(128, device=dev)}
+        if fp8:
+            # rowwise e4m3 codes and scales, quantised once at load
+            buf = torch.empty(F.weights_fp8r_bytes(dims), dtype=torch.uint8, device=dev)
+            return F.weights_quantize_fp8r(dims, w, buf)
         if args.linear_weights:
             return w
         # static weights go to the GEMMs' packed operand layout once, at load
@@ -295,12 +309,12 @@ def main():
     ws = torch.empty(F.workspace_bytes(dims, n), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
 
-    def step():
+    def step(pm=per_mode, jt=joint):
         F.rope_tables_build(lay, rope, stream=stream)
         F.modulation_forward(dims, mod_w[0], t_by_mode, segs, m1, mws, stream=stream)
         F.modulation_forward(dims, mod_w[1], t_by_mode, segs, m2, mws, stream=stream)
         x.copy_(x0)
-        F.stack_forward(dims, per_mode, joint, x, segs, m1, m2, rope, ws, stream=stream)
+        F.stack_forward(dims, pm, jt, x, segs, m1, m2, rope, ws, stream=stream)
 
     for _ in range(args.warmup):
         step()
@@ -374,6 +388,51 @@ def main():
         block["attention_frac_peak"] = block["attention_tflops"] / PEAK_BF16_TFLOPS
         if not args.no_sample:
             whole = time_whole_calls(F, dims, lay, segs, n, rand, per_mode, joint, emb_w, mod_w)
+    fp8 = None
+    if not args.no_fp8:
+        fp8 = {"weights": "rowwise e4m3 codes + fp32 row scales (flux3_weights_quantize_fp8r); "
+                          "h and [o | act] quantised per token in each block",
+               "peak_tflops": PEAK_FP8_TFLOPS}
+        if not args.no_block:
+            b8 = time_joint_block(F, dims, lay, segs, n, rand, lambda: rand_block(True),
+                                  peak=PEAK_FP8_TFLOPS)
+            b8["gemm_frac_fp8_peak"] = b8["gemm_tflops"] / PEAK_FP8_TFLOPS
+            b8["attention_frac_bf16_peak"] = b8["attention_tflops"] / PEAK_BF16_TFLOPS
+            fp8["block"] = b8
+        pm8 = {m: [rand_block(True) for _ in range(N_PM)] for m in modes}
+        jt8 = [rand_block(True) for _ in range(N_JOINT)]
+        for _ in range(args.warmup):
+            step(pm8, jt8)
+        torch.cuda.synchronize()
+        assert torch.isfinite(x).all(), "non-finite fp8 stack output"
+        F.profile_reset()
+        F.profile_enable(True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            step(pm8, jt8)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        F.profile_enable(False)
+        st8 = {k: F.profile_read(k) for k in F.KERNELS}
+        F.profile_reset()
+        ms8 = (t1 - t0) / args.steps * 1e3
+        fp8["ms_per_step"] = ms8
+        fp8["block_tokens_per_s"] = passes / (ms8 / 1e3)
+        fp8["speedup_vs_bf16_step"] = ms_per_step / ms8
+        fp8["kernel_ms_per_step"] = {k: v["total_ms"] / args.steps for k, v in st8.items()
+                                     if v["launches"]}
+        g8 = st8["gemm_proj"]
+        g8_ms = g8["total_ms"] / max(g8["launches"], 1)
+        g8_tf = proj_fpt * g8["tokens"] / max(g8["launches"], 1) / (g8_ms * 1e-3) / 1e12
+        fp8["gemm_proj"] = {"avg_us": 1e3 * g8_ms, "tflops": g8_tf,
+                            "frac_fp8_peak": g8_tf / PEAK_FP8_TFLOPS}
+        o8 = st8["gemm_out"]
+        o8_ms = o8["total_ms"] / max(o8["launches"], 1)
+        o8_tf = out_fpt * o8["tokens"] / max(o8["launches"], 1) / (o8_ms * 1e-3) / 1e12
+        fp8["gemm_out"] = {"avg_us": 1e3 * o8_ms, "tflops": o8_tf,
+                           "frac_fp8_peak": o8_tf / PEAK_FP8_TFLOPS}
+        del pm8, jt8
     devinfo = F.device_query(0)
     peak = {"spec_tflops": PEAK_BF16_TFLOPS, "derived_tflops": devinfo["bf16_dense_tflops"],
             "compute_units": devinfo["compute_units"], "clock_mhz": devinfo["clock_khz"] / 1e3,
@@ -412,6 +471,7 @@ def main():
         "whole_call": whole,
         "peak": peak,
         "roofline": roofline,
+        "fp8r": fp8,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out))

@@ -500,22 +500,12 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_gemm_proj(ProjArgs p) {
     gemm_mainloop<true, PW, true, F8>(smem, acc, H, W, Dk / BK, W, 0, Dk / BK);
   else
     gemm_mainloop<PW, true, false, F8>(smem, acc, W, H, Dk / BK, H, 0, Dk / BK);
-  if constexpr (F8) {
-    // scale of weight row r of matrix kind (q k v gate up) in p.sw
-    auto w_scale = [&](int i) -> const float* {
-      const int base = kind < 3 ? kind * D : 3 * D + ((i & 3) < 2 ? 0 : p.F);
-      return p.sw + base + w_row(i);
-    };
-    if (kind == 2) {
-      const float* const a_run[4] = {p.sh + m0 + wm * 128, p.sh + m0 + wm * 128 + 32,
-                                     p.sh + m0 + wm * 128 + 64, p.sh + m0 + wm * 128 + 96};
-      scale_acc(acc, a_run, w_scale(4 * wn), lane);
-    } else {
-      const float* const a_run[4] = {w_scale(4 * wm), w_scale(4 * wm + 1), w_scale(4 * wm + 2),
-                                     w_scale(4 * wm + 3)};
-      scale_acc(acc, a_run, p.sh + m0 + wn * 128, lane);
-    }
-  }
+  // F8: the row scales multiply the products where the epilogues read them
+  // (a scaled copy of the whole accumulator would not fit in registers);
+  // sw_kind: the scales of this tile's weight matrix rows, or of the gate
+  // rows for SwiGLU (the up rows follow F rows later)
+  const float* sw_kind = nullptr;
+  if constexpr (F8) sw_kind = p.sw + (kind < 3 ? kind * D : 3 * D);
 
   const int r32 = lane & 31, hi = lane >> 5;
   // LDS is free once every wave is past the main loop.  Values and SwiGLU
@@ -552,11 +542,22 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_gemm_proj(ProjArgs p) {
     bf16* dst = (kind == 0 ? p.q : p.k) + (size_t)head0 * p.n_pad * kHeadDim;
     // the norm weights of this lane's 64 dims, loaded once
     float4 nwv[4][4];
+    // F8: the scales of the head's 128 weight rows (this wave's head
+    // head0 + wm), folded into the norm weights
+    const float* swh = F8 ? sw_kind + (head0 + wm) * 128 : nullptr;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int g = 0; g < 4; ++g)
+      for (int g = 0; g < 4; ++g) {
         nwv[i][g] = *reinterpret_cast<const float4*>(nw + i * 32 + 8 * g + 4 * hi);
+        if constexpr (F8) {
+          const float4 sv = *reinterpret_cast<const float4*>(swh + i * 32 + 8 * g + 4 * hi);
+          nwv[i][g].x *= sv.x;
+          nwv[i][g].y *= sv.y;
+          nwv[i][g].z *= sv.z;
+          nwv[i][g].w *= sv.w;
+        }
+      }
     // Output rows go out through the 32 KiB of LDS past the RoPE rows, one
     // register block j at a time: the four waves' 32 tokens x 128 dims
     // (staged row (2 wm + wn) 32 + token, 256 B, 16-byte chunk c in slot
@@ -568,12 +569,30 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_gemm_proj(ProjArgs p) {
       const int t = wn * 128 + j * 32 + r32;             // token within the tile
       const bool live = m0 + t < p.M;
       float ss = 0.f;
+      float rs;
+      if constexpr (F8) {
+        // x = acc * sw[dim] * sh[token]: the RMS over the head's dims of
+        // acc * sw, times the token scale; the output factor sh * rs
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) ss += acc.c[i][j][e] * acc.c[i][j][e];
-      ss += xor_lane(ss, 32);
-      const float rs = 1.0f / sqrtf(ss * (1.0f / kHeadDim) + p.eps);
+          for (int g = 0; g < 4; ++g) {
+            const float4 sv = *reinterpret_cast<const float4*>(swh + i * 32 + 8 * g + 4 * hi);
+            const float a0 = acc.c[i][j][4 * g] * sv.x, a1 = acc.c[i][j][4 * g + 1] * sv.y;
+            const float a2 = acc.c[i][j][4 * g + 2] * sv.z, a3 = acc.c[i][j][4 * g + 3] * sv.w;
+            ss += (a0 * a0 + a1 * a1) + (a2 * a2 + a3 * a3);
+          }
+        ss += xor_lane(ss, 32);
+        const float st = p.sh[m0 + t];
+        rs = st / sqrtf(st * st * ss * (1.0f / kHeadDim) + p.eps);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) ss += acc.c[i][j][e] * acc.c[i][j][e];
+        ss += xor_lane(ss, 32);
+        rs = 1.0f / sqrtf(ss * (1.0f / kHeadDim) + p.eps);
+      }
       const int srow = (2 * wm + wn) * 32 + r32;
       // all of the token's RoPE chunks first: a read placed after a staging
       // write would wait for it
@@ -617,19 +636,29 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_gemm_proj(ProjArgs p) {
     }
   } else if (kind == 2) {
     // values, transposed: staged as [head][dim][256 token positions]
+    float swj[4] = {1.f, 1.f, 1.f, 1.f};   // F8: scales of the lane's dim rows
+    if constexpr (F8) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) swj[j] = sw_kind[head0 * 128 + wn * 128 + j * 32 + r32];
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int mb = wm * 128 + i * 32 + 8 * g + 4 * hi;   // first of 4 tokens, tile-local
         const int pos = vt_pos(mb);
+        float4 stv = make_float4(1.f, 1.f, 1.f, 1.f);      // F8: the 4 tokens' scales
+        if constexpr (F8) stv = *reinterpret_cast<const float4*>(p.sh + m0 + mb);
+        const float st[4] = {stv.x, stv.y, stv.z, stv.w};
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int r = wn * 128 + j * 32 + r32;             // head-local dim row
           bf16x4 v;
 #pragma unroll
-          for (int e = 0; e < 4; ++e)
-            v[e] = f2bf(m0 + mb + e < p.M ? acc.c[i][j][4 * g + e] : 0.f);
+          for (int e = 0; e < 4; ++e) {
+            const float a = F8 ? acc.c[i][j][4 * g + e] * (st[e] * swj[j]) : acc.c[i][j][4 * g + e];
+            v[e] = f2bf(m0 + mb + e < p.M ? a : 0.f);
+          }
           *(lds_bf16x4*)(smem + r * 512 + (((pos >> 3) ^ (r & 31)) << 4) + (pos & 7) * 2) = v;
         }
       }
@@ -647,10 +676,24 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_gemm_proj(ProjArgs p) {
   } else {
     // SwiGLU: register blocks 0,1 are gate rows, 2,3 the matching up rows;
     // staged as [token][128 hidden units]
+    // F8: scales of the lane's gate and up rows (hidden units
+    // hid0 + 64 wm + 32 i + 8 g + 4 hi + e)
+    float4 sgv[2][4], suv[2][4];
+    if constexpr (F8) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const float* sg = sw_kind + hid0 + 64 * wm + 32 * i + 8 * g + 4 * hi;
+          sgv[i][g] = *reinterpret_cast<const float4*>(sg);
+          suv[i][g] = *reinterpret_cast<const float4*>(sg + p.F);
+        }
+    }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int t = wn * 128 + j * 32 + r32;
       const bool live = m0 + t < p.M;
+      const float st = F8 ? p.sh[m0 + t] : 1.f;
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -658,7 +701,13 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_gemm_proj(ProjArgs p) {
           bf16x4 o;
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            const float gt = acc.c[i][j][4 * g + e], up = acc.c[i + 2][j][4 * g + e];
+            float gt = acc.c[i][j][4 * g + e], up = acc.c[i + 2][j][4 * g + e];
+            if constexpr (F8) {
+              const float sg[4] = {sgv[i][g].x, sgv[i][g].y, sgv[i][g].z, sgv[i][g].w};
+              const float su[4] = {suv[i][g].x, suv[i][g].y, suv[i][g].z, suv[i][g].w};
+              gt *= sg[e] * st;
+              up *= su[e] * st;
+            }
             const float a = gt * __builtin_amdgcn_rcpf(1.0f + __expf(-gt)) * up;
             o[e] = f2bf(live ? a : 0.f);
           }
