@@ -394,7 +394,7 @@ def output_layer(x_img, shift, scale, w_out, dtype=np.float64, eps=EPS_LN):
 
 
 def transformer_forward(text, image, refs, segs, io_w, emb_w, w_mod, per_mode, joint, rope,
-                        t, t_target=None, dtype=np.float64, keep=False):
+                        t, t_target=None, dtype=np.float64, keep=False, block_fn=None):
     """One transformer call: input projections, the two stages' modulation
     from the timesteps (image tokens t, text and references 0), the two-stage
     stack, then the output layer on the image rows.
@@ -403,7 +403,8 @@ def transformer_forward(text, image, refs, segs, io_w, emb_w, w_mod, per_mode, j
     for the distilled model, {w1_tgt, w2_tgt}; w_mod[stage][mode] the
     per-(stage, mode) modulation linears.  segs: (start, count, mode) in the
     order text, image, references.  Returns the velocity of the image tokens
-    (and, with keep, the residual stream after the stack).
+    (and, with keep, the residual stream after the stack).  block_fn: as for
+    stack_forward.
     """
     x = input_projection(text, image, refs, io_w["w_text"], io_w["w_img_in"],
                          io_w["w_ref_in"], dtype)
@@ -415,7 +416,8 @@ def transformer_forward(text, image, refs, segs, io_w, emb_w, w_mod, per_mode, j
         per = modulation_from_t(t_by_mode, emb_w["w1"], emb_w["w2"], w_mod[stage],
                                 dtype=dtype, **tgt)
         mods.append(np.stack([per[m] for _s, _c, m in segs]))
-    x = stack_forward(x, per_mode, joint, segs, mods[0], mods[1], rope, dtype=dtype)
+    x = stack_forward(x, per_mode, joint, segs, mods[0], mods[1], rope, dtype=dtype,
+                      block_fn=block_fn)
     shift, scale = final_modulation(t, emb_w["w1"], emb_w["w2"], io_w["w_final"], dtype=dtype,
                                     **tgt)
     img = [(st, c) for st, c, m in segs if m == MODE_IMAGE]

@@ -20,8 +20,8 @@ from oracle import flux3_oracle as O
 pytestmark = pytest.mark.gpu
 
 from layouts import unpack8_rows, unpack_rows  # noqa: E402
-from gpu_util import (DEV, assert_close, assert_close_stack, rope_dev, seg_tuples,  # noqa: E402
-                      upload_weights, workspace)
+from gpu_util import (DEV, assert_close, assert_close_stack, bf16_dev, rope_dev,  # noqa: E402
+                      seg_tuples, upload_weights, workspace)
 
 SMALL = synth.Dims(width=256, heads=2, head_dim=128, mlp_hidden=384)
 
@@ -245,3 +245,77 @@ def test_stack_small_dims_full_depth():
     want = O.stack_forward(x_np, pm_o, jt_o, seg_tuples(segs), m1, m2, oracle_rope(layout),
                            block_fn=O.block_forward_fp8)
     assert_close_stack(got, want, x_np, "fp8 stack")
+
+
+def test_block_4k_sampled_rows():
+    """The 65,776-token block (240 text + 256 x 256 image tokens): the
+    largest configuration, the quantiser over 65,776 rows and K4's
+    stream-K tail on fp8 tiles, checked on sampled rows."""
+    dims = synth.DIMS
+    layout = synth.workload("t2i4k65776").layout
+    segs, w, x, mod = _case(layout, 4)
+    got, _ = run_fp8_block(dims, w, x, segs, mod, layout)
+    rng = np.random.default_rng(4)
+    n = layout.n_tokens
+    rows = np.unique(np.concatenate([[0, 239, 240, 241, n - 2, n - 1],
+                                     rng.choice(n, 26, replace=False)]))
+    want = O.block_forward_fp8(x, oracle_fp8(w), seg_tuples(segs), mod, oracle_rope(layout),
+                               rows=rows, dtype=np.float32, attn_chunk=16)
+    assert_close(got[rows], want, "x_out fp8 rows 4k")
+    assert_close(got[rows] - x[rows], want - x[rows], "delta fp8 rows 4k")
+
+
+def test_transformer_call_with_fp8_blocks():
+    """A whole transformer call (input linears, both stages' modulation from
+    t, 2 + 2 rowwise-FP8 blocks, the output layer) against the oracle's call
+    with its FP8 block; the bar of the bf16 transformer tests."""
+    dims = SMALL
+    layout = synth.RopeLayout(80, 8, 12, ((8, 12),))
+    text_dim, t, t_target, seed = 256, 0.45, 0.25, 8
+    D = dims.width
+    segs = layout.segments()
+    n = layout.n_tokens
+    modes = sorted({s_.mode for s_ in segs})
+    n_text = sum(s_.count for s_ in segs if s_.mode == 0)
+    n_img = sum(s_.count for s_ in segs if s_.mode == 1)
+    n_ref = sum(s_.count for s_ in segs if s_.mode == 2)
+    io = synth.io_weights(seed, D, text_dim=text_dim)
+    mw = synth.modulation_weights(seed, D, stages=(0, 1), modes=modes, target=True)
+    per_mode = {m: [synth.block_weights(seed, 10 * m + b, dims) for b in range(2)] for m in modes}
+    joint = [synth.block_weights(seed, 100 + b, dims) for b in range(2)]
+    text, image, refs = synth.edge_inputs(seed, n_text, n_img, n_ref, text_dim=text_dim)
+    keep = []
+
+    def dev(w):
+        w8, buf = fp8_weights(dims, w)
+        keep.append((w8, buf))
+        return w8
+
+    def mod_d(stage):
+        out = {k: bf16_dev(mw[k]) for k in ("w1", "w2", "w1_tgt", "w2_tgt")}
+        out["w_mod"] = {m: bf16_dev(v) for m, v in mw["w_mod"][stage].items()}
+        return out
+
+    io_d = {k: bf16_dev(v) for k, v in io.items()}
+    v = torch.full((n_img, synth.LATENT_DIM), float("nan"), dtype=torch.float32, device=DEV)
+    io_dims = F.IoDims(text_dim, synth.LATENT_DIM)
+    ws = torch.empty(F.transformer_workspace_bytes(dims, io_dims, n), dtype=torch.uint8,
+                     device=DEV)
+    F.transformer_forward(dims, io_dims, io_d, [mod_d(0), mod_d(1)],
+                          {m: [dev(w) for w in ws_] for m, ws_ in per_mode.items()},
+                          [dev(w) for w in joint], bf16_dev(text),
+                          torch.from_numpy(image).to(DEV), torch.from_numpy(refs).to(DEV), segs,
+                          t, rope_dev(layout), v, ws, t_target=t_target)
+    torch.cuda.synchronize()
+    got = v.cpu().numpy()
+
+    f = synth.bf16_bits_to_f32
+    emb = {k: f(mw[k]) for k in ("w1", "w2", "w1_tgt", "w2_tgt")}
+    w_mod = [{m: f(w) for m, w in mw["w_mod"][st].items()} for st in (0, 1)]
+    want = O.transformer_forward(f(text), image, refs, seg_tuples(segs),
+                                 {k: f(v_) for k, v_ in io.items()}, emb, w_mod,
+                                 {m: [oracle_fp8(w) for w in ws_] for m, ws_ in per_mode.items()},
+                                 [oracle_fp8(w) for w in joint], oracle_rope(layout), t,
+                                 t_target=t_target, block_fn=O.block_forward_fp8)
+    rms = float(np.sqrt(np.mean(want ** 2)))
+    assert_close(got, want, "fp8 transformer velocity", maxabs_tol=3e-2 * max(1.0, rms))
