@@ -1236,10 +1236,17 @@ hipError_t launch_gemm_out(const BlockShape& bs, const BlockWeightsDev& w,
   const int G = p.groups;
   p.dp_rounds = n_tiles / G;
   p.tail = n_tiles % G;
-  // a tail filling nearly a whole round runs whole (its tiles keep sharing
-  // L2); a thinner one is spread over all workgroups (at 4096 tokens, 192
-  // tiles on 256 CUs: 328 us split against 351 us whole)
-  if (p.tail * 20 > G * 17) {
+  // The leftover tiles run as one more round of whole tiles unless they are
+  // few.  A split slice costs about 1.6x (bf16) / 2x (fp8) a whole-tile one:
+  // split ranges do not walk the same slices as their XCD neighbours, so
+  // their operands come from the Infinity Cache instead of L2.  Measured
+  // per bf16 launch, split against whole: 240 tokens (12 tiles, 5% of a
+  // round) 70 us against 222 us; 8432 tokens (55%) 611 against 650; 4096
+  // tokens (75%) 306 against 314; 4336 tokens (80%) 392 against 316.  fp8
+  // prefers whole
+  // tiles from about half a round (8432 tokens: 328 split, 310 whole).
+  const int split_pct = w.fp8 ? 45 : 78;
+  if (p.tail * 100 >= G * split_pct) {
     p.dp_rounds += 1;
     p.tail = 0;
   }
