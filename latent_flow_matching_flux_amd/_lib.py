@@ -105,7 +105,8 @@ def load(path=LIB_PATH):
     if _lib is not None:
         return _lib
     if not os.path.exists(path):
-        raise ImportError(f"libflux3.so not built at {path}; run __graft_entry__.build()")
+        raise ImportError(f"libflux3.so not built at {path}; build it with "
+                          "python -m latent_flow_matching_flux_amd.build")
     lib = ctypes.CDLL(path)
     P = ctypes.POINTER
     i32, i64, sz, vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_void_p
