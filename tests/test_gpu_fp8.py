@@ -319,3 +319,55 @@ def test_transformer_call_with_fp8_blocks():
                                  t_target=t_target, block_fn=O.block_forward_fp8)
     rms = float(np.sqrt(np.mean(want ** 2)))
     assert_close(got, want, "fp8 transformer velocity", maxabs_tol=3e-2 * max(1.0, rms))
+
+
+def test_stack_mixes_weight_layouts():
+    """One stack whose blocks come in all three layouts (Linear bf16, packed
+    bf16, rowwise FP8): each block follows its own weights' arithmetic."""
+    dims = SMALL
+    layout = synth.RopeLayout(40, 6, 8, ((6, 8),))
+    segs = layout.segments()
+    n = layout.n_tokens
+    kinds = ("linear", "packed", "fp8")
+    pm_np = {m: [synth.block_weights(51 + m, b, dims) for b in range(3)] for m in range(3)}
+    jt_np = [synth.block_weights(57, b, dims) for b in range(3)]
+    x_np = synth.tokens(51, n, dims.width)
+    m1 = synth.modulation(51, 1, len(segs), dims.width)
+    m2 = synth.modulation(51, 2, len(segs), dims.width)
+    keep = []
+
+    def dev(w, kind):
+        if kind == "fp8":
+            w8, buf = fp8_weights(dims, w)
+            keep.append((w8, buf))
+            return w8
+        w_dev = upload_weights(w)
+        keep.append(w_dev)
+        if kind == "linear":
+            return w_dev
+        buf = torch.empty(F.weights_packed_bytes(dims), dtype=torch.uint8, device=DEV)
+        pw = F.weights_pack(dims, w_dev, buf)
+        keep.append((pw, buf))
+        return pw
+
+    pm = {m: [dev(w, kinds[b]) for b, w in enumerate(ws)] for m, ws in pm_np.items()}
+    jt = [dev(w, kinds[(b + 1) % 3]) for b, w in enumerate(jt_np)]
+    x = torch.from_numpy(x_np).to(DEV)
+    F.stack_forward(dims, pm, jt, x, segs,
+                    torch.from_numpy(np.ascontiguousarray(m1, np.float32)).to(DEV),
+                    torch.from_numpy(np.ascontiguousarray(m2, np.float32)).to(DEV),
+                    rope_dev(layout), workspace(dims, n))
+    torch.cuda.synchronize()
+    got = x.cpu().numpy()
+
+    def block(xb, w, sg, md, rp, dtype=np.float64):
+        if "w1" in w:
+            return O.block_forward_fp8(xb, w, sg, md, rp, dtype=dtype)
+        return O.block_forward(xb, w, sg, md, rp, dtype=dtype)
+
+    pm_o = {m: [oracle_fp8(w) if kinds[b] == "fp8" else w for b, w in enumerate(ws)]
+            for m, ws in pm_np.items()}
+    jt_o = [oracle_fp8(w) if kinds[(b + 1) % 3] == "fp8" else w for b, w in enumerate(jt_np)]
+    want = O.stack_forward(x_np, pm_o, jt_o, seg_tuples(segs), m1, m2, oracle_rope(layout),
+                           block_fn=block)
+    assert_close_stack(got, want, x_np, "mixed-layout stack")
