@@ -856,3 +856,32 @@ def test_fp8_block_is_the_block_on_dequantised_operands():
     rows = [1, 6, 12]
     np.testing.assert_allclose(O.block_forward_fp8(x, w8, segs, mod, tab, rows=rows), got[rows],
                                rtol=1e-12, atol=1e-12)
+
+
+def test_quantize_rowwise_decides_in_fp32():
+    """The rounding decision is taken on the fp32 product v * (448 / a): rows
+    built so that this product lands exactly on e4m3 midpoints while the
+    exact product does not must round to the even neighbour of the
+    midpoint (brute-force search on the fp32 product)."""
+    mids = (O.E4M3[1:0x7E] + O.E4M3[2:0x7F]) / 2
+    rows, discriminating = [], 0
+    for amax in (1344.0, 2240.0, 3136.0, 492.8, 1000.0):
+        mult = np.float32(448.0) / np.float32(amax)
+        row = [np.float32(amax)]
+        for mdp in mids[::3]:
+            x = np.float32(mdp / float(mult))
+            for _ in range(8):          # walk to an x whose fp32 product is the midpoint
+                p = np.float32(x * mult)
+                if p == mdp:
+                    break
+                x = np.nextafter(x, np.float32(np.inf) if p < mdp else np.float32(-np.inf))
+            if np.float32(x * mult) == mdp and 0 < x < amax:
+                row.append(x)
+                discriminating += float(x) * float(mult) != mdp
+        rows.append(np.array(row + [0.0] * (64 - len(row)), np.float32)[:64])
+    a = np.stack(rows)
+    assert discriminating > 10       # the exact products miss the midpoints
+    codes, _ = O.quantize_rowwise(a)
+    amax = np.abs(a).max(axis=1)
+    prod = (a * (np.float32(448.0) / amax)[:, None]).astype(np.float32)
+    np.testing.assert_array_equal(codes, _e4m3_brute(prod.astype(np.float64)))
