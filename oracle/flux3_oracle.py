@@ -12,7 +12,7 @@ Sources (the release pages; cited by page title and section):
         sections "Speed, architecture, and how the tokens move" and
         "Smaller GPUs, single files, and custom LoRA training" (rowwise FP8).
 * [P3]  The Chinese translation of the Diffusers release post (everytik.com):
-        the `block(x, shift, scale, gate)` listing and the RoPE position
+        the block listing (modulated by shift, scale and gate) and the RoPE position
         table under the model walk-through.
 * [P4]  "How to Run FLUX 3 Image Klein Locally" (rohitghumare.com), sections
         "Inside the transformer", "The latent space and the VAE",
@@ -154,6 +154,14 @@ def rms_norm_heads(x, weight, eps=EPS_RMS):
     return x / np.sqrt(ms + eps) * weight
 
 
+# Attention's heads and query chunks are independent computations; they may
+# be evaluated by THREADS threads at once (numpy releases the GIL inside its
+# kernels, and the BLAS library is held to one thread per call meanwhile).
+# Every piece runs the same operations either way; THREADS only changes how
+# long the oracle takes (and, at most, the BLAS library's own blocking).
+THREADS = 1
+
+
 def attention(q, k, v, chunk=None):
     """Full bidirectional softmax attention per head, no mask.
 
@@ -165,17 +173,28 @@ def attention(q, k, v, chunk=None):
     nq, n_heads, hd = q.shape
     scale = 1.0 / np.sqrt(hd)
     out = np.empty((nq, n_heads, hd), dtype=q.dtype)
-    step = nq if not chunk else chunk
-    for h in range(n_heads):
+    step = max(nq if not chunk else chunk, 1)
+
+    def piece(h, r0):
         kh = k[:, h, :]
         vh = v[:, h, :]
-        for r0 in range(0, nq, max(step, 1)):
-            qh = q[r0:r0 + step, h, :]
-            s = (qh @ kh.T) * scale
-            s = s - s.max(axis=-1, keepdims=True)
-            p = np.exp(s)
-            p = p / p.sum(axis=-1, keepdims=True)
-            out[r0:r0 + step, h, :] = p @ vh
+        qh = q[r0:r0 + step, h, :]
+        s = (qh @ kh.T) * scale
+        s = s - s.max(axis=-1, keepdims=True)
+        p = np.exp(s)
+        p = p / p.sum(axis=-1, keepdims=True)
+        out[r0:r0 + step, h, :] = p @ vh
+
+    jobs = [(h, r0) for h in range(n_heads) for r0 in range(0, nq, step)]
+    if THREADS > 1 and len(jobs) > 1:
+        from concurrent.futures import ThreadPoolExecutor
+        from threadpoolctl import threadpool_limits
+        with threadpool_limits(limits=1, user_api="blas"), ThreadPoolExecutor(THREADS) as ex:
+            for f in [ex.submit(piece, h, r0) for h, r0 in jobs]:
+                f.result()
+    else:
+        for h, r0 in jobs:
+            piece(h, r0)
     return out
 
 
@@ -213,14 +232,16 @@ def _weights(w, dtype):
 
 def block_forward(x, w, segs, mod, rope, heads=None, dtype=np.float64,
                   eps_ln=EPS_LN, eps_rms=EPS_RMS, keep=False, attn_chunk=None):
-    """One transformer block, following the release's block listing [P3]:
+    """One transformer block, in the order of the model walk-through of the
+    Diffusers release post ([P3], its block section; [P4] "Inside the
+    transformer"):
 
-      h = layer_norm(x)                       (no learned affine)
-      h = (1 + scale) * h + shift             (per-segment modulation)
-      q, k, v = to_q(h), to_k(h), to_v(h)
-      q, k = rope(rms_norm(q)), rope(rms_norm(k))
-      out = to_out(attention(q, k, v)) + mlp(h)      (parallel; SwiGLU)
-      return x + gate * out
+      h   = (1 + c_scale) . LN(x) + c_shift     LN without affine; c per segment
+      Q   = R(N_q(h Wq^T)),  K = R(N_k(h Wk^T)),  V = h Wv^T
+            (N: per-head RMS normalisation with a [128] scale, R: 4-axis rotation)
+      A   = softmax(Q K^T / sqrt(128)) V  per head, then A Wo^T
+      G   = (silu(h Wg^T) * (h Wu^T)) Wd^T     (SwiGLU, beside attention)
+      x'  = x + c_gate . (A Wo^T + G)
 
     x: [N][D]; w: dict of weights (torch Linear layout [out][in]); segs:
     list of (start, count, mode) covering [0, N); mod: [n_segs][3][D]

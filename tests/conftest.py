@@ -13,6 +13,23 @@ def pytest_configure(config):
     config.addinivalue_line("markers", "slow: long-running CPU oracle check")
 
 
+def oracle_threads():
+    """Threads the oracle's attention may use: the host's CPU share (the
+    OMP_NUM_THREADS setting where there is one), at most 16."""
+    n = len(os.sched_getaffinity(0))
+    env = os.environ.get("OMP_NUM_THREADS", "")
+    if env.isdigit() and int(env) > 0:
+        n = min(n, int(env))
+    return max(1, min(n, 16))
+
+
+@pytest.fixture(scope="session", autouse=True)
+def _oracle_threads():
+    from oracle import flux3_oracle as O
+    O.THREADS = oracle_threads()
+    yield
+
+
 @pytest.fixture(scope="session")
 def repo_root():
     return ROOT

@@ -198,19 +198,16 @@ def test_block_small_dims_three_segments():
     assert_close(got - x, want - x, "delta fp8 small dims")
 
 
-def test_block_edit8432_sampled_rows():
-    """The 8432-token edit block (the bench's workload), on sampled rows."""
+def test_block_edit8432_all_rows():
+    """The 8432-token edit block (the bench's workload), every row."""
     dims = synth.DIMS
     layout = synth.workload("edit8432").layout
     segs, w, x, mod = _case(layout, 0)
     got, _ = run_fp8_block(dims, w, x, segs, mod, layout)
-    rng = np.random.default_rng(0)
-    rows = np.unique(np.concatenate([[0, 239, 240, 4335, 4336, 8431],
-                                     rng.choice(8432, 58, replace=False)]))
     want = O.block_forward_fp8(x, oracle_fp8(w), seg_tuples(segs), mod, oracle_rope(layout),
-                               rows=rows, dtype=np.float32)
-    assert_close(got[rows], want, "x_out fp8 rows")
-    assert_close(got[rows] - x[rows], want - x[rows], "delta fp8 rows")
+                               dtype=np.float32, attn_chunk=2048)
+    assert_close(got, want, "x_out fp8 edit8432")
+    assert_close(got - x, want - x, "delta fp8 edit8432")
 
 
 def test_stack_small_dims_full_depth():
@@ -245,6 +242,37 @@ def test_stack_small_dims_full_depth():
     want = O.stack_forward(x_np, pm_o, jt_o, seg_tuples(segs), m1, m2, oracle_rope(layout),
                            block_fn=O.block_forward_fp8)
     assert_close_stack(got, want, x_np, "fp8 stack")
+
+
+def test_stack336_full_width():
+    """5 per-mode + 28 joint rowwise-FP8 blocks at the model width on the
+    336-token workload (weights cycle through 2 sets per mode and 3 joint
+    sets), against the oracle's stack of block_forward_fp8."""
+    from stack_inputs import stack_inputs
+    dims = synth.DIMS
+    layout = synth.workload("block336").layout
+    segs, pm_np, jt_np, x_np, m1, m2 = stack_inputs(dims, layout, 5, 28, seed=47)
+    n = layout.n_tokens
+    dev8 = {}
+
+    def dev(w):
+        if id(w) not in dev8:
+            dev8[id(w)] = fp8_weights(dims, w)
+        return dev8[id(w)][0]
+
+    x = torch.from_numpy(x_np).to(DEV)
+    F.stack_forward(dims, {m: [dev(w) for w in ws] for m, ws in pm_np.items()},
+                    [dev(w) for w in jt_np], x, segs,
+                    torch.from_numpy(np.ascontiguousarray(m1, np.float32)).to(DEV),
+                    torch.from_numpy(np.ascontiguousarray(m2, np.float32)).to(DEV),
+                    rope_dev(layout), workspace(dims, n))
+    torch.cuda.synchronize()
+    got = x.cpu().numpy()
+    pm_o = {m: [oracle_fp8(w) for w in ws] for m, ws in pm_np.items()}
+    jt_o = [oracle_fp8(w) for w in jt_np]
+    want = O.stack_forward(x_np, pm_o, jt_o, seg_tuples(segs), m1, m2, oracle_rope(layout),
+                           dtype=np.float32, block_fn=O.block_forward_fp8)
+    assert_close_stack(got, want, x_np, "fp8 stack336 full width")
 
 
 def test_block_4k_sampled_rows():

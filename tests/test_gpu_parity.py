@@ -30,14 +30,7 @@ def _lib():
     torch.cuda.synchronize()
 
 
-_WCACHE = {}
-
-
-def weights(seed, block_id, dims=synth.DIMS, norm_stress=False):
-    key = (seed, block_id, dims, norm_stress)
-    if key not in _WCACHE:
-        _WCACHE[key] = synth.block_weights(seed, block_id, dims, norm_stress=norm_stress)
-    return _WCACHE[key]
+from stack_inputs import stack_inputs as _stack_inputs, weights  # noqa: E402
 
 
 def run_block(dims, w_np, x_np, segs, mod_np, layout):
@@ -177,41 +170,23 @@ def test_error_leaves_x_untouched():
 
 
 # --------------------------------------------------------------------------
-# full-size block, edit workload [240 | 4096 | 4096]: sampled rows
+# full-size block, edit workload [240 | 4096 | 4096]: every row
 # --------------------------------------------------------------------------
-def test_block_edit8432_sampled_rows():
+def test_block_edit8432_all_rows():
+    """The 8432-token joint block the bench times, every row against the
+    fp32 oracle."""
     dims = synth.DIMS
     layout, segs, w, x, mod = _case(name="edit8432", seed=0)
     got, _, _ = run_block(dims, w, x, segs, mod, layout)
-    rng = np.random.default_rng(0)
-    rows = np.unique(np.concatenate([[0, 239, 240, 4335, 4336, 8431],
-                                     rng.choice(8432, 58, replace=False)]))
-    want = O.block_forward_rows(x, w, seg_tuples(segs), mod, oracle_rope(layout), rows,
-                                dtype=np.float32)
-    assert_close(got[rows], want, "x_out rows")
-    assert_close(got[rows] - x[rows], want - x[rows], "delta rows")
+    want = O.block_forward(x, w, seg_tuples(segs), mod, oracle_rope(layout), dtype=np.float32,
+                           attn_chunk=2048)
+    assert_close(got, want, "x_out edit8432")
+    assert_close(got - x, want - x, "delta edit8432")
 
 
 # --------------------------------------------------------------------------
 # stack
 # --------------------------------------------------------------------------
-def _stack_inputs(dims, layout, n_pm, n_joint, seed, distinct_pm=2, distinct_joint=3,
-                  per_block=False):
-    segs = layout.segments()
-    n = layout.n_tokens
-    pm_np = {m: [weights(seed, 100 + 10 * m + (b % distinct_pm), dims) for b in range(n_pm)]
-             for m in range(3)}
-    jt_np = [weights(seed, 200 + (b % distinct_joint), dims) for b in range(n_joint)]
-    x = synth.tokens(seed, n, dims.width)
-    if per_block:
-        m1 = np.stack([synth.modulation(seed, 10 + b, len(segs), dims.width) for b in range(n_pm)])
-        m2 = np.stack([synth.modulation(seed, 100 + b, len(segs), dims.width) for b in range(n_joint)])
-    else:
-        m1 = synth.modulation(seed, 1, len(segs), dims.width)
-        m2 = synth.modulation(seed, 2, len(segs), dims.width)
-    return segs, pm_np, jt_np, x, m1, m2
-
-
 def _run_stack(dims, layout, segs, pm_np, jt_np, x_np, m1, m2, per_block):
     n = x_np.shape[0]
     up = {}
@@ -246,14 +221,25 @@ def test_stack_small_dims_full_depth(per_block):
 
 def test_stack_block336_full_dims():
     """5 + 28 blocks at the model width on the 336-token workload (weights
-    cycle through 2 sets per mode and 3 joint sets)."""
+    cycle through 2 sets per mode and 3 joint sets).  Beside the fp32
+    oracle, the same stack with bf16 rounding at the kernels' storage points
+    and no other error (tests/bf16_emulation.py) gives the floor any bf16
+    implementation sits on; the GPU must land within 1.5 times it."""
+    from bf16_emulation import stack as emulated_stack
     dims = synth.DIMS
     layout = synth.workload("block336").layout
     segs, pm, jt, x, m1, m2 = _stack_inputs(dims, layout, 5, 28, seed=0)
     got = _run_stack(dims, layout, segs, pm, jt, x, m1, m2, False)
-    want = O.stack_forward(x, pm, jt, seg_tuples(segs), m1, m2, oracle_rope(layout),
-                           dtype=np.float32)
+    rope = oracle_rope(layout)
+    want = O.stack_forward(x, pm, jt, seg_tuples(segs), m1, m2, rope, dtype=np.float32)
     assert_close_stack(got, want, x, "stack")
+    emu = emulated_stack(x, pm, jt, seg_tuples(segs), m1, m2, rope)
+    floor = float(np.abs(emu.astype(np.float64) - want).max())
+    err = float(np.abs(got.astype(np.float64) - want).max())
+    gap = float(np.abs(got.astype(np.float64) - emu).max())
+    print(f"[floor] stack336: GPU vs oracle {err:.4e}, bf16 emulation vs oracle {floor:.4e} "
+          f"(ratio {err / floor:.3f}), GPU vs emulation {gap:.4e}")
+    assert err <= 1.5 * floor
 
 
 def test_stack_stage1_streams_independent_on_gpu():

@@ -61,11 +61,23 @@ def _setup(dims, layout, text_dim, n_pm, n_joint, target, seed=9):
     return segs, io, mw, per_mode, joint, text, noise, refs
 
 
-@pytest.mark.parametrize("steps,distilled", [(4, True), (3, False), (1, True)],
-                         ids=["distilled4", "base3", "one_step"])
-def test_sample_matches_oracle(steps, distilled):
-    dims, text_dim = SMALL, 256
-    layout = synth.RopeLayout(80, 8, 8, ((8, 8),))
+_SMALL_EDIT = synth.RopeLayout(80, 8, 8, ((8, 8),))
+SAMPLE_CASES = {
+    # width 256, [80 text | 8x8 image | 8x8 reference], 1 + 1 blocks
+    "distilled4": (SMALL, 256, _SMALL_EDIT, 4, True),
+    "base3": (SMALL, 256, _SMALL_EDIT, 3, False),
+    "one_step": (SMALL, 256, _SMALL_EDIT, 1, True),
+    # the pages' default: 16 distilled steps ("The denoise loop")
+    "distilled16": (SMALL, 256, _SMALL_EDIT, 16, True),
+    # model width 3072 with the 20,480-wide text linear, 80 text + 16x16
+    # image tokens, 1 + 1 blocks, two distilled steps
+    "full_width_distilled2": (synth.DIMS, synth.TEXT_DIM, synth.RopeLayout(80, 16, 16), 2, True),
+}
+
+
+@pytest.mark.parametrize("case", sorted(SAMPLE_CASES))
+def test_sample_matches_oracle(case):
+    dims, text_dim, layout, steps, distilled = SAMPLE_CASES[case]
     segs, io, mw, per_mode, joint, text, noise, refs = _setup(dims, layout, text_dim, 1, 1,
                                                               distilled)
     n = layout.n_tokens
