@@ -211,9 +211,11 @@ def time_whole_calls(F, dims, lay, segs, n, rand, per_mode, joint, emb_w, mod_w,
                     f"{steps} distilled steps (call + Euler step each), shift 6.93"}
 
 
-def cpu_baseline(workload_name):
-    """The oracle, as it stands (NumPy float64), on one joint block of the
-    same workload; value in block tokens/s."""
+def cpu_baseline(workload_name, blocks=2):
+    """The oracle, as it stands, on `blocks` joint blocks of the same
+    workload: NumPy float32 with the BLAS library and the oracle's attention
+    threads on the process's CPU share (at most 16 cores); value in block
+    tokens/s."""
     import numpy as np
     import synth
     from oracle import flux3_oracle as O
@@ -221,18 +223,22 @@ def cpu_baseline(workload_name):
     lay = wl.layout
     n = lay.n_tokens
     segs = [(s.start, s.count, s.mode) for s in lay.segments()]
+    cores = max(1, min(16, len(os.sched_getaffinity(0))))
+    O.THREADS = cores
     w = synth.block_weights(0, 0, synth.DIMS)
     x = synth.tokens(0, n, synth.DIMS.width)
     mod = synth.modulation(0, 0, len(segs), synth.DIMS.width)
     rope = O.rope_tables(O.token_positions(lay.n_text, lay.grid_h, lay.grid_w, lay.refs))
-    t0 = time.perf_counter()
-    y = O.block_forward(x, w, segs, mod, rope)
-    dt = time.perf_counter() - t0
-    assert np.isfinite(y).all()
-    cores = len(os.sched_getaffinity(0))
-    return {"value": n / dt, "unit": "block tokens/s", "cores": cores, "kind": "oracle",
-            "sample": f"one joint block over the {n}-token {workload_name} sequence, "
-                      f"NumPy float64, {dt:.1f} s"}
+    from threadpoolctl import threadpool_limits
+    with threadpool_limits(limits=cores, user_api="blas"):
+        t0 = time.perf_counter()
+        for _ in range(blocks):
+            x = O.block_forward(x, w, segs, mod, rope, dtype=np.float32, attn_chunk=2048)
+        dt = time.perf_counter() - t0
+    assert np.isfinite(x).all()
+    return {"value": blocks * n / dt, "unit": "block tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"{blocks} joint blocks over the {n}-token {workload_name} sequence, "
+                      f"NumPy float32 ({cores} BLAS and attention threads), {dt:.1f} s"}
 
 
 def main():
@@ -251,6 +257,9 @@ def main():
     ap.add_argument("--no-block", action="store_true",
                     help="skip the single-block, whole-call and denoise-loop timings "
                          "(profiling runs of the step alone)")
+    ap.add_argument("--block-only", action="store_true",
+                    help="time the single joint block alone and print its figures "
+                         "(counter runs of the block kernels at one size)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path; run with --gpus 1",
@@ -290,6 +299,11 @@ def main():
         # static weights go to the GEMMs' packed operand layout once, at load
         buf = torch.empty(F.weights_packed_bytes(dims), dtype=torch.uint8, device=dev)
         return F.weights_pack(dims, w, buf)
+
+    if args.block_only:
+        block = time_joint_block(F, dims, lay, segs, n, rand, rand_block)
+        print(json.dumps({"workload": args.workload, "block": block}))
+        return
 
     modes = sorted({s.mode for s in segs})
     per_mode = {m: [rand_block() for _ in range(N_PM)] for m in modes}
@@ -331,6 +345,8 @@ def main():
     t1 = time.perf_counter()
     F.profile_enable(False)
     stats = {k: F.profile_read(k) for k in F.KERNELS}
+    # the joint blocks' launches (all n tokens) apart from the per-stream ones
+    joint_stats = {k: F.profile_read(k, n_tokens=n) for k in ("gemm_proj", "attention", "gemm_out")}
     F.profile_reset()
 
     ms_per_step = (t1 - t0) / args.steps * 1e3
@@ -369,15 +385,33 @@ def main():
     step_flops += 4.0 * D * stats["attention"]["tokens_sq"]
     step_flops /= args.steps
 
-    # dominant kernel: the projection GEMM (the largest FLOP share)
-    gp = stats["gemm_proj"]
+    # dominant kernel: the projection GEMM (the largest FLOP share), over
+    # its launches at the full n tokens (the 28 joint blocks of each step);
+    # the mean over every launch size is given beside it
+    gp = joint_stats["gemm_proj"]
     avg_ms = gp["total_ms"] / max(gp["launches"], 1)
-    flops_per_launch = proj_fpt * gp["tokens"] / max(gp["launches"], 1)
-    achieved = flops_per_launch / (avg_ms * 1e-3) / 1e12
+    achieved = proj_fpt * n / (avg_ms * 1e-3) / 1e12 if avg_ms > 0 else 0.0
+    ga = stats["gemm_proj"]
+    all_avg_ms = ga["total_ms"] / max(ga["launches"], 1)
+    all_achieved = (proj_fpt * ga["tokens"] / max(ga["launches"], 1) / (all_avg_ms * 1e-3) / 1e12
+                    if all_avg_ms > 0 else 0.0)
     roofline = {"bound": "mfma", "kernel": "gemm_proj", "achieved": achieved,
                 "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
                 "traffic": measured_traffic(n),
-                "work_per_launch": f"{proj_fpt / 1e6:.2f} MFLOP/token x {gp['tokens'] / max(gp['launches'], 1):.0f} tokens (mean over stage-1 and stage-2 launches)"}
+                "launches": gp["launches"], "avg_us": 1e3 * avg_ms,
+                "work_per_launch": f"{proj_fpt / 1e6:.2f} MFLOP/token x {n} tokens "
+                                   f"(the joint blocks' launches of the timed steps)",
+                "all_launches": {"launches": ga["launches"], "avg_us": 1e3 * all_avg_ms,
+                                 "mean_tokens": ga["tokens"] / max(ga["launches"], 1),
+                                 "achieved": all_achieved,
+                                 "frac": all_achieved / PEAK_BF16_TFLOPS}}
+    joint = {}
+    for k, st in joint_stats.items():
+        ms = st["total_ms"] / max(st["launches"], 1)
+        fl = (proj_fpt * n if k == "gemm_proj" else out_fpt * n if k == "gemm_out"
+              else 4.0 * D * n * n)
+        joint[k] = {"launches": st["launches"], "avg_us": 1e3 * ms,
+                    "tflops": tflops(fl, ms), "frac_peak": tflops(fl, ms) / PEAK_BF16_TFLOPS}
 
     # single joint block over all tokens (the same segments and layout), and
     # the whole transformer call and denoise loop around the same blocks
@@ -467,6 +501,7 @@ def main():
         "step_frac_peak": step_flops / (ms_per_step * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
         "stack_tokens_per_s": n / (ms_per_step / 1e3),
         "kernels": kern,
+        "joint_launches": joint,
         "block": block,
         "whole_call": whole,
         "peak": peak,

@@ -6,7 +6,7 @@
  *   [P1] "FLUX.3 Image Klein Is Now Available in Diffusers" (15jq.com),
  *        section "Speed, architecture, and how the tokens move".
  *   [P3] Chinese translation of the Diffusers release post (everytik.com):
- *        the block listing `block(x, shift, scale, gate)` and the RoPE
+ *        the block listing (shift, scale and gate arguments) and the RoPE
  *        position table; the modular pipeline's `prepare_rope_inputs` step.
  *   [P4] "How to Run FLUX 3 Image Klein Locally" (rohitghumare.com),
  *        sections "Inside the transformer", "The latent space and the VAE".
@@ -448,8 +448,13 @@ flux3_status flux3_sample(const flux3_dims *dims, const flux3_io_dims *io_dims,
  * one kernel kind, the number of launches, their summed duration in
  * milliseconds, and the summed token count M and M^2 of those launches (the
  * units the kernels' algorithmic work is counted in).  flux3_profile_reset
- * drops all records.  Recording allocates HIP events on the host side; the
- * facility is not thread-safe and is off by default. */
+ * waits for and drops all records.  Records belong to the calling thread:
+ * enable, the profiled calls, read and reset must come from one thread, and
+ * other threads are unaffected.  Off by default.
+ * This facility is the one exception to the library keeping nothing across
+ * calls: while profiling is on, every launch creates two HIP events (host
+ * runtime objects, no device buffers), held in the thread's records until
+ * flux3_profile_reset destroys them. */
 enum {
   FLUX3_K_ROPE_TABLES = 0,
   FLUX3_K_LN_MODULATE = 1,
@@ -473,6 +478,11 @@ void flux3_profile_reset(void);
 /* FLUX3_E_INVALID for a bad kind or NULL out; FLUX3_E_HIP if an event
  * cannot be read. */
 flux3_status flux3_profile_read(int32_t kernel, flux3_kernel_stats *out);
+/* As flux3_profile_read, over the launches of that kind whose token count
+ * M equals n_tokens (a block's joint launches apart from its per-stream
+ * ones, say).  FLUX3_E_SHAPE for a negative n_tokens. */
+flux3_status flux3_profile_read_tokens(int32_t kernel, int64_t n_tokens,
+                                       flux3_kernel_stats *out);
 
 /* What the kernels run on: compute units and shader clock of a HIP device,
  * its architecture name, and the dense bf16 MFMA peak those imply for the

@@ -9,7 +9,8 @@ import ctypes
 import os
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libflux3.so")
+# FLUX3_LIB names another build of the library (the sanitizer check uses it)
+LIB_PATH = os.environ.get("FLUX3_LIB") or os.path.join(HERE, "libflux3.so")
 
 FLUX3_OK = 0
 STATUS_NAMES = {0: "FLUX3_OK", -1: "FLUX3_E_INVALID", -2: "FLUX3_E_SHAPE",
@@ -27,6 +28,7 @@ EXPORTS = ("flux3_layout_tokens", "flux3_rope_tables_build", "flux3_workspace_by
            "flux3_sigmas", "flux3_euler_step", "flux3_sample_workspace_bytes", "flux3_sample",
            "flux3_modulation_workspace_bytes", "flux3_modulation_forward",
            "flux3_profile_enable", "flux3_profile_reset", "flux3_profile_read",
+           "flux3_profile_read_tokens",
            "flux3_device_query", "flux3_set_debug_sync", "flux3_status_string",
            "flux3_last_error_detail")
 KERNELS = ("rope_tables", "ln_modulate", "gemm_proj", "attention", "gemm_out", "modulation",
@@ -161,6 +163,8 @@ def load(path=LIB_PATH):
     lib.flux3_profile_reset.restype = None
     lib.flux3_profile_read.argtypes = [i32, P(KernelStats)]
     lib.flux3_profile_read.restype = i32
+    lib.flux3_profile_read_tokens.argtypes = [i32, i64, P(KernelStats)]
+    lib.flux3_profile_read_tokens.restype = i32
     lib.flux3_device_query.argtypes = [i32, P(DeviceInfo)]
     lib.flux3_device_query.restype = i32
     lib.flux3_set_debug_sync.argtypes = [i32]
@@ -466,12 +470,16 @@ def profile_reset():
     load().flux3_profile_reset()
 
 
-def profile_read(kernel):
+def profile_read(kernel, n_tokens=None):
     """Stats for one kernel kind (name from KERNELS or its index): dict with
-    launches, total_ms, tokens (sum of M), tokens_sq (sum of M^2)."""
+    launches, total_ms, tokens (sum of M), tokens_sq (sum of M^2); with
+    n_tokens, over the launches with M == n_tokens only."""
     idx = KERNELS.index(kernel) if isinstance(kernel, str) else int(kernel)
     out = KernelStats()
-    _check(load().flux3_profile_read(idx, ctypes.byref(out)))
+    if n_tokens is None:
+        _check(load().flux3_profile_read(idx, ctypes.byref(out)))
+    else:
+        _check(load().flux3_profile_read_tokens(idx, n_tokens, ctypes.byref(out)))
     return {"launches": out.launches, "total_ms": out.total_ms, "tokens": out.tokens,
             "tokens_sq": out.tokens_sq}
 

@@ -20,22 +20,18 @@ namespace {
 thread_local char g_detail[512] = "";
 int g_debug_sync = 0;
 
-// kernel timing records (flux3_profile_*)
+// Kernel timing records (flux3_profile_*), kept per calling thread.  The
+// HIP events of a record are created when its launch is enqueued with
+// profiling on, and destroyed by flux3_profile_reset on the same thread.
 struct ProfRec {
   int kind;
   hipEvent_t a, b;
   double m;
 };
-bool g_prof_on = false;
-std::vector<ProfRec> g_prof;
-std::vector<hipEvent_t> g_event_pool;
+thread_local bool g_prof_on = false;
+thread_local std::vector<ProfRec> g_prof;
 
-hipEvent_t pool_event() {
-  if (!g_event_pool.empty()) {
-    hipEvent_t e = g_event_pool.back();
-    g_event_pool.pop_back();
-    return e;
-  }
+hipEvent_t new_event() {
   hipEvent_t e = nullptr;
   if (hipEventCreate(&e) != hipSuccess) return nullptr;
   return e;
@@ -44,9 +40,12 @@ hipEvent_t pool_event() {
 // Records the start event of a launch when profiling; returns its index.
 int prof_begin(int kind, double m, hipStream_t s) {
   if (!g_prof_on) return -1;
-  ProfRec r{kind, pool_event(), pool_event(), m};
-  if (!r.a || !r.b) return -1;
-  if (hipEventRecord(r.a, s) != hipSuccess) return -1;
+  ProfRec r{kind, new_event(), new_event(), m};
+  if (!r.a || !r.b || hipEventRecord(r.a, s) != hipSuccess) {
+    if (r.a) (void)hipEventDestroy(r.a);
+    if (r.b) (void)hipEventDestroy(r.b);
+    return -1;
+  }
   g_prof.push_back(r);
   return (int)g_prof.size() - 1;
 }
@@ -987,18 +986,21 @@ void flux3_profile_enable(int32_t on) { g_prof_on = on != 0; }
 void flux3_profile_reset(void) {
   for (const ProfRec& r : g_prof) {
     (void)hipEventSynchronize(r.b);
-    g_event_pool.push_back(r.a);
-    g_event_pool.push_back(r.b);
+    (void)hipEventDestroy(r.a);
+    (void)hipEventDestroy(r.b);
   }
   g_prof.clear();
 }
 
-flux3_status flux3_profile_read(int32_t kernel, flux3_kernel_stats* out) {
+namespace {
+// Stats of the records of one kind, those with token count m only when
+// m >= 0.
+flux3_status profile_stats(int32_t kernel, int64_t m, flux3_kernel_stats* out) {
   if (!out) return fail(FLUX3_E_INVALID, "out is NULL");
   if (kernel < 0 || kernel >= FLUX3_K_COUNT) return fail(FLUX3_E_INVALID, "kernel kind %d", kernel);
   flux3_kernel_stats st = {0, 0.0, 0.0, 0.0};
   for (const ProfRec& r : g_prof) {
-    if (r.kind != kernel) continue;
+    if (r.kind != kernel || (m >= 0 && r.m != (double)m)) continue;
     hipError_t e = hipEventSynchronize(r.b);
     float ms = 0.f;
     if (e == hipSuccess) e = hipEventElapsedTime(&ms, r.a, r.b);
@@ -1010,6 +1012,17 @@ flux3_status flux3_profile_read(int32_t kernel, flux3_kernel_stats* out) {
   }
   *out = st;
   return ok();
+}
+}  // namespace
+
+flux3_status flux3_profile_read(int32_t kernel, flux3_kernel_stats* out) {
+  return profile_stats(kernel, -1, out);
+}
+
+flux3_status flux3_profile_read_tokens(int32_t kernel, int64_t n_tokens,
+                                       flux3_kernel_stats* out) {
+  if (n_tokens < 0) return fail(FLUX3_E_SHAPE, "n_tokens %lld is negative", (long long)n_tokens);
+  return profile_stats(kernel, n_tokens, out);
 }
 
 const char* flux3_status_string(flux3_status s) {

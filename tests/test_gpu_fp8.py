@@ -8,7 +8,11 @@ the bf16 bar (max-abs 3e-2, cosine 0.9995) against block_forward_fp8: the
 oracle quantises its fp64 h and [o | act], the kernels their fp32 h and
 bf16 [o | act], so a code can differ by one step where a value lies next to
 a rounding boundary, and the fp8 matrix cores sum with a narrower adder
-than fp32 (a few 2^-12 of the largest product of a group)."""
+than fp32 (a few 2^-12 of the largest product of a group).  Over the
+full-width 33-block stack those flipped codes compound: that test is held to
+the oracle's own float32-against-float64 spread on the same stack."""
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -272,7 +276,22 @@ def test_stack336_full_width():
     jt_o = [oracle_fp8(w) for w in jt_np]
     want = O.stack_forward(x_np, pm_o, jt_o, seg_tuples(segs), m1, m2, oracle_rope(layout),
                            dtype=np.float32, block_fn=O.block_forward_fp8)
-    assert_close_stack(got, want, x_np, "fp8 stack336 full width")
+    # The bar is the oracle's own spread on this stack (float32 against
+    # float64, tests/golden/fp8_stack336_spread.txt): quantisation codes
+    # flip with the last bits of the sums before them and the flips compound
+    # over 33 blocks, so a correct FP8 stack summed in another order lands
+    # about that far away.  The GPU must stay within 1.5 times the spread;
+    # the stack without FP8 weights is more than twice as far.
+    spread = {}
+    with open(os.path.join(os.path.dirname(__file__), "golden", "fp8_stack336_spread.txt")) as f:
+        for line in f:
+            if line.strip() and not line.startswith("#"):
+                k, v = line.split()
+                spread[k] = float(v)
+    assert_close(got, want, "fp8 stack336 full width x_out",
+                 maxabs_tol=1.5 * spread["maxabs"], cos_tol=1 - 1.5 * (1 - spread["cos_x"]))
+    assert_close(got - x_np, want - x_np, "fp8 stack336 full width delta",
+                 maxabs_tol=1.5 * spread["maxabs"], cos_tol=1 - 1.5 * (1 - spread["cos_delta"]))
 
 
 def test_block_4k_sampled_rows():
