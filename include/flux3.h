@@ -17,7 +17,10 @@
  *   - Device pointers are caller-owned HIP device memory; the library never
  *     allocates, frees or keeps any of them past the call.  Host pointers
  *     (segment lists, weight-struct arrays, layout arrays, dims) are read
- *     during the call only.
+ *     during the call only.  The library allocates nothing and keeps
+ *     nothing across calls, with two stated exceptions: the fixed per-GPU
+ *     array of flux3_block_forward_noalloc, and the HIP events of the
+ *     opt-in kernel timing (flux3_profile_*).
  *   - `stream` is a hipStream_t passed as void*; NULL means the default
  *     stream.  Calls only enqueue work and return; results are ready after
  *     the caller synchronises that stream.
@@ -242,6 +245,28 @@ flux3_status flux3_block_forward(const flux3_dims *dims,
                                  int32_t n_segs, const float *mod,
                                  const float *rope, void *workspace,
                                  size_t workspace_bytes, void *stream);
+
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * block of flux3_block_forward with the same arguments minus the
+ * workspace.  Its intermediates (h, q, k, v^T, [o | act]) live in a device
+ * array of FLUX3_NOALLOC_SCRATCH_BYTES bytes inside the library, one copy
+ * per GPU, held from the first call on that GPU until the process ends;
+ * the call itself allocates nothing.  n_tokens is limited to what fits --
+ * 1024 tokens at width 3072, hidden 9216 -- and a larger call returns
+ * FLUX3_E_WORKSPACE having enqueued nothing.  There is no split-partial
+ * region, so the output GEMM and attention run every tile whole: slower
+ * for small n_tokens than flux3_block_forward, and equal to it up to the
+ * order of fp32 sums.  Calls that overlap on one GPU share the array and
+ * race: serialise them (one stream, or events between streams).  The
+ * first call on a device looks up the array's address there and returns
+ * FLUX3_E_HIP if that fails.  Other errors as for flux3_block_forward. */
+#define FLUX3_NOALLOC_SCRATCH_BYTES (48u * 1024u * 1024u)
+flux3_status flux3_block_forward_noalloc(const flux3_dims *dims,
+                                         const flux3_block_weights *w, float *x,
+                                         int64_t n_tokens, const flux3_segment *segs,
+                                         int32_t n_segs, const float *mod,
+                                         const float *rope, void *stream);
 
 /* The two-stage stack [P1; P4 "Inside the transformer"]:
  * stage 1 runs, for every segment s, the n_pm per-mode blocks of its mode

@@ -6,7 +6,8 @@ binding with the same entry-point names.
 """
 from ._lib import (Flux3Error, Dims, Segment, BlockWeights, RopeLayout, WorkspaceLayout,
                    load, layout_tokens, rope_tables_build, workspace_bytes, workspace_layout,
-                   block_forward, stack_forward, set_debug_sync, status_string, EXPORTS,
+                   block_forward, block_forward_noalloc, NOALLOC_SCRATCH_BYTES, stack_forward,
+                   set_debug_sync, status_string, EXPORTS,
                    LIB_PATH, KERNELS, profile_enable, profile_reset, profile_read,
                    device_query, modulation_workspace_bytes, modulation_forward,
                    ModulationWeights, weights_packed_bytes, weights_pack, WEIGHTS_LINEAR,
@@ -16,7 +17,8 @@ from ._lib import (Flux3Error, Dims, Segment, BlockWeights, RopeLayout, Workspac
 
 __all__ = ["Flux3Error", "Dims", "Segment", "BlockWeights", "RopeLayout", "WorkspaceLayout",
            "load", "layout_tokens", "rope_tables_build", "workspace_bytes", "workspace_layout",
-           "block_forward", "stack_forward", "set_debug_sync", "status_string", "EXPORTS",
+           "block_forward", "block_forward_noalloc", "NOALLOC_SCRATCH_BYTES", "stack_forward",
+           "set_debug_sync", "status_string", "EXPORTS",
            "LIB_PATH", "KERNELS", "profile_enable", "profile_reset", "profile_read",
            "device_query", "modulation_workspace_bytes", "modulation_forward",
            "ModulationWeights", "weights_packed_bytes", "weights_pack", "WEIGHTS_LINEAR",

@@ -18,10 +18,12 @@ STATUS_NAMES = {0: "FLUX3_OK", -1: "FLUX3_E_INVALID", -2: "FLUX3_E_SHAPE",
                 -5: "FLUX3_E_WORKSPACE", -6: "FLUX3_E_HIP"}
 MAX_SEGMENTS = 16
 MAX_REFS = 15
+NOALLOC_SCRATCH_BYTES = 48 * 1024 * 1024   # FLUX3_NOALLOC_SCRATCH_BYTES
 
 # exported symbols, in the order include/flux3.h declares them
 EXPORTS = ("flux3_layout_tokens", "flux3_rope_tables_build", "flux3_workspace_bytes",
-           "flux3_workspace_layout_get", "flux3_block_forward", "flux3_stack_forward",
+           "flux3_workspace_layout_get", "flux3_block_forward", "flux3_block_forward_noalloc",
+           "flux3_stack_forward",
            "flux3_weights_packed_bytes", "flux3_weights_pack",
            "flux3_weights_fp8r_bytes", "flux3_weights_quantize_fp8r",
            "flux3_transformer_workspace_bytes", "flux3_transformer_forward",
@@ -123,6 +125,9 @@ def load(path=LIB_PATH):
     lib.flux3_block_forward.argtypes = [P(Dims), P(BlockWeights), vp, i64, P(Segment), i32,
                                         vp, vp, vp, sz, vp]
     lib.flux3_block_forward.restype = i32
+    lib.flux3_block_forward_noalloc.argtypes = [P(Dims), P(BlockWeights), vp, i64, P(Segment),
+                                                i32, vp, vp, vp]
+    lib.flux3_block_forward_noalloc.restype = i32
     lib.flux3_stack_forward.argtypes = [P(Dims), P(BlockWeights), i32, P(BlockWeights), i32,
                                         vp, i64, P(Segment), i32, vp, vp, i64, vp, vp, sz, vp]
     lib.flux3_stack_forward.restype = i32
@@ -316,6 +321,19 @@ def block_forward(dims, w, x, segs, mod, rope, workspace, n_tokens=None,
     _check(load().flux3_block_forward(ctypes.byref(make_dims(dims)), ctypes.byref(W), _ptr(x),
                                       n_tokens, seg_arr, n_segs, _ptr(mod), _ptr(rope),
                                       _ptr(workspace), workspace_nbytes, _stream_handle(stream)))
+
+
+def block_forward_noalloc(dims, w, x, segs, mod, rope, n_tokens=None, stream=None):
+    """flux3_block_forward_noalloc: one block in place on x [N][D] fp32 with
+    the library's own fixed intermediates (no workspace; N limited to what
+    NOALLOC_SCRATCH_BYTES holds)."""
+    seg_arr, n_segs = make_segments(segs)
+    W = make_weights(w)
+    if n_tokens is None:
+        n_tokens = x.shape[0]
+    _check(load().flux3_block_forward_noalloc(ctypes.byref(make_dims(dims)), ctypes.byref(W),
+                                              _ptr(x), n_tokens, seg_arr, n_segs, _ptr(mod),
+                                              _ptr(rope), _stream_handle(stream)))
 
 
 def stack_forward(dims, per_mode, joint, x, segs, mod_stage1, mod_stage2, rope, workspace,

@@ -33,7 +33,7 @@ HOST_SANITIZE = ["-Xarch_host", "-fsanitize=address,undefined", "-Xarch_host", "
                  "-Xarch_host", "-g"]
 
 SOURCES = ["rope.hip", "ln_modulate.hip", "gemm.hip", "attention.hip", "modulation.hip", "quant.hip",
-           "sampler.hip", "abi.cpp"]
+           "sampler.hip", "noalloc.hip", "abi.cpp"]
 
 
 def _compile(src, defines=(), build_dir=BUILD, extra=()):

@@ -13,6 +13,7 @@
 #include <vector>
 
 #include "../../include/flux3.h"
+#include "abi_internal.hpp"
 #include "kernels.hpp"
 
 namespace {
@@ -220,12 +221,16 @@ flux3_status after_launch(hipError_t e, const char* what, hipStream_t s) {
 }
 
 // Enqueue one block on rows [0, n) of x (already validated).
+// With split false the workspace has no split-partial region (only the
+// buffers before `part`); the output GEMM and attention then run their
+// leftover tiles whole instead of splitting them.
 flux3_status run_block(const flux3_dims* d, const flux3_block_weights& w, float* x, int64_t n,
                        const flux3::SegTableHost& st, const float* mod, const float* rope,
-                       void* ws, hipStream_t s) {
+                       void* ws, hipStream_t s, bool split = true) {
   flux3_workspace_layout L;
   layout_of(d, n, &L);
   flux3::WsPtrs wp = carve(ws, L);
+  if (!split) wp.part = nullptr;
   const flux3::BlockWeightsDev wd = dev_weights(w);
   if (wd.fp8) {
     // h's codes and scales in h's buffer (dead until the next block's K1);
@@ -454,6 +459,51 @@ flux3_status io_linear(const void* a_packed, const void* w, bool w_packed, int64
 
 }  // namespace
 
+// Entry points defined in other source files share these (abi_internal.hpp).
+namespace flux3 {
+
+flux3_status validate_block(const flux3_dims* dims, const flux3_block_weights* w, const float* x,
+                            int64_t n_tokens, const flux3_segment* segs, int32_t n_segs,
+                            const float* mod, const float* rope, SegTableHost* st) {
+  flux3_status r = check_dims(dims);
+  if (r != FLUX3_OK) return r;
+  if (n_tokens < 0 || n_tokens > kMaxTokens)
+    return fail(FLUX3_E_SHAPE, "n_tokens %lld outside [0, %lld]", (long long)n_tokens, (long long)kMaxTokens);
+  if (n_tokens == 0) {
+    if (n_segs != 0) return fail(FLUX3_E_SHAPE, "n_tokens is 0 but n_segs is %d", n_segs);
+    return ok();
+  }
+  if ((r = check_weights(w, "w", 0, dims)) != FLUX3_OK) return r;
+  if (!x || !mod || !rope) return fail(FLUX3_E_INVALID, "x, mod or rope is NULL");
+  if (!aligned16(x) || !aligned16(mod) || !aligned16(rope))
+    return fail(FLUX3_E_ALIGN, "x, mod or rope is not 16-byte aligned");
+  return check_segments(segs, n_segs, n_tokens, st);
+}
+
+size_t block_buffer_bytes(const flux3_dims* dims, int64_t n_tokens) {
+  flux3_workspace_layout L;
+  layout_of(dims, n_tokens, &L);
+  return L.part;
+}
+
+flux3_status run_block_whole_tiles(const flux3_dims* dims, const flux3_block_weights* w, float* x,
+                                   int64_t n_tokens, const SegTableHost& st, const float* mod,
+                                   const float* rope, void* buffers, void* stream) {
+  flux3_status r = run_block(dims, *w, x, n_tokens, st, mod, rope, buffers,
+                             static_cast<hipStream_t>(stream), /*split=*/false);
+  return r == FLUX3_OK ? ok() : r;
+}
+
+flux3_status set_error(flux3_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_detail, sizeof g_detail, fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+}  // namespace flux3
+
 extern "C" {
 
 int64_t flux3_layout_tokens(const flux3_rope_layout* L) {
@@ -635,20 +685,9 @@ flux3_status flux3_block_forward(const flux3_dims* dims, const flux3_block_weigh
                                  int64_t n_tokens, const flux3_segment* segs, int32_t n_segs,
                                  const float* mod, const float* rope, void* workspace,
                                  size_t workspace_bytes, void* stream) {
-  flux3_status r = check_dims(dims);
-  if (r != FLUX3_OK) return r;
-  if (n_tokens < 0 || n_tokens > kMaxTokens)
-    return fail(FLUX3_E_SHAPE, "n_tokens %lld outside [0, %lld]", (long long)n_tokens, (long long)kMaxTokens);
-  if (n_tokens == 0) {
-    if (n_segs != 0) return fail(FLUX3_E_SHAPE, "n_tokens is 0 but n_segs is %d", n_segs);
-    return ok();
-  }
-  if ((r = check_weights(w, "w", 0, dims)) != FLUX3_OK) return r;
-  if (!x || !mod || !rope) return fail(FLUX3_E_INVALID, "x, mod or rope is NULL");
-  if (!aligned16(x) || !aligned16(mod) || !aligned16(rope))
-    return fail(FLUX3_E_ALIGN, "x, mod or rope is not 16-byte aligned");
   flux3::SegTableHost st;
-  if ((r = check_segments(segs, n_segs, n_tokens, &st)) != FLUX3_OK) return r;
+  flux3_status r = flux3::validate_block(dims, w, x, n_tokens, segs, n_segs, mod, rope, &st);
+  if (r != FLUX3_OK || n_tokens == 0) return r;
   flux3_workspace_layout L;
   if ((r = check_ws(dims, n_tokens, workspace, workspace_bytes, &L)) != FLUX3_OK) return r;
   r = run_block(dims, *w, x, n_tokens, st, mod, rope, workspace, static_cast<hipStream_t>(stream));

@@ -618,9 +618,10 @@ hipError_t launch_attention(const BlockShape& bs, const WsPtrs& ws, hipStream_t 
   p.groups = G;
   p.dp_rounds = units / G;
   p.tail = units % G;
-  // a tail filling most of a round runs whole; a thin one has its key tiles
-  // spread over up to G ranges of at least 4 tiles each
-  if (p.tail * 10 > G * 7) {
+  // a tail filling most of a round runs whole (as does every tail without a
+  // partial-slot region, ws.part null); a thin one has its key tiles spread
+  // over up to G ranges of at least 4 tiles each
+  if (p.tail * 10 > G * 7 || ws.part == nullptr) {
     p.dp_rounds += 1;
     p.tail = 0;
   }

@@ -1246,7 +1246,8 @@ hipError_t launch_gemm_out(const BlockShape& bs, const BlockWeightsDev& w,
   // prefers whole
   // tiles from about half a round (8432 tokens: 328 split, 310 whole).
   const int split_pct = w.fp8 ? 45 : 78;
-  if (p.tail * 100 >= G * split_pct) {
+  // without a partial-slot region (ws.part null) every tile runs whole
+  if (p.tail * 100 >= G * split_pct || ws.part == nullptr) {
     p.dp_rounds += 1;
     p.tail = 0;
   }

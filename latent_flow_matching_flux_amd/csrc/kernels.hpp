@@ -31,7 +31,8 @@ struct WsPtrs {
   void* k;    // bf16 [H][n_pad][128]
   void* vt;   // bf16 [H][128][n_pad]
   void* cat;  // bf16 [n_pad][D + F]
-  void* part; // fp32 [2 kMaxSplitGroups][256 * 256]: split-tile partials of K4
+  void* part; // fp32 [2 kMaxSplitGroups][256 * 256]: split-tile partials of K4 and K3;
+              // null: no such region, the split kernels run every tile whole
   // rowwise-fp8 blocks only (packed e4m3 codes, fp32 row scales); they live in
   // buffers that are dead at the time: h8 / sh from K1 to K2, cat8 / scat from
   // the cat quantisation to K4 (over h, q, k, vt once attention is done)

@@ -134,6 +134,27 @@ def test_block_sizes_and_workspace():
     assert _call_block(n=0, segs=((0, 1, 0),)) == E_SHAPE
 
 
+def test_block_noalloc_validation():
+    """The allocation-free block validates like flux3_block_forward and
+    rejects sizes beyond its array before touching a device."""
+    lib = F.load()
+    d = _dims()
+    seg_arr, n_segs = L.make_segments([(0, 80, 0), (80, 256, 1)])
+    def call(n=336, segs=(seg_arr, n_segs), x=FAKE, w=None):
+        return lib.flux3_block_forward_noalloc(ctypes.byref(d), ctypes.byref(w or _w()), x, n,
+                                               segs[0], segs[1], FAKE, FAKE, 0)
+    assert call(x=None) == E_INVALID
+    assert call(x=FAKE + 4) == E_ALIGN
+    assert call(n=337) == E_SHAPE
+    big = L.make_segments([(0, 1025, 0)])
+    assert call(n=1025, segs=big) == E_WORKSPACE
+    assert b"1025" in lib.flux3_last_error_detail()
+    assert call(n=0, segs=L.make_segments([])) == OK
+    # the array holds exactly the 1024-token intermediates at the model dims
+    assert F.workspace_layout(synth.DIMS, 1024).part == L.NOALLOC_SCRATCH_BYTES
+    assert F.workspace_layout(synth.DIMS, 1025).part > L.NOALLOC_SCRATCH_BYTES
+
+
 def test_rope_build_validation():
     lib = F.load()
     lay = L.make_layout(synth.workload("block336").layout)
