@@ -405,12 +405,12 @@ def main():
                                  "mean_tokens": ga["tokens"] / max(ga["launches"], 1),
                                  "achieved": all_achieved,
                                  "frac": all_achieved / PEAK_BF16_TFLOPS}}
-    joint = {}
+    joint_rates = {}
     for k, st in joint_stats.items():
         ms = st["total_ms"] / max(st["launches"], 1)
         fl = (proj_fpt * n if k == "gemm_proj" else out_fpt * n if k == "gemm_out"
               else 4.0 * D * n * n)
-        joint[k] = {"launches": st["launches"], "avg_us": 1e3 * ms,
+        joint_rates[k] = {"launches": st["launches"], "avg_us": 1e3 * ms,
                     "tflops": tflops(fl, ms), "frac_peak": tflops(fl, ms) / PEAK_BF16_TFLOPS}
 
     # single joint block over all tokens (the same segments and layout), and
@@ -501,7 +501,7 @@ def main():
         "step_frac_peak": step_flops / (ms_per_step * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
         "stack_tokens_per_s": n / (ms_per_step / 1e3),
         "kernels": kern,
-        "joint_launches": joint,
+        "joint_launches": joint_rates,
         "block": block,
         "whole_call": whole,
         "peak": peak,

@@ -23,10 +23,12 @@
 // their use, one workgroup barrier per tile.
 //
 // Online softmax with lazy rescaling: scores are kept in the log2 domain
-// (log2(e)/sqrt(128) folded into one FMA with the max); the reference max of
-// a query only moves -- and O and the running sum are only rescaled -- when
-// a tile's max exceeds it by more than TAU, so exp2(s - m) <= 2^TAU and fp32
-// / bf16 never overflow.  Keys past the sequence end are masked in the last
+// (log2(e)/sqrt(128) folded into one FMA with the reference); a tile's
+// probabilities are taken against a query's current reference max, and
+// only when some lane's sum of them exceeds 2^TAU is the tile's own max
+// taken, the reference moved and O and the running sum rescaled -- so every
+// exp2(s - m) stays <= 2^TAU and fp32 / bf16 never overflow, and most tiles
+// need no max at all.  Keys past the sequence end are masked in the last
 // tile (the workspace pads them with zeros).
 #include <algorithm>
 #include <type_traits>
@@ -173,16 +175,34 @@ __device__ __forceinline__ void pin(T& v) {
 struct SoftState {
   float m_ref;   // reference max, log2 domain
   float l_sum;   // running sum of the bf16-rounded exp2(s - m_ref) over this lane's keys
-  float alpha;   // factor O must take before the next PV (1 if m_ref held)
-  bool moved;    // wave-uniform: m_ref moved in the last softmax
+  bool moved;    // wave-uniform: the last softmax region left its tile to settle()
 };
+
+constexpr float kTauExp = 256.0f;   // 2^TAU
+
+// Score idx (key block idx / 16, register idx % 16) of this lane's query in
+// a tile: keys past the sequence end are -inf under MASK.
+template <bool MASK>
+__device__ __forceinline__ float score(const STile& Sc, int idx, int key0, int M, int hh) {
+  const int kb = idx >> 4, e = idx & 15;
+  float s = Sc[kb][e];
+  if constexpr (MASK) {
+    const int jk = key0 + kb * 32 + 8 * (e >> 2) + 4 * hh + (e & 3);
+    s = jk < M ? s : -INFINITY;
+  }
+  return s;
+}
 
 // One tile's worth of pipelined work, in 32 slots.  Even slot 2j: QK^T
 // MFMA j of tile t+1 (k-step j/2, key block j%2) into Sn; odd slot 2j+1: PV
 // MFMA j of tile t-1 (key block j/8, 16-key half (j/4)%2, dim block j%4)
 // with probabilities Pp.  Softmax of tile t (scores Sc -> Pc) rides along:
-// slots 0-7 take the max, slot 8 moves the reference, slots 9-24 take two
-// exponentials each, slot 25 closes the sum.
+// slots 0-15 take two exponentials each against the current reference,
+// slot 16 checks them.  Every exp2(s - m_ref) is bounded by the lane's sum
+// of them, so while that sum stays within 2^TAU no probability exceeds
+// 2^TAU and the tile needs no max; otherwise (or on NaN: the first tile,
+// where m_ref is still -inf) `moved` is set and settle() redoes the tile
+// against its true max after the region.
 template <bool QK, bool PV, bool SM, bool MASK>
 __device__ __forceinline__ void region(STile& Sn, uint32_t k_off, f32x16 (&o)[4], uint32_t v_off,
                                        const PTile& Pp, const STile& Sc, PTile& Pc, SoftState& st,
@@ -208,18 +228,7 @@ __device__ __forceinline__ void region(STile& Sn, uint32_t k_off, f32x16 (&o)[4]
   };
   static_for<0, PREFETCH>(load);
 
-  float vals[32];
-  float m = -INFINITY, l = 0.f;
-  auto val = [&](int idx) -> float {
-    const int kb = idx >> 4, e = idx & 15;
-    float s = Sc[kb][e];
-    if constexpr (MASK) {
-      const int jk = key0 + kb * 32 + 8 * (e >> 2) + 4 * hh + (e & 3);
-      s = jk < M ? s : -INFINITY;
-    }
-    return s;
-  };
-
+  float l = 0.f;
   static_for<0, 32>([&](auto ic) {
     constexpr int i = decltype(ic)::value;
     constexpr int j = i / 2;
@@ -236,36 +245,22 @@ __device__ __forceinline__ void region(STile& Sn, uint32_t k_off, f32x16 (&o)[4]
     }
     if constexpr (i + PREFETCH < 32) load(std::integral_constant<int, i + PREFETCH>{});
     if constexpr (SM) {
-      if constexpr (i < 8) {
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          vals[4 * i + u] = val(4 * i + u);
-          m = fmaxf(m, vals[4 * i + u]);
-        }
-      } else if constexpr (i == 8) {
-        m *= scale;
-        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m),
-                                                         false, false);
-        const float mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
-        st.moved = __any(mx > st.m_ref + TAU);
-        const float m_new = st.moved ? fmaxf(st.m_ref, mx) : st.m_ref;
-        st.alpha = __builtin_amdgcn_exp2f(st.m_ref - m_new);
-        st.m_ref = m_new;
-        st.l_sum *= st.alpha;
-      } else if constexpr (i >= 9 && i <= 24) {
-        constexpr int idx = 2 * (i - 9);
+      if constexpr (i < 16) {
+        constexpr int idx = 2 * i;
         f32x2 pp;
 #pragma unroll
         for (int u = 0; u < 2; ++u)
-          pp[u] = __builtin_amdgcn_exp2f(__builtin_fmaf(vals[idx + u], scale, -st.m_ref));
+          pp[u] = __builtin_amdgcn_exp2f(
+              __builtin_fmaf(score<MASK>(Sc, idx + u, key0, M, hh), scale, -st.m_ref));
         const bf16x2 pb = __builtin_convertvector(pp, bf16x2);
         // the running sum takes the bf16 probabilities the PV product uses
         l = __builtin_amdgcn_fdot2_f32_bf16(pb, kOnes2, l, false);
         uint32_t w = __builtin_bit_cast(uint32_t, pb);
         pin(w);
         Pc[idx >> 4][(idx >> 3) & 1][(idx & 7) >> 1] = w;
-      } else if constexpr (i == 25) {
-        st.l_sum += l;
+      } else if constexpr (i == 16) {
+        st.moved = __any(!(l <= kTauExp));
+        st.l_sum += st.moved ? 0.f : l;
         pin(st.l_sum);
       }
     }
@@ -273,13 +268,41 @@ __device__ __forceinline__ void region(STile& Sn, uint32_t k_off, f32x16 (&o)[4]
   });
 }
 
-__device__ __forceinline__ void rescale(f32x16 (&o)[4], const SoftState& st) {
-  if (st.moved) {
+// After a softmax region that set `moved`: the tile's max (over both lanes
+// of each query) becomes the reference when it is above the current one,
+// O and the running sum are rescaled by 2^(old - new), and the tile's
+// probabilities and sum are taken again against it.
+template <bool MASK>
+__device__ __forceinline__ void settle(f32x16 (&o)[4], SoftState& st, const STile& Sc, PTile& Pc,
+                                       float scale, int key0, int M, int lane) {
+  if (!st.moved) return;
+  const int hh = lane >> 5;
+  float m = -INFINITY;
 #pragma unroll
-    for (int d = 0; d < 4; ++d)
+  for (int idx = 0; idx < 32; ++idx) m = fmaxf(m, score<MASK>(Sc, idx, key0, M, hh));
+  m *= scale;
+  const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m),
+                                                   false, false);
+  const float m_new = fmaxf(st.m_ref, fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])));
+  const float alpha = __builtin_amdgcn_exp2f(st.m_ref - m_new);
+  st.m_ref = m_new;
+  float l = 0.f;
 #pragma unroll
-      for (int e = 0; e < 16; ++e) o[d][e] *= st.alpha;
+  for (int idx = 0; idx < 32; idx += 2) {
+    f32x2 pp;
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+      pp[u] = __builtin_amdgcn_exp2f(
+          __builtin_fmaf(score<MASK>(Sc, idx + u, key0, M, hh), scale, -m_new));
+    const bf16x2 pb = __builtin_convertvector(pp, bf16x2);
+    l = __builtin_amdgcn_fdot2_f32_bf16(pb, kOnes2, l, false);
+    Pc[idx >> 4][(idx >> 3) & 1][(idx & 7) >> 1] = __builtin_bit_cast(uint32_t, pb);
   }
+  st.l_sum = st.l_sum * alpha + l;
+#pragma unroll
+  for (int d = 0; d < 4; ++d)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) o[d][e] *= alpha;
 }
 
 // Attention of one unit (head, query block qblk) over key tiles
@@ -322,7 +345,7 @@ __device__ __forceinline__ void attend(const AttnArgs& p, const lds_u8* smem, ui
   for (int d = 0; d < 4; ++d)
 #pragma unroll
     for (int e = 0; e < 16; ++e) o[d][e] = 0.f;
-  SoftState st{-INFINITY, 0.f, 1.f, false};
+  SoftState st{-INFINITY, 0.f, false};
   STile S0, S1;
   PTile P0, P1;
 
@@ -345,36 +368,36 @@ __device__ __forceinline__ void attend(const AttnArgs& p, const lds_u8* smem, ui
   top(0);
   if (nt == 1) {
     region<false, false, true, true>(S1, 0, o, 0, P1, S0, P0, st, qf, smem, sc, kbase, M, lane);
-    rescale(o, st);
+    settle<true>(o, st, S0, P0, sc, kbase, M, lane);
     wait_vm<0>();
     __syncthreads();
     region<false, true, false, false>(S1, 0, o, v_stage(0), P0, S0, P1, st, qf, smem, sc, 0, M, lane);
   } else {
     region<true, false, true, false>(S1, k_stage(1), o, 0, P1, S0, P0, st, qf, smem, sc, kbase, M,
                                      lane);
-    rescale(o, st);
+    settle<false>(o, st, S0, P0, sc, kbase, M, lane);
     int it = 1;
     for (; it + 1 < nt - 1; it += 2) {
       // it odd: scores in S1, probabilities to P1; then it+1 even
       top(it);
       region<true, true, true, false>(S0, k_stage(it + 1), o, v_stage(it - 1), P0, S1, P1, st, qf,
                                       smem, sc, kbase + it * AKV, M, lane);
-      rescale(o, st);
+      settle<false>(o, st, S1, P1, sc, kbase + it * AKV, M, lane);
       top(it + 1);
       region<true, true, true, false>(S1, k_stage(it + 2), o, v_stage(it), P1, S0, P0, st, qf,
                                       smem, sc, kbase + (it + 1) * AKV, M, lane);
-      rescale(o, st);
+      settle<false>(o, st, S0, P0, sc, kbase + (it + 1) * AKV, M, lane);
     }
     if (it < nt - 1) {
       // it = nt-2 (odd), then the last tile nt-1 (even)
       top(it);
       region<true, true, true, false>(S0, k_stage(it + 1), o, v_stage(it - 1), P0, S1, P1, st, qf,
                                       smem, sc, kbase + it * AKV, M, lane);
-      rescale(o, st);
+      settle<false>(o, st, S1, P1, sc, kbase + it * AKV, M, lane);
       top(it + 1);
       region<false, true, true, true>(S1, 0, o, v_stage(it), P1, S0, P0, st, qf, smem, sc,
                                       kbase + (it + 1) * AKV, M, lane);
-      rescale(o, st);
+      settle<true>(o, st, S0, P0, sc, kbase + (it + 1) * AKV, M, lane);
       wait_vm<0>();
       __syncthreads();
       region<false, true, false, false>(S1, 0, o, v_stage(it + 1), P0, S0, P1, st, qf, smem, sc, 0,
@@ -384,7 +407,7 @@ __device__ __forceinline__ void attend(const AttnArgs& p, const lds_u8* smem, ui
       top(it);
       region<false, true, true, true>(S0, 0, o, v_stage(it - 1), P0, S1, P1, st, qf, smem, sc,
                                       kbase + it * AKV, M, lane);
-      rescale(o, st);
+      settle<true>(o, st, S1, P1, sc, kbase + it * AKV, M, lane);
       wait_vm<0>();
       __syncthreads();
       region<false, true, false, false>(S0, 0, o, v_stage(it), P1, S1, P0, st, qf, smem, sc, 0, M,
