@@ -2,6 +2,7 @@
 
     python -m latent_flow_matching_flux_amd.profile_summary trace DIR
     python -m latent_flow_matching_flux_amd.profile_summary pmc DIR [DIR ...]
+    python -m latent_flow_matching_flux_amd.profile_summary report TRACE_DIR PMC_DIR ...
 
 `trace` reads the *_kernel_trace.csv files under DIR (rocprofv3
 --kernel-trace --output-format csv) and gives, per kernel and per grid size,
@@ -11,16 +12,22 @@ under each DIR (rocprofv3 --pmc ...) and gives, per kernel and grid size, the
 mean of every counter over the dispatches, plus the derived figures the
 counters support:
 
-  MFMA busy   SQ_VALU_MFMA_BUSY_CYCLES / (SIMDs x GRBM_GUI_ACTIVE): share of
-              the SIMDs' cycles their matrix unit was busy
-  clock       SQ_BUSY_CYCLES / duration (SQ_BUSY_CYCLES counts each shader
-              engine's busy cycles; divided by the engine count)
-  VALU busy   SQ_ACTIVE_INST_VALU / (4 x SQ_BUSY_CU_CYCLES)
-  LDS bytes   SQ_INSTS_LDS is per wave; bandwidth needs the kernel's own
-              bytes per instruction, so only counts are reported
+  MFMA busy   SQ_VALU_MFMA_BUSY_CYCLES / (SIMDs x GRBM_GUI_ACTIVE / 8): share
+              of the SIMDs' cycles their matrix unit was busy (the CSV gives
+              GRBM_GUI_ACTIVE summed over the 8 XCDs)
+  clock       SQ_BUSY_CYCLES / 32 / duration (SQ_BUSY_CYCLES sums the busy
+              cycles of the 32 shader engines)
+  VALU busy   SQ_ACTIVE_INST_VALU / (CUs x GRBM_GUI_ACTIVE / 8)
+  LDS active  SQ_LDS_IDX_ACTIVE / (CUs x GRBM_GUI_ACTIVE / 8): cycles the LDS
+              served indexed (ds_*) instructions; the direct global->LDS
+              loads are not counted
   DRAM bytes  32 x TCC_EA0_RDREQ_DRAM_32B (reads), 32 x
               TCC_EA0_WRREQ_WRITE_DRAM_32B (writes); FETCH_SIZE / WRITE_SIZE
               are the L2's requests beyond itself (Infinity Cache or DRAM)
+
+`report` combines a trace and counter passes of `bench.py --block-only`
+(the joint block at 8432 tokens) into one table per block kernel, with the
+algorithmic bytes of each kernel at that size beside the measured ones.
 
 Kernel names are shortened to the function name (k_gemm_proj, ...).
 """
@@ -32,7 +39,9 @@ import statistics
 import sys
 from collections import defaultdict
 
-SIMDS = 1024          # 256 CUs x 4 SIMDs (MI355X)
+CUS = 256             # MI355X
+SIMDS = 4 * CUS
+XCDS = 8
 SHADER_ENGINES = 32   # 8 XCDs x 4 shader engines
 
 
@@ -109,10 +118,13 @@ def pmc(dirs):
         for n in sorted(c):
             print(f"| {n} | {c[n]:.6g} |")
         derived = []
-        if "SQ_VALU_MFMA_BUSY_CYCLES" in c and c.get("GRBM_GUI_ACTIVE"):
-            derived.append(("MFMA busy", f"{100 * c['SQ_VALU_MFMA_BUSY_CYCLES'] / (SIMDS * c['GRBM_GUI_ACTIVE']):.1f}% of SIMD cycles"))
-        if "SQ_ACTIVE_INST_VALU" in c and c.get("SQ_BUSY_CU_CYCLES"):
-            derived.append(("VALU busy", f"{100 * c['SQ_ACTIVE_INST_VALU'] / (4 * c['SQ_BUSY_CU_CYCLES']):.1f}%"))
+        gui = c.get("GRBM_GUI_ACTIVE", 0.0) / XCDS     # the CSV sums it over the XCDs
+        if "SQ_VALU_MFMA_BUSY_CYCLES" in c and gui:
+            derived.append(("MFMA busy", f"{100 * c['SQ_VALU_MFMA_BUSY_CYCLES'] / (SIMDS * gui):.1f}% of SIMD cycles"))
+        if "SQ_ACTIVE_INST_VALU" in c and gui:
+            derived.append(("VALU busy", f"{100 * c['SQ_ACTIVE_INST_VALU'] / (CUS * gui):.1f}%"))
+        if "SQ_LDS_IDX_ACTIVE" in c and gui:
+            derived.append(("LDS active", f"{100 * c['SQ_LDS_IDX_ACTIVE'] / (CUS * gui):.1f}% of CU cycles"))
         if "SQ_VALU_MFMA_COEXEC_CYCLES" in c and c.get("SQ_VALU_MFMA_BUSY_CYCLES"):
             derived.append(("VALU co-issued with MFMA",
                             f"{100 * c['SQ_VALU_MFMA_COEXEC_CYCLES'] / c['SQ_VALU_MFMA_BUSY_CYCLES']:.1f}% of MFMA-busy cycles"))
@@ -140,11 +152,85 @@ def pmc(dirs):
                 print(f"- {n}: {v}")
 
 
+def _block_kernels(dirs):
+    """Mean counter values per dispatch of each kernel's most frequent
+    launch shape, merged over the counter passes."""
+    vals = defaultdict(lambda: defaultdict(list))
+    for d in dirs:
+        for r in _rows("*counter_collection.csv", d):
+            vals[(short(r["Kernel_Name"]), _grid(r))][r["Counter_Name"]].append(
+                float(r["Counter_Value"]))
+    best = {}
+    for (k, g), c in vals.items():
+        n = max(len(v) for v in c.values())
+        if k not in best or n > best[k][1]:
+            best[k] = (g, n, {name: statistics.mean(v) for name, v in c.items()})
+    return best
+
+
+def report(trace_dir, pmc_dirs, tokens=8432, D=3072, F=9216, H=24):
+    """Markdown table of the block kernels of `bench.py --block-only`."""
+    rows = _rows("*kernel_trace.csv", trace_dir)
+    dur = defaultdict(list)
+    scratch = {}
+    for r in rows:
+        k = short(r["Kernel_Name"])
+        dur[k].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+        scratch[k] = max(scratch.get(k, 0), int(_get(r, "Private_Segment_Size", "Scratch_Size",
+                                                     default="0")))
+    c = _block_kernels(pmc_dirs)
+    n_pad = (tokens + 255) // 256 * 256
+    mb = 1e6
+    alg = {  # algorithmic HBM bytes per launch at this size
+        "k_ln_modulate": tokens * D * 4 + n_pad * D * 2,
+        "k_gemm_proj": n_pad * D * 2 + (3 * D + 2 * F) * D * 2 + 3 * n_pad * D * 2 + n_pad * F * 2,
+        "k_attention": 3 * H * n_pad * 128 * 2 + n_pad * D * 2,
+        "k_gemm_out": n_pad * (D + F) * 2 + D * (D + F) * 2 + 2 * tokens * D * 4,
+    }
+    copy = c.get("__amd_rocclr_copyBuffer")
+    fscale = wscale = 1.0
+    if copy and copy[2].get("FETCH_SIZE") and copy[2].get("WRITE_SIZE"):
+        nbytes = tokens * D * 4
+        fscale = nbytes / (copy[2]["FETCH_SIZE"] * 1024)
+        wscale = nbytes / (copy[2]["WRITE_SIZE"] * 1024)
+    print(f"Calibration: the block's input copy (`__amd_rocclr_copyBuffer`, {tokens * D * 4} B "
+          f"read and written) gives FETCH_SIZE x {fscale:.4f} and WRITE_SIZE x {wscale:.4f}; "
+          f"32 x TCC_EA0_RDREQ_DRAM_32B reads {32 * copy[2].get('TCC_EA0_RDREQ_DRAM_32B', 0) / mb:.1f} MB "
+          f"for it (exact).\n" if copy else "")
+    print("| kernel | launches | mean (us) | clock (GHz) | MFMA busy | VALU busy | LDS active | "
+          "LDS bank conflicts | L2 fetch beyond L2 (MB) | memory-side reads (MB) | writes (MB) | "
+          "algorithmic (MB) | scratch B/lane |")
+    print("|" + "---|" * 13)
+    for k in ("k_ln_modulate", "k_gemm_proj", "k_attention", "k_attention_fixup", "k_gemm_out",
+              "k_gemm_out_fixup"):
+        if k not in c:
+            continue
+        g, n, v = c[k]
+        d = dur.get(k, [0.0])
+        mean_us = statistics.mean(d)
+        gui = v.get("GRBM_GUI_ACTIVE", 0.0) / XCDS     # summed over the XCDs
+        clk = v.get("SQ_BUSY_CYCLES", 0.0) / SHADER_ENGINES / (mean_us * 1e3) if mean_us else 0
+        mfma = 100 * v.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) / (SIMDS * gui) if gui else 0
+        valu = 100 * v.get("SQ_ACTIVE_INST_VALU", 0.0) / (CUS * gui) if gui else 0
+        lds = 100 * v.get("SQ_LDS_IDX_ACTIVE", 0.0) / (CUS * gui) if gui else 0
+        bank = (100 * v.get("SQ_LDS_BANK_CONFLICT", 0.0) / v["SQ_ACTIVE_INST_LDS"]
+                if v.get("SQ_ACTIVE_INST_LDS") else 0)
+        fetch = v.get("FETCH_SIZE", 0.0) * 1024 * fscale / mb
+        dram = 32 * v.get("TCC_EA0_RDREQ_DRAM_32B", 0.0) / mb
+        wr = v.get("WRITE_SIZE", 0.0) * 1024 * wscale / mb
+        a = alg.get(k)
+        print(f"| {k} | {len(d)} | {mean_us:.1f} | {clk:.2f} | {mfma:.1f}% | {valu:.1f}% | "
+              f"{lds:.1f}% | {bank:.2f}% | {fetch:.1f} | {dram:.1f} | {wr:.1f} | "
+              f"{a / mb if a else float('nan'):.1f} | {scratch.get(k, 0)} |")
+
+
 if __name__ == "__main__":
     if len(sys.argv) >= 3 and sys.argv[1] == "trace":
         trace(sys.argv[2])
     elif len(sys.argv) >= 3 and sys.argv[1] == "pmc":
         pmc(sys.argv[2:])
+    elif len(sys.argv) >= 4 and sys.argv[1] == "report":
+        report(sys.argv[2], sys.argv[3:])
     else:
         print(__doc__)
         sys.exit(2)
