@@ -345,7 +345,9 @@ def main():
     t1 = time.perf_counter()
     F.profile_enable(False)
     stats = {k: F.profile_read(k) for k in F.KERNELS}
-    # the joint blocks' launches (all n tokens) apart from the per-stream ones
+    # the launches over all n tokens (the joint blocks; for the GEMMs also the
+    # per-mode blocks, whose streams share one launch per block) apart from
+    # the per-stream attention launches
     joint_stats = {k: F.profile_read(k, n_tokens=n) for k in ("gemm_proj", "attention", "gemm_out")}
     F.profile_reset()
 
@@ -386,8 +388,8 @@ def main():
     step_flops /= args.steps
 
     # dominant kernel: the projection GEMM (the largest FLOP share), over
-    # its launches at the full n tokens (the 28 joint blocks of each step);
-    # the mean over every launch size is given beside it
+    # its launches at the full n tokens (each step's 28 joint blocks and 5
+    # grouped per-mode blocks); the mean over every launch is given beside it
     gp = joint_stats["gemm_proj"]
     avg_ms = gp["total_ms"] / max(gp["launches"], 1)
     achieved = proj_fpt * n / (avg_ms * 1e-3) / 1e12 if avg_ms > 0 else 0.0
@@ -400,7 +402,7 @@ def main():
                 "traffic": measured_traffic(n),
                 "launches": gp["launches"], "avg_us": 1e3 * avg_ms,
                 "work_per_launch": f"{proj_fpt / 1e6:.2f} MFLOP/token x {n} tokens "
-                                   f"(the joint blocks' launches of the timed steps)",
+                                   f"(the launches over all tokens in the timed steps)",
                 "all_launches": {"launches": ga["launches"], "avg_us": 1e3 * all_avg_ms,
                                  "mean_tokens": ga["tokens"] / max(ga["launches"], 1),
                                  "achieved": all_achieved,

@@ -272,7 +272,13 @@ flux3_status flux3_block_forward_noalloc(const flux3_dims *dims,
  * stage 1 runs, for every segment s, the n_pm per-mode blocks of its mode
  * on that segment's rows alone (each stream attends only to itself);
  * stage 2 runs the n_joint joint blocks over all n_tokens with per-segment
- * modulation.
+ * modulation.  When the segments, each padded to 256 rows, fit the
+ * workspace's rows (n_tokens rounded up to 256; true of [240 | 4096] and
+ * [240 | 4096 | 4096]) and their modes' block-b weights share one layout,
+ * stage 1 enqueues one launch sequence per block for all segments, each a
+ * row group with its own weights and its own attention; otherwise one
+ * sequence per segment.  Both give the same per-segment results (up to the
+ * summation order of split output tiles).
  *   per_mode : host array [3 * n_pm]; block b of mode m is
  *              per_mode[m * n_pm + b] (entries of unused modes may be
  *              zeroed; they are only checked if a segment uses that mode).

@@ -220,18 +220,23 @@ flux3_status after_launch(hipError_t e, const char* what, hipStream_t s) {
   return FLUX3_OK;
 }
 
-// Enqueue one block on rows [0, n) of x (already validated).
-// With split false the workspace has no split-partial region (only the
-// buffers before `part`); the output GEMM and attention then run their
-// leftover tiles whole instead of splitting them.
-flux3_status run_block(const flux3_dims* d, const flux3_block_weights& w, float* x, int64_t n,
-                       const flux3::SegTableHost& st, const float* mod, const float* rope,
-                       void* ws, hipStream_t s, bool split = true) {
+// One block launch sequence (arguments already validated).  `rg` maps workspace rows to tokens: one
+// group at rows = tokens for a plain block, one group per segment (each
+// starting on a 256-row boundary, with its own weight set and attention over
+// its own rows) for a grouped launch of stage-1 blocks; n is the launch's
+// token count and rows the workspace rows its GEMM tiles cover.  With split
+// false the workspace has no split-partial region (only the buffers before
+// `part`); the output GEMM and attention then run their leftover tiles whole
+// instead of splitting them.
+flux3_status run_block_groups(const flux3_dims* d, const flux3::WeightSets& sets,
+                              const flux3::RowGroups& rg, int64_t rows, float* x, int64_t n,
+                              const flux3::SegTableHost& st, const float* mod, const float* rope,
+                              void* ws, int64_t ws_tokens, hipStream_t s, bool split) {
   flux3_workspace_layout L;
-  layout_of(d, n, &L);
+  layout_of(d, ws_tokens, &L);
   flux3::WsPtrs wp = carve(ws, L);
   if (!split) wp.part = nullptr;
-  const flux3::BlockWeightsDev wd = dev_weights(w);
+  const flux3::BlockWeightsDev& wd = sets.w[0];
   if (wd.fp8) {
     // h's codes and scales in h's buffer (dead until the next block's K1);
     // those of [o | act] from the start of h over q, k and vt, which nothing
@@ -250,6 +255,8 @@ flux3_status run_block(const flux3_dims* d, const flux3_block_weights& w, float*
   bs.D = d->width;
   bs.H = d->heads;
   bs.F = d->mlp_hidden;
+  bs.rows = (int32_t)rows;
+  bs.rg = rg;
   flux3_status r;
   const double m = (double)n;
   int pi = prof_begin(FLUX3_K_LN_MODULATE, m, s);
@@ -258,24 +265,50 @@ flux3_status run_block(const flux3_dims* d, const flux3_block_weights& w, float*
   prof_end(pi, s);
   if ((r = after_launch(e, "ln_modulate", s)) != FLUX3_OK) return r;
   pi = prof_begin(FLUX3_K_GEMM_PROJ, m, s);
-  e = flux3::launch_gemm_proj(bs, wd, rope, wp, kEpsRMS, s);
+  e = flux3::launch_gemm_proj(bs, sets, rope, wp, kEpsRMS, s);
   prof_end(pi, s);
   if ((r = after_launch(e, "gemm_proj", s)) != FLUX3_OK) return r;
-  pi = prof_begin(FLUX3_K_ATTENTION, m, s);
-  e = flux3::launch_attention(bs, wp, s);
-  prof_end(pi, s);
-  if ((r = after_launch(e, "attention", s)) != FLUX3_OK) return r;
+  // attention within each group: its q, k, v^T and output rows start at the
+  // group's first workspace row (a multiple of 256, so the packed output
+  // layout shifts by whole row blocks)
+  for (int g = 0; g < rg.n; ++g) {
+    flux3::WsPtrs wg = wp;
+    const size_t r0 = (size_t)rg.ws_start[g];
+    wg.q = static_cast<char*>(wp.q) + r0 * 128 * 2;
+    wg.k = static_cast<char*>(wp.k) + r0 * 128 * 2;
+    wg.vt = static_cast<char*>(wp.vt) + r0 * 2;
+    wg.cat = static_cast<char*>(wp.cat) + r0 * (size_t)(bs.D + bs.F) * 2;
+    flux3::BlockShape bg = bs;
+    bg.M = rg.count[g];
+    pi = prof_begin(FLUX3_K_ATTENTION, (double)bg.M, s);
+    e = flux3::launch_attention(bg, wg, s);
+    prof_end(pi, s);
+    if ((r = after_launch(e, "attention", s)) != FLUX3_OK) return r;
+  }
   if (wd.fp8) {
     pi = prof_begin(FLUX3_K_QUANT, m, s);
-    e = flux3::launch_quant_packed_rows(wp.cat, wp.cat8, wp.scat, bs.M, bs.D + bs.F, s);
+    e = flux3::launch_quant_packed_rows(wp.cat, wp.cat8, wp.scat, rg.n == 1 ? bs.M : bs.rows,
+                                        bs.D + bs.F, s);
     prof_end(pi, s);
     if ((r = after_launch(e, "quant_cat", s)) != FLUX3_OK) return r;
   }
   pi = prof_begin(FLUX3_K_GEMM_OUT, m, s);
-  e = flux3::launch_gemm_out(bs, wd, wp, x, mod, st, s);
+  e = flux3::launch_gemm_out(bs, sets, wp, x, mod, st, s);
   prof_end(pi, s);
   if ((r = after_launch(e, "gemm_out", s)) != FLUX3_OK) return r;
   return FLUX3_OK;
+}
+
+// A plain block on rows [0, n) of x with one weight set.
+flux3_status run_block(const flux3_dims* d, const flux3_block_weights& w, float* x, int64_t n,
+                       const flux3::SegTableHost& st, const float* mod, const float* rope,
+                       void* ws, hipStream_t s, bool split = true) {
+  flux3::WeightSets sets;
+  sets.w[0] = dev_weights(w);
+  sets.n = 1;
+  const int64_t rows = (n + kRowAlign - 1) / kRowAlign * kRowAlign;
+  return run_block_groups(d, sets, flux3::one_group((int32_t)n), rows, x, n, st, mod, rope, ws, n,
+                          s, split);
 }
 
 
@@ -352,6 +385,8 @@ flux3_status check_stack_weights(const flux3_dims* d, const flux3_block_weights*
   return FLUX3_OK;
 }
 
+int64_t pad256(int64_t v) { return (v + 255) / 256 * 256; }
+
 // Enqueues the two stages on validated arguments.
 flux3_status run_stack(const flux3_dims* dims, const flux3_block_weights* per_mode, int32_t n_pm,
                        const flux3_block_weights* joint, int32_t n_joint, float* x,
@@ -361,7 +396,49 @@ flux3_status run_stack(const flux3_dims* dims, const flux3_block_weights* per_mo
                        void* workspace, hipStream_t s) {
   flux3_status r;
   const size_t D = (size_t)dims->width;
-  // stage 1: each segment runs its own mode's blocks on its rows alone
+  // stage 1: each segment runs its own mode's blocks on its rows alone.
+  // Several segments go through one launch sequence per block when their
+  // rows, each segment padded to 256, fit the workspace and their weights
+  // share a layout: every segment is a row group with its mode's weight set
+  // and attends within itself, so the result is that of separate blocks.
+  if (n_pm > 0 && n_segs > 1) {
+    flux3::RowGroups rg;
+    memset(&rg, 0, sizeof rg);
+    rg.n = n_segs;
+    int64_t rows = 0;
+    bool used[flux3::kMaxWeightSets] = {false, false, false};
+    for (int sg = 0; sg < n_segs; ++sg) {
+      used[segs[sg].mode] = true;
+      rg.ws_start[sg] = (int32_t)rows;
+      rg.x_start[sg] = segs[sg].start;
+      rg.count[sg] = segs[sg].count;
+      rg.wsel[sg] = segs[sg].mode;
+      rows += pad256(segs[sg].count);
+    }
+    flux3_workspace_layout L;
+    layout_of(dims, n_tokens, &L);
+    bool grouped = rows <= L.n_pad;
+    for (int b = 0; b < n_pm && grouped; ++b) {
+      const flux3_block_weights& w0 = per_mode[segs[0].mode * n_pm + b];
+      for (int sg = 1; sg < n_segs; ++sg)
+        if (per_mode[segs[sg].mode * n_pm + b].layout != w0.layout) grouped = false;
+    }
+    if (grouped) {
+      for (int b = 0; b < n_pm; ++b) {
+        // set m holds mode m's block b; a mode no segment uses points at a
+        // used mode's weights (never read, and never validated)
+        flux3::WeightSets sets;
+        sets.n = flux3::kMaxWeightSets;
+        for (int m = 0; m < flux3::kMaxWeightSets; ++m)
+          sets.w[m] = dev_weights(per_mode[(used[m] ? m : segs[0].mode) * n_pm + b]);
+        r = run_block_groups(dims, sets, rg, rows, x, n_tokens, st,
+                             mod_stage1 + (size_t)b * mod_block_stride, rope, workspace, n_tokens,
+                             s, true);
+        if (r != FLUX3_OK) return r;
+      }
+      n_pm = 0;
+    }
+  }
   for (int sg = 0; sg < n_segs && n_pm > 0; ++sg) {
     flux3::SegTableHost one;
     memset(&one, 0, sizeof one);
@@ -388,8 +465,6 @@ struct TransformerLayout {
   size_t block, x, stage, w_out, mod1, mod2, mod_final, mod_ws, total;
   int64_t text_pad, img_pad, ref_pad;
 };
-
-int64_t pad256(int64_t v) { return (v + 255) / 256 * 256; }
 
 void transformer_layout(const flux3_dims* d, const flux3_io_dims* io, int64_t n, int n_segs,
                         int64_t n_text, int64_t n_img, int64_t n_ref, TransformerLayout* L) {
@@ -905,6 +980,8 @@ flux3_status flux3_transformer_forward(const flux3_dims* dims, const flux3_io_di
   bs.D = D;
   bs.H = dims->heads;
   bs.F = dims->mlp_hidden;
+  bs.rows = (int32_t)L.img_pad;
+  bs.rg = flux3::one_group((int32_t)n_img);
   flux3::SegTableHost one;
   memset(&one, 0, sizeof one);
   one.n = 1;

@@ -36,6 +36,26 @@ __device__ __forceinline__ int seg_of(const SegTable& st, int m) {
   return s;
 }
 
+// One group of a launch's RowGroups, as a tile of workspace rows sees it:
+// workspace row r holds token x0 + (r - ws0) when r - ws0 < n (live), and is
+// padding otherwise; token() clamps padding rows to the group's last token
+// (for loads whose results are discarded).
+struct RowMap {
+  int ws0, x0, n, w;
+  __device__ __forceinline__ bool live(int r) const { return r - ws0 < n; }
+  __device__ __forceinline__ int token(int r) const { return x0 + min(r - ws0, n - 1); }
+};
+
+// The group holding workspace row r (groups ascend in workspace rows).
+template <class RG>
+__device__ __forceinline__ RowMap row_map(const RG& rg, int r) {
+  int g = 0;
+#pragma unroll
+  for (int i = 1; i < kMaxSegs; ++i)
+    if (i < rg.n && r >= rg.ws_start[i]) g = i;
+  return RowMap{rg.ws_start[g], rg.x_start[g], rg.count[g], rg.wsel[g]};
+}
+
 // 32x32x16 bf16 MFMA, fp32 accumulate.  Output layout (per lane l, reg r):
 // column l % 32, row 8*(r/4) + 4*(l/32) + r%4.
 __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {

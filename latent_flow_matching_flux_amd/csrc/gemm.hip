@@ -398,13 +398,17 @@ __device__ __forceinline__ void gemm_mainloop(lds_u8* smem, Acc& acc, const Src&
 
 struct ProjArgs {
   const bf16* h;       // packed bf16 h, or packed e4m3 codes of h (F8)
-  const bf16 *wq, *wk, *wv, *wg, *wu;
+  // weight sets; a tile takes the set of its row group
+  const bf16 *wq[kMaxWeightSets], *wk[kMaxWeightSets], *wv[kMaxWeightSets];
+  const bf16 *wg[kMaxWeightSets], *wu[kMaxWeightSets];
   const float* sh;     // F8: dequantisation scale of each h row [n_pad]
-  const float* sw;     // F8: scale of each weight row [3D + 2F], q k v gate up
-  const float *qn, *kn;
-  const float2* rope;
+  const float* sw[kMaxWeightSets];   // F8: scale of each weight row [3D + 2F], q k v gate up
+  const float *qn[kMaxWeightSets], *kn[kMaxWeightSets];
+  const float2* rope;  // rows of tokens
   bf16 *q, *k, *vt, *cat;
-  int M, n_pad, D, H, F;
+  RowGroups rg;        // workspace rows -> tokens
+  int rows;            // workspace rows covered by tiles
+  int n_pad, D, H, F;
   float eps;
 };
 
@@ -456,10 +460,13 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_gemm_proj(ProjArgs p) {
   const int wm = wave >> 1, wn = wave & 1;
   const int qkv_tiles = p.H / 2;
   const int n_n = 3 * qkv_tiles + p.F / 128;
-  const int n_m = p.n_pad / BM;
+  const int n_m = p.rows / BM;
   int mt, nt;
   tile_coords(blockIdx.x, n_m, n_n, mt, nt);
   const int m0 = mt * BM;
+  // the tile's 256 workspace rows lie in one row group (groups start on
+  // 256-row boundaries), which also selects the weight set
+  const RowMap grp = row_map(p.rg, m0);
 
   int kind, head0 = 0, hid0 = 0;
   if (nt < 3 * qkv_tiles) {
@@ -478,9 +485,10 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_gemm_proj(ProjArgs p) {
     // of the same hidden units, so gate and up land in one lane's registers
     return hid0 + 64 * (i >> 2) + 32 * (i & 1);
   };
+  const int ws = grp.w;
   auto w_mat = [&](int i) -> const bf16* {
-    if (kind < 3) return kind == 0 ? p.wq : (kind == 1 ? p.wk : p.wv);
-    return (i & 3) < 2 ? p.wg : p.wu;
+    if (kind < 3) return kind == 0 ? p.wq[ws] : (kind == 1 ? p.wk[ws] : p.wv[ws]);
+    return (i & 3) < 2 ? p.wg[ws] : p.wu[ws];
   };
   auto w_run = [&](int i) -> const bf16* { return w_mat(i) + (size_t)w_row(i) * Dk; };
   Src H, W;   // h is packed, the weights row-major
@@ -505,7 +513,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_gemm_proj(ProjArgs p) {
   // sw_kind: the scales of this tile's weight matrix rows, or of the gate
   // rows for SwiGLU (the up rows follow F rows later)
   const float* sw_kind = nullptr;
-  if constexpr (F8) sw_kind = p.sw + (kind < 3 ? kind * D : 3 * D);
+  if constexpr (F8) sw_kind = p.sw[ws] + (kind < 3 ? kind * D : 3 * D);
 
   const int r32 = lane & 31, hi = lane >> 5;
   // LDS is free once every wave is past the main loop.  Values and SwiGLU
@@ -531,14 +539,14 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_gemm_proj(ProjArgs p) {
     for (int it = 0; it < 32; ++it) {
       const int row = wave * 64 + it * 2 + (lane >> 5);
       const int c = (lane & 31) ^ (row & 31);
-      const int m = min(m0 + row, p.M - 1);
+      const int m = grp.token(m0 + row);
       dma16(reinterpret_cast<const bf16*>(rope + (size_t)m * 2 * kRopePairs + c * 4),
             lds0 + (uint32_t)((wave * 64 + it * 2) * 512));
     }
     wait_vm<0>();
     __syncthreads();
     typedef const __attribute__((address_space(3))) f32x4 lds_f4;
-    const float* nw = kind == 0 ? p.qn : p.kn;
+    const float* nw = kind == 0 ? p.qn[ws] : p.kn[ws];
     bf16* dst = (kind == 0 ? p.q : p.k) + (size_t)head0 * p.n_pad * kHeadDim;
     // the norm weights of this lane's 64 dims, loaded once
     float4 nwv[4][4];
@@ -566,8 +574,8 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_gemm_proj(ProjArgs p) {
     constexpr int STAGE = 256 * 512;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int t = wn * 128 + j * 32 + r32;             // token within the tile
-      const bool live = m0 + t < p.M;
+      const int t = wn * 128 + j * 32 + r32;             // row within the tile
+      const bool live = grp.live(m0 + t);
       float ss = 0.f;
       float rs;
       if constexpr (F8) {
@@ -657,7 +665,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_gemm_proj(ProjArgs p) {
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const float a = F8 ? acc.c[i][j][4 * g + e] * (st[e] * swj[j]) : acc.c[i][j][4 * g + e];
-            v[e] = f2bf(m0 + mb + e < p.M ? a : 0.f);
+            v[e] = f2bf(grp.live(m0 + mb + e) ? a : 0.f);
           }
           *(lds_bf16x4*)(smem + r * 512 + (((pos >> 3) ^ (r & 31)) << 4) + (pos & 7) * 2) = v;
         }
@@ -692,7 +700,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_gemm_proj(ProjArgs p) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int t = wn * 128 + j * 32 + r32;
-      const bool live = m0 + t < p.M;
+      const bool live = grp.live(m0 + t);
       const float st = F8 ? p.sh[m0 + t] : 1.f;
 #pragma unroll
       for (int i = 0; i < 2; ++i)
@@ -731,14 +739,17 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_gemm_proj(ProjArgs p) {
 
 struct OutArgs {
   const bf16* cat;     // packed bf16 [o | act], or its packed e4m3 codes (F8)
-  const bf16 *wo, *wd;
+  // weight sets; a tile takes the set of its row group
+  const bf16 *wo[kMaxWeightSets], *wd[kMaxWeightSets];
   const float* scat;   // F8: scale of each cat row [n_pad]
-  const float* sw;     // F8: scale of each row of [wo | wd] [D]
-  float* x;
+  const float* sw[kMaxWeightSets];   // F8: scale of each row of [wo | wd] [D]
+  float* x;            // rows of tokens
   const float* mod;
   float* part;       // split-tile partial sums: 2 slots of BM x BN fp32 per workgroup
-  SegTable segs;
-  int M, n_pad, D, F;
+  SegTable segs;     // tokens -> segments (modulation rows)
+  RowGroups rg;      // workspace rows -> tokens
+  int rows;          // workspace rows covered by tiles
+  int n_pad, D, F;
   int nk, nk0;       // k slices of a tile, of them from wo
   int groups;        // persistent workgroups G
   int dp_rounds;     // whole-tile rounds before the split tail
@@ -757,28 +768,29 @@ struct OutArgs {
 // by the fixup kernel from the partials of its ranges, in k order.  A
 // range's first segment writes slot 2v, its last (when it is another tile)
 // slot 2v + 1.
-// gate_s row of the segment holding token row m.
+// gate_s row of the segment holding token m.
 __device__ __forceinline__ const float* gate_row(const OutArgs& p, int m) {
   return p.mod + (size_t)seg_of(p.segs, m) * 3 * p.D + 2 * p.D;
 }
 
 // x += gate_s * acc for row block i of a wave (32 rows x 128 columns).
 // Lane l holds column l % 32 of each 32-column block j and rows
-// 8 (e / 4) + 4 (l / 32) + e % 4, e < 16.  Every load is issued before the
-// first store and none sits behind a branch: row indices past the last token
-// are clamped for the loads, and only the stores are predicated.  When the
-// wave's 128 rows lie in one segment (gate_one != null) its gate values are
-// read once per tile.
+// 8 (e / 4) + 4 (l / 32) + e % 4, e < 16 (workspace rows of the tile's row
+// group grp; each live one is the x row of its token).  Every load is issued
+// before the first store and none sits behind a branch: padding rows are
+// clamped to the group's last token for the loads, and only the stores are
+// predicated.  When the wave's 128 rows lie in one segment (gate_one !=
+// null) its gate values are read once per tile.
 __device__ __forceinline__ void out_rows(const OutArgs& p, const f32x16 (&v)[4], int i, int m0,
                                          int n0, int wm, int wn, int lane,
-                                         const float* gate_one) {
+                                         const float* gate_one, const RowMap& grp) {
   const int D = p.D;
   const int mb = m0 + wm * 128 + i * 32 + 4 * (lane >> 5);
   const int nb = n0 + wn * 128 + (lane & 31);
   float xv[16][4];
 #pragma unroll
   for (int e = 0; e < 16; ++e) {
-    const int m = min(mb + 8 * (e >> 2) + (e & 3), p.M - 1);
+    const int m = grp.token(mb + 8 * (e >> 2) + (e & 3));
     const float* xr = p.x + (size_t)m * D + nb;
 #pragma unroll
     for (int j = 0; j < 4; ++j) xv[e][j] = xr[32 * j];
@@ -790,13 +802,14 @@ __device__ __forceinline__ void out_rows(const OutArgs& p, const f32x16 (&v)[4],
   }
 #pragma unroll
   for (int e = 0; e < 16; ++e) {
-    const int m = mb + 8 * (e >> 2) + (e & 3);
+    const int r = mb + 8 * (e >> 2) + (e & 3);
+    const int m = grp.token(r);
     if (!gate_one) {
-      const float* g = gate_row(p, min(m, p.M - 1)) + nb;
+      const float* g = gate_row(p, m) + nb;
 #pragma unroll
       for (int j = 0; j < 4; ++j) gv[j] = g[32 * j];
     }
-    if (m < p.M) {
+    if (grp.live(r)) {
       float* xr = p.x + (size_t)m * D + nb;
 #pragma unroll
       for (int j = 0; j < 4; ++j) xr[32 * j] = xv[e][j] + gv[j] * v[j][e];
@@ -806,18 +819,19 @@ __device__ __forceinline__ void out_rows(const OutArgs& p, const f32x16 (&v)[4],
 
 // The gate row shared by all 128 rows of wave row-block wm, or null when
 // they straddle a segment boundary.
-__device__ __forceinline__ const float* wave_gate(const OutArgs& p, int m0, int wm) {
-  const int first = min(m0 + wm * 128, p.M - 1), last = min(m0 + wm * 128 + 127, p.M - 1);
+__device__ __forceinline__ const float* wave_gate(const OutArgs& p, int m0, int wm,
+                                                  const RowMap& grp) {
+  const int first = grp.token(m0 + wm * 128), last = grp.token(m0 + wm * 128 + 127);
   const int s = seg_of(p.segs, first);
   return s == seg_of(p.segs, last) ? p.mod + (size_t)s * 3 * p.D + 2 * p.D : nullptr;
 }
 
 // x += gate_s * acc for the tile's live rows.
 __device__ __forceinline__ void out_epilogue(const OutArgs& p, const Acc& acc, int m0, int n0,
-                                             int wm, int wn, int lane) {
-  const float* g = wave_gate(p, m0, wm);
+                                             int wm, int wn, int lane, const RowMap& grp) {
+  const float* g = wave_gate(p, m0, wm, grp);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) out_rows(p, acc.c[i], i, m0, n0, wm, wn, lane, g);
+  for (int i = 0; i < 4; ++i) out_rows(p, acc.c[i], i, m0, n0, wm, wn, lane, g, grp);
 }
 
 // Partial slot layout: float4 q = 4 (4 i + j) + g of a lane holds
@@ -829,17 +843,17 @@ __device__ __forceinline__ float4* slot_base(const OutArgs& p, int slot) {
 }
 
 template <bool PW, bool F8>
-__device__ __forceinline__ void out_tile_ptrs(const OutArgs& p, int m0, int n0, int wave, Src& A,
-                                              Src& B0, Src& B1) {
+__device__ __forceinline__ void out_tile_ptrs(const OutArgs& p, int m0, int n0, int wave, int ws,
+                                              Src& A, Src& B0, Src& B1) {
   // row lengths in 2-byte units
   const int D = F8 ? p.D / 2 : p.D, F = F8 ? p.F / 2 : p.F, ldc = D + F;
   A.lo = p.cat + (size_t)(m0 + 64 * wave) * ldc;   // packed
   A.hi = A.lo;
   A.ld = 8 * ldc;
-  B0.lo = p.wo + (size_t)(n0 + 64 * wave) * D;
+  B0.lo = p.wo[ws] + (size_t)(n0 + 64 * wave) * D;
   B0.hi = B0.lo + (size_t)32 * D;
   B0.ld = PW ? 8 * D : D;
-  B1.lo = p.wd + (size_t)(n0 + 64 * wave) * F;
+  B1.lo = p.wd[ws] + (size_t)(n0 + 64 * wave) * F;
   B1.hi = B1.lo + (size_t)32 * F;
   B1.ld = PW ? 8 * F : F;
 }
@@ -856,7 +870,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_gemm_out(OutArgs p) {
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6), lane = t & 63;
   const int wm = wave >> 1, wn = wave & 1;
   const int n_n = p.D / BN;
-  const int n_m = p.n_pad / BM;
+  const int n_m = p.rows / BM;
   const int n_tiles = n_m * n_n;
   const int nk = p.nk;
   const int G = p.groups;
@@ -893,8 +907,9 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_gemm_out(OutArgs p) {
     } else {
       break;
     }
+    const RowMap grp = row_map(p.rg, mt * BM);
     Src A, B0, B1;
-    out_tile_ptrs<PW, F8>(p, mt * BM, nt * BN, wave, A, B0, B1);
+    out_tile_ptrs<PW, F8>(p, mt * BM, nt * BN, wave, grp.w, A, B0, B1);
     if (!first) __syncthreads();   // the previous item's LDS reads are done
     first = false;
     Acc acc;
@@ -902,10 +917,10 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_gemm_out(OutArgs p) {
     if constexpr (F8) {
       const float* a0 = p.scat + mt * BM + wm * 128;
       const float* const a_run[4] = {a0, a0 + 32, a0 + 64, a0 + 96};
-      scale_acc(acc, a_run, p.sw + nt * BN + wn * 128, lane);
+      scale_acc(acc, a_run, p.sw[grp.w] + nt * BN + wn * 128, lane);
     }
     if (kb == 0 && ke == nk) {
-      out_epilogue(p, acc, mt * BM, nt * BN, wm, wn, lane);
+      out_epilogue(p, acc, mt * BM, nt * BN, wm, wn, lane, grp);
     } else {
       float4* dst = slot_base(p, sk.slot(v, tt)) + (size_t)wave * 64 * 64 + lane;
 #pragma unroll
@@ -933,7 +948,7 @@ constexpr int FIX_SPLIT = 16;   // fixup workgroups per split tile
 // x and gate are loaded before the partials are summed.
 __global__ __launch_bounds__(NTHREADS) void k_gemm_out_fixup(OutArgs p) {
   const int n_n = p.D / BN;
-  const int n_m = p.n_pad / BM;
+  const int n_m = p.rows / BM;
   SplitK sk;
   sk.nk = p.nk;
   sk.G = p.groups;
@@ -952,12 +967,13 @@ __global__ __launch_bounds__(NTHREADS) void k_gemm_out_fixup(OutArgs p) {
   const int ij = q >> 2, g = q & 3, ii = ij >> 2, jj = ij & 3;
   int mt, nt;
   tile_coords(p.dp_rounds * p.groups + tt, n_m, n_n, mt, nt);
-  const int m = mt * BM + (w >> 1) * 128 + ii * 32 + 8 * g + 4 * (l0 >> 5);
+  const int m = mt * BM + (w >> 1) * 128 + ii * 32 + 8 * g + 4 * (l0 >> 5);   // workspace row
   const int n = nt * BN + (w & 1) * 128 + jj * 32 + (l0 & 31);
+  const RowMap grp = row_map(p.rg, mt * BM);
   float4 xv[4], gv[4];
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
-    const int mr = min(m + r, p.M - 1);
+    const int mr = grp.token(m + r);
     xv[r] = *reinterpret_cast<const float4*>(p.x + (size_t)mr * p.D + n);
     gv[r] = *reinterpret_cast<const float4*>(gate_row(p, mr) + n);
   }
@@ -983,13 +999,13 @@ __global__ __launch_bounds__(NTHREADS) void k_gemm_out_fixup(OutArgs p) {
                          {sum[0].w, sum[1].w, sum[2].w, sum[3].w}};
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
-    if (m + r >= p.M) continue;
+    if (!grp.live(m + r)) continue;
     float4 o = xv[r];
     o.x += gv[r].x * c[r][0];
     o.y += gv[r].y * c[r][1];
     o.z += gv[r].z * c[r][2];
     o.w += gv[r].w * c[r][3];
-    *reinterpret_cast<float4*>(p.x + (size_t)(m + r) * p.D + n) = o;
+    *reinterpret_cast<float4*>(p.x + (size_t)grp.token(m + r) * p.D + n) = o;
   }
 }
 
@@ -1161,33 +1177,39 @@ hipError_t launch_gemm_split(const SplitGemm& g, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_gemm_proj(const BlockShape& bs, const BlockWeightsDev& w,
+hipError_t launch_gemm_proj(const BlockShape& bs, const WeightSets& sets,
                             const float* rope, const WsPtrs& ws, float eps,
                             hipStream_t s) {
+  if (!rows_valid(bs) || sets.n < 1) return hipErrorInvalidValue;
+  const BlockWeightsDev& w = sets.w[0];   // layout flags shared by every set
   ProjArgs p;
   p.h = static_cast<const bf16*>(w.fp8 ? ws.h8 : ws.h);
   p.sh = ws.sh;
-  p.sw = w.s_proj;
-  p.wq = static_cast<const bf16*>(w.wq);
-  p.wk = static_cast<const bf16*>(w.wk);
-  p.wv = static_cast<const bf16*>(w.wv);
-  p.wg = static_cast<const bf16*>(w.w_gate);
-  p.wu = static_cast<const bf16*>(w.w_up);
-  p.qn = w.q_norm;
-  p.kn = w.k_norm;
+  for (int i = 0; i < kMaxWeightSets; ++i) {
+    const BlockWeightsDev& v = sets.w[i < sets.n ? i : 0];
+    p.sw[i] = v.s_proj;
+    p.wq[i] = static_cast<const bf16*>(v.wq);
+    p.wk[i] = static_cast<const bf16*>(v.wk);
+    p.wv[i] = static_cast<const bf16*>(v.wv);
+    p.wg[i] = static_cast<const bf16*>(v.w_gate);
+    p.wu[i] = static_cast<const bf16*>(v.w_up);
+    p.qn[i] = v.q_norm;
+    p.kn[i] = v.k_norm;
+  }
   p.rope = reinterpret_cast<const float2*>(rope);
   p.q = static_cast<bf16*>(ws.q);
   p.k = static_cast<bf16*>(ws.k);
   p.vt = static_cast<bf16*>(ws.vt);
   p.cat = static_cast<bf16*>(ws.cat);
-  p.M = bs.M;
+  p.rg = bs.rg;
+  p.rows = bs.rows;
   p.n_pad = bs.n_pad;
   p.D = bs.D;
   p.H = bs.H;
   p.F = bs.F;
   p.eps = eps;
   const int n_n = 3 * (bs.H / 2) + bs.F / 128;
-  const int n_m = bs.n_pad / BM;
+  const int n_m = bs.rows / BM;
   if (w.fp8)
     hipLaunchKernelGGL((k_gemm_proj<true, true>), dim3(n_m * n_n), dim3(NTHREADS), 0, s, p);
   else if (w.packed)
@@ -1209,15 +1231,20 @@ int stream_k_groups() {
   return cus < kMaxSplitGroups ? cus : kMaxSplitGroups;
 }
 
-hipError_t launch_gemm_out(const BlockShape& bs, const BlockWeightsDev& w,
+hipError_t launch_gemm_out(const BlockShape& bs, const WeightSets& sets,
                            const WsPtrs& ws, float* x, const float* mod,
                            const SegTableHost& segs, hipStream_t s) {
+  if (!rows_valid(bs) || sets.n < 1) return hipErrorInvalidValue;
+  const BlockWeightsDev& w = sets.w[0];   // layout flags shared by every set
   OutArgs p;
   p.cat = static_cast<const bf16*>(w.fp8 ? ws.cat8 : ws.cat);
-  p.wo = static_cast<const bf16*>(w.wo);
-  p.wd = static_cast<const bf16*>(w.w_down);
+  for (int i = 0; i < kMaxWeightSets; ++i) {
+    const BlockWeightsDev& v = sets.w[i < sets.n ? i : 0];
+    p.wo[i] = static_cast<const bf16*>(v.wo);
+    p.wd[i] = static_cast<const bf16*>(v.w_down);
+    p.sw[i] = v.s_out;
+  }
   p.scat = ws.scat;
-  p.sw = w.s_out;
   // a slice is 64 bf16 values or 128 fp8 codes deep
   const int slice = w.fp8 ? 2 * BK : BK;
   p.nk = (bs.D + bs.F) / slice;
@@ -1227,12 +1254,13 @@ hipError_t launch_gemm_out(const BlockShape& bs, const BlockWeightsDev& w,
   p.part = static_cast<float*>(ws.part);
   for (int i = 0; i < kMaxSegs; ++i) p.segs.start[i] = segs.start[i];
   p.segs.n = segs.n;
-  p.M = bs.M;
+  p.rg = bs.rg;
+  p.rows = bs.rows;
   p.n_pad = bs.n_pad;
   p.D = bs.D;
   p.F = bs.F;
   p.groups = stream_k_groups();
-  const int n_tiles = (bs.n_pad / BM) * (bs.D / BN);
+  const int n_tiles = (bs.rows / BM) * (bs.D / BN);
   const int G = p.groups;
   p.dp_rounds = n_tiles / G;
   p.tail = n_tiles % G;

@@ -12,13 +12,41 @@ struct RopeLayoutDev {
   double theta, hw_scale;
 };
 
+// Rows of one block launch.  Group g's tokens [x_start, x_start + count)
+// (rows of x, of the rotary tables and of the segment table) sit at
+// workspace rows [ws_start, ws_start + count), ws_start a multiple of 256;
+// workspace rows from there up to the next group's start are padding.  Group
+// g takes weight set wsel and, in a grouped launch, attends within itself.  A
+// plain block is one group with ws_start = x_start = 0 and count = M.
+struct RowGroups {
+  int32_t ws_start[16], x_start[16], count[16], wsel[16];
+  int32_t n;
+};
+
+// The plain block's mapping: tokens [0, M) at workspace rows [0, M), set 0.
+inline RowGroups one_group(int32_t M) {
+  RowGroups g = {};
+  g.n = 1;
+  g.count[0] = M;
+  return g;
+}
+
 struct BlockShape {
   int32_t M;       // tokens in this call
-  int32_t n_pad;   // M rounded up to 256: row count of workspace buffers
+  int32_t n_pad;   // M rounded up to 256: row count (stride) of workspace buffers
   int32_t D;       // width
   int32_t H;       // heads
   int32_t F;       // SwiGLU hidden
+  int32_t rows = 0;    // workspace rows the GEMMs cover (a multiple of 256, <= n_pad)
+  RowGroups rg = {};   // launchers reject a shape whose groups are unset (n == 0)
 };
+
+// The row set-up a launcher accepts: 1..16 groups, rows a multiple of 256
+// within n_pad.
+inline bool rows_valid(const BlockShape& bs) {
+  return bs.rg.n >= 1 && bs.rg.n <= 16 && bs.rows >= 0 && bs.rows % 256 == 0 &&
+         bs.rows <= bs.n_pad;
+}
 
 struct SegTableHost {
   int32_t start[16];
@@ -54,6 +82,14 @@ struct BlockWeightsDev {
   bool fp8;      // rowwise e4m3 codes in the packed fp8 layout (packed too)
   const float* s_proj;  // fp8: row scales of wq, wk, wv, w_gate, w_up [3D + 2F]
   const float* s_out;   // fp8: row scales of [wo | w_down] [D]
+};
+
+// The weight sets of one launch (a group's RowGroups::wsel indexes them);
+// all share the layout flags of w[0].
+constexpr int kMaxWeightSets = 3;
+struct WeightSets {
+  BlockWeightsDev w[kMaxWeightSets];
+  int n;
 };
 
 // Linear-layout [R][K] bf16 (R % 8 == 0, K % 64 == 0) -> packed operand layout.
@@ -129,13 +165,13 @@ hipError_t launch_quant_packed_rows(const void* in, void* out, float* scale, int
 // Ka + Kb <= kQuantMaxK.
 hipError_t launch_quant_weight_rows(const void* a, int Ka, const void* b, int Kb, void* out_a,
                                     void* out_b, float* scale, int R, hipStream_t s);
-hipError_t launch_gemm_proj(const BlockShape& bs, const BlockWeightsDev& w,
+hipError_t launch_gemm_proj(const BlockShape& bs, const WeightSets& w,
                             const float* rope, const WsPtrs& ws, float eps,
                             hipStream_t s);
 hipError_t launch_attention(const BlockShape& bs, const WsPtrs& ws,
                             hipStream_t s);
 int stream_k_groups();
-hipError_t launch_gemm_out(const BlockShape& bs, const BlockWeightsDev& w,
+hipError_t launch_gemm_out(const BlockShape& bs, const WeightSets& w,
                            const WsPtrs& ws, float* x, const float* mod,
                            const SegTableHost& segs, hipStream_t s);
 

@@ -10,7 +10,9 @@
 // operand layout (1-KiB blocks of 8 rows x 64 k, chunks swizzled).
 //
 // One wave per row; each lane holds width/64 values.  HBM-bound: reads 4 B
-// and writes 2 B per element (the modulation vectors stay in cache).
+// and writes 2 B per element (the modulation vectors stay in cache).  Rows
+// are workspace rows: a grouped launch (RowGroups) maps each to its token
+// and skips padding rows.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -18,12 +20,15 @@ namespace flux3 {
 
 template <int D>
 __global__ __launch_bounds__(256) void k_ln_modulate(
-    const float* __restrict__ x, const float* __restrict__ mod, SegTable segs,
-    bf16* __restrict__ h, int M, float eps) {
+    const float* __restrict__ x, const float* __restrict__ mod, SegTable segs, RowGroups rg,
+    bf16* __restrict__ h, int rows, float eps) {
   constexpr int V = D / (kWave * 4);  // float4 per lane
   const int lane = threadIdx.x & 63;
-  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (row >= M) return;
+  const int wr = blockIdx.x * 4 + (threadIdx.x >> 6);   // workspace row
+  if (wr >= rows) return;
+  const RowMap g = row_map(rg, wr);
+  if (!g.live(wr)) return;
+  const int row = g.token(wr);
   const float4* xr = reinterpret_cast<const float4*>(x + (size_t)row * D);
   float4 v[V];
   float s = 0.f;
@@ -58,17 +63,20 @@ __global__ __launch_bounds__(256) void k_ln_modulate(
     o[1] = f2bf((1.0f + sc.y) * ((v[i].y - mean) * rstd) + sh.y);
     o[2] = f2bf((1.0f + sc.z) * ((v[i].z - mean) * rstd) + sh.z);
     o[3] = f2bf((1.0f + sc.w) * ((v[i].w - mean) * rstd) + sh.w);
-    *reinterpret_cast<bf16x4*>(h + packed_index(row, 4 * c, D)) = o;
+    *reinterpret_cast<bf16x4*>(h + packed_index(wr, 4 * c, D)) = o;
   }
 }
 
 // Generic width (any multiple of 256): loops instead of a register array.
 __global__ __launch_bounds__(256) void k_ln_modulate_any(
-    const float* __restrict__ x, const float* __restrict__ mod, SegTable segs,
-    bf16* __restrict__ h, int M, int D, float eps) {
+    const float* __restrict__ x, const float* __restrict__ mod, SegTable segs, RowGroups rg,
+    bf16* __restrict__ h, int rows, int D, float eps) {
   const int lane = threadIdx.x & 63;
-  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (row >= M) return;
+  const int wr = blockIdx.x * 4 + (threadIdx.x >> 6);   // workspace row
+  if (wr >= rows) return;
+  const RowMap g = row_map(rg, wr);
+  if (!g.live(wr)) return;
+  const int row = g.token(wr);
   const float* xr = x + (size_t)row * D;
   float s = 0.f;
   for (int c = lane; c < D; c += 64) s += xr[c];
@@ -85,7 +93,7 @@ __global__ __launch_bounds__(256) void k_ln_modulate_any(
   const float* shift = mod + (size_t)sg * 3 * D;
   const float* scale = shift + D;
   for (int c = lane; c < D; c += 64)
-    h[packed_index(row, c, D)] = f2bf((1.0f + scale[c]) * ((xr[c] - mean) * rstd) + shift[c]);
+    h[packed_index(wr, c, D)] = f2bf((1.0f + scale[c]) * ((xr[c] - mean) * rstd) + shift[c]);
 }
 
 // Rowwise-fp8 output (blocks with e4m3 weights): the same h values in fp32,
@@ -96,8 +104,8 @@ __global__ __launch_bounds__(256) void k_ln_modulate_any(
 template <int V>
 __device__ __forceinline__ void ln_row_f8(const float* __restrict__ x, const float* __restrict__ mod,
                                           const SegTable& segs, uint8_t* __restrict__ h8,
-                                          float* __restrict__ sh, int row, int D, int nv,
-                                          float eps) {
+                                          float* __restrict__ sh, int row, int wr, int D,
+                                          int nv, float eps) {
   const int lane = threadIdx.x & 63;
   const float4* xr = reinterpret_cast<const float4*>(x + (size_t)row * D);
   float4 v[V > 0 ? V : 1];
@@ -147,19 +155,21 @@ __device__ __forceinline__ void ln_row_f8(const float* __restrict__ x, const flo
 #pragma unroll
   for (int i = 0; i < (V > 0 ? V : nv); ++i) {
     const float4 h = V > 0 ? v[i] : hval(i);
-    *reinterpret_cast<uint32_t*>(h8 + packed8_index(row, 4 * (lane + 64 * i), D)) =
+    *reinterpret_cast<uint32_t*>(h8 + packed8_index(wr, 4 * (lane + 64 * i), D)) =
         e4m3x4(h.x, h.y, h.z, h.w, mult);
   }
-  if (lane == 0) sh[row] = rscale;
+  if (lane == 0) sh[wr] = rscale;
 }
 
 template <int V>
 __global__ __launch_bounds__(256) void k_ln_modulate_f8(
-    const float* __restrict__ x, const float* __restrict__ mod, SegTable segs,
-    uint8_t* __restrict__ h8, float* __restrict__ sh, int M, int D, float eps) {
-  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (row >= M) return;
-  ln_row_f8<V>(x, mod, segs, h8, sh, row, D, D / 256, eps);
+    const float* __restrict__ x, const float* __restrict__ mod, SegTable segs, RowGroups rg,
+    uint8_t* __restrict__ h8, float* __restrict__ sh, int rows, int D, float eps) {
+  const int wr = blockIdx.x * 4 + (threadIdx.x >> 6);   // workspace row
+  if (wr >= rows) return;
+  const RowMap g = row_map(rg, wr);
+  if (!g.live(wr)) return;
+  ln_row_f8<V>(x, mod, segs, h8, sh, g.token(wr), wr, D, D / 256, eps);
 }
 
 hipError_t launch_ln_modulate_f8(const BlockShape& bs, const float* x, const float* mod,
@@ -168,15 +178,18 @@ hipError_t launch_ln_modulate_f8(const BlockShape& bs, const float* x, const flo
   SegTable st;
   for (int i = 0; i < kMaxSegs; ++i) st.start[i] = segs.start[i];
   st.n = segs.n;
-  const unsigned blocks = (unsigned)((bs.M + 3) / 4);
+  if (!rows_valid(bs)) return hipErrorInvalidValue;
+  // one group stops at its last token; several cover every workspace row
+  const int rows = bs.rg.n == 1 ? bs.rg.ws_start[0] + bs.rg.count[0] : bs.rows;
+  const unsigned blocks = (unsigned)((rows + 3) / 4);
   if (blocks == 0) return hipSuccess;
   uint8_t* out = static_cast<uint8_t*>(h8);
   if (bs.D == 3072)
-    hipLaunchKernelGGL(k_ln_modulate_f8<12>, dim3(blocks), dim3(256), 0, s, x, mod, st, out, sh,
-                       bs.M, bs.D, eps);
+    hipLaunchKernelGGL(k_ln_modulate_f8<12>, dim3(blocks), dim3(256), 0, s, x, mod, st, bs.rg, out,
+                       sh, rows, bs.D, eps);
   else
-    hipLaunchKernelGGL(k_ln_modulate_f8<0>, dim3(blocks), dim3(256), 0, s, x, mod, st, out, sh,
-                       bs.M, bs.D, eps);
+    hipLaunchKernelGGL(k_ln_modulate_f8<0>, dim3(blocks), dim3(256), 0, s, x, mod, st, bs.rg, out,
+                       sh, rows, bs.D, eps);
   return hipGetLastError();
 }
 
@@ -186,14 +199,17 @@ hipError_t launch_ln_modulate(const BlockShape& bs, const float* x,
   SegTable st;
   for (int i = 0; i < kMaxSegs; ++i) st.start[i] = segs.start[i];
   st.n = segs.n;
-  const unsigned blocks = (unsigned)((bs.M + 3) / 4);
+  if (!rows_valid(bs)) return hipErrorInvalidValue;
+  // one group stops at its last token; several cover every workspace row
+  const int rows = bs.rg.n == 1 ? bs.rg.ws_start[0] + bs.rg.count[0] : bs.rows;
+  const unsigned blocks = (unsigned)((rows + 3) / 4);
   if (blocks == 0) return hipSuccess;
   if (bs.D == 3072) {
     hipLaunchKernelGGL(k_ln_modulate<3072>, dim3(blocks), dim3(256), 0, s, x,
-                       mod, st, reinterpret_cast<bf16*>(h), bs.M, eps);
+                       mod, st, bs.rg, reinterpret_cast<bf16*>(h), rows, eps);
   } else {
     hipLaunchKernelGGL(k_ln_modulate_any, dim3(blocks), dim3(256), 0, s, x,
-                       mod, st, reinterpret_cast<bf16*>(h), bs.M, bs.D, eps);
+                       mod, st, bs.rg, reinterpret_cast<bf16*>(h), rows, bs.D, eps);
   }
   return hipGetLastError();
 }

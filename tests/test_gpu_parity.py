@@ -254,6 +254,54 @@ def test_stack_stage1_streams_independent_on_gpu():
     assert not np.array_equal(a[:48], b[:48])
 
 
+# [200 text | 16x16 image | 12x20 reference] = 696 tokens: each stream padded
+# to 256 rows fills the 768-row workspace exactly, so the per-mode stage runs
+# as one launch sequence per block with a row group per stream; the layout of
+# the two tests above (208 tokens, 256 workspace rows) takes one sequence per
+# stream instead.
+GROUPED = synth.RopeLayout(200, 16, 16, ((12, 20),))
+
+
+def _stage1_launches(dims, layout, segs, pm, x, m1):
+    F.profile_reset()
+    F.profile_enable(True)
+    try:
+        out = _run_stack(dims, layout, segs, pm, [], x, m1, m1, False)
+    finally:
+        F.profile_enable(False)
+    return out, F.profile_read("gemm_proj")["launches"], F.profile_read("attention")["launches"]
+
+
+def test_stack_stage1_grouped_launch():
+    """The per-mode stage as grouped launches: full depth against the
+    oracle, streams still independent, and one projection launch per block
+    (an attention launch per stream)."""
+    dims = SMALL
+    segs, pm, jt, x, m1, m2 = _stack_inputs(dims, GROUPED, 5, 2, seed=27)
+    got = _run_stack(dims, GROUPED, segs, pm, jt, x, m1, m2, False)
+    want = O.stack_forward(x, pm, jt, seg_tuples(segs), m1, m2, oracle_rope(GROUPED))
+    assert_close_stack(got, want, x, "grouped stack")
+    a, n_proj, n_attn = _stage1_launches(dims, GROUPED, segs, pm, x, m1)
+    assert (n_proj, n_attn) == (5, 15)
+    x2 = x.copy()
+    x2[:200] += 1.0
+    b = _run_stack(dims, GROUPED, segs, pm, [], x2, m1, m1, False)
+    np.testing.assert_array_equal(a[200:], b[200:])
+    assert not np.array_equal(a[:200], b[:200])
+    want1 = O.stack_forward(x, pm, [], seg_tuples(segs), m1, m1, oracle_rope(GROUPED))
+    assert_close_stack(a, want1, x, "grouped stage 1")
+
+
+def test_stack_stage1_per_stream_fallback_launches():
+    """Streams whose padded rows exceed the workspace run one launch
+    sequence per stream."""
+    dims = SMALL
+    layout = synth.RopeLayout(48, 8, 10, ((8, 10),))
+    segs, pm, jt, x, m1, m2 = _stack_inputs(dims, layout, 2, 0, seed=29)
+    _, n_proj, n_attn = _stage1_launches(dims, layout, segs, pm, x, m1)
+    assert (n_proj, n_attn) == (6, 6)
+
+
 def test_per_mode_block_equals_single_segment_block():
     """A stack with one per-mode block and no joint blocks equals
     block_forward on each stream alone."""
