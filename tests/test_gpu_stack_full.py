@@ -22,7 +22,8 @@ import latent_flow_matching_flux_amd as F
 import synth
 from oracle import flux3_oracle as O
 
-from gpu_util import DEV, assert_close_stack, rope_dev, seg_tuples, upload_weights, workspace
+from gpu_util import (DEV, assert_close, assert_close_stack, rope_dev, seg_tuples, upload_weights,
+                      workspace)
 from stack_inputs import clear_cache, stack_inputs
 
 pytestmark = pytest.mark.gpu
@@ -89,3 +90,89 @@ def test_full_stack_all_rows(name):
                            dtype=np.float32)
     print(f"[stack] {name}: oracle {time.time() - t0:.1f} s on {O.THREADS} threads", flush=True)
     assert_close_stack(got, want, x, f"stack {name}")
+
+
+@pytest.mark.timeout(900)
+def test_stack_t2i4k65776_composition():
+    """The 5 + 28 stack at 65,776 tokens [240 text | 256x256 image] (4096^2
+    px), where an oracle stack does not finish in test time.  Checked
+    instead: (1) the stack call equals its blocks enqueued one at a time (5
+    stack calls of one per-mode block, then 28 block calls) bit for bit, so
+    it runs every block in order with its weights and modulation; (2) the
+    first per-mode block -- both streams in one grouped launch -- given the
+    device's input, matches the oracle's per-stream block on every text row
+    and on sampled image rows; (3) so does the last joint block on sampled
+    rows of the whole sequence."""
+    dims = synth.DIMS
+    layout = synth.workload("t2i4k65776").layout
+    n = layout.n_tokens
+    seed = 45
+    segs, pm, jt, x, m1, m2 = stack_inputs(dims, layout, 5, 28, seed=seed)
+    print(f"[stack] t2i4k65776: {n} tokens, seed {seed}, segments {seg_tuples(segs)}", flush=True)
+    dev = {}
+
+    def dev_w(w):
+        if id(w) not in dev:
+            dev[id(w)] = upload_weights(w)
+        return dev[id(w)]
+
+    pm_d = {m: [dev_w(w) for w in ws] for m, ws in pm.items()}
+    jt_d = [dev_w(w) for w in jt]
+    m1d = torch.from_numpy(np.ascontiguousarray(m1)).to(DEV)
+    m2d = torch.from_numpy(np.ascontiguousarray(m2)).to(DEV)
+    rope = rope_dev(layout)
+    ws = workspace(dims, n)
+    x0 = torch.from_numpy(x).to(DEV)
+
+    xs = x0.clone()
+    F.stack_forward(dims, pm_d, jt_d, xs, segs, m1d, m2d, rope, ws)
+    torch.cuda.synchronize()
+    got_stack = xs.cpu().numpy()
+    del xs
+
+    xc = x0.clone()
+    x_after_pm0 = x_before_last = None
+    for b in range(5):
+        F.stack_forward(dims, {m: [ws_[b]] for m, ws_ in pm_d.items()}, [], xc, segs, m1d, m2d,
+                        rope, ws)
+        if b == 0:
+            torch.cuda.synchronize()
+            x_after_pm0 = xc.cpu().numpy()
+    for b in range(28):
+        if b == 27:
+            torch.cuda.synchronize()
+            x_before_last = xc.cpu().numpy()
+        F.block_forward(dims, jt_d[b], xc, segs, m2d, rope, ws)
+    torch.cuda.synchronize()
+    got_chain = xc.cpu().numpy()
+    del xc, x0, ws, dev, pm_d, jt_d
+    torch.cuda.empty_cache()
+    assert np.all(np.isfinite(got_stack))
+    np.testing.assert_array_equal(got_stack, got_chain)
+
+    t0 = time.time()
+    rope_o = O.rope_tables(O.token_positions(layout.n_text, layout.grid_h, layout.grid_w,
+                                             layout.refs, layout.hw_scale), layout.theta)
+    rng = np.random.default_rng(seed)
+    n_text = segs[0].count
+    # first per-mode block: each stream alone, from the stack's input
+    text_rows = np.arange(n_text)
+    want = O.block_forward_rows(x[:n_text], _f32(pm[0][0]), [(0, n_text, 0)], m1[0:1],
+                                rope_o[:n_text], text_rows, dtype=np.float32, attn_chunk=16)
+    assert_close(x_after_pm0[:n_text], want, "t2i4k65776 per-mode block 0, text rows")
+    n_img = n - n_text
+    img_rows = np.unique(np.concatenate([[0, 1, 255, 256, n_img - 1],
+                                         rng.choice(n_img, 27, replace=False)]))
+    want = O.block_forward_rows(x[n_text:], _f32(pm[1][0]), [(0, n_img, 1)], m1[1:2],
+                                rope_o[n_text:], img_rows, dtype=np.float32, attn_chunk=16)
+    assert_close(x_after_pm0[n_text + img_rows], want, "t2i4k65776 per-mode block 0, image rows")
+    # last joint block over the whole sequence, from its device input
+    rows = np.unique(np.concatenate([[0, n_text - 1, n_text, n - 1],
+                                     rng.choice(n, 28, replace=False)]))
+    want = O.block_forward_rows(x_before_last, _f32(jt[27]), seg_tuples(segs), m2, rope_o, rows,
+                                dtype=np.float32, attn_chunk=16)
+    assert_close(got_stack[rows], want, "t2i4k65776 joint block 27, sampled rows")
+    assert_close(got_stack[rows] - x_before_last[rows], want - x_before_last[rows],
+                 "t2i4k65776 joint block 27 delta")
+    print(f"[stack] t2i4k65776: oracle rows {time.time() - t0:.1f} s on {O.THREADS} threads",
+          flush=True)
