@@ -81,13 +81,11 @@ struct Acc {
   f32x16 c[4][4];
 };
 
-// Tile coordinates for workgroup id b: XCD-major (ids b, b+8, ... share an
-// XCD) and grouped GROUP_M M-tiles at a time within each XCD's range.
-__device__ __forceinline__ void tile_coords(int b, int n_m, int n_n, int& mt,
-                                            int& nt) {
-  const int total = n_m * n_n;
-  const int per = total / 8;
-  const int lin = (b < per * 8) ? (b % 8) * per + b / 8 : b;
+// Tile coordinates of linear tile index lin: GROUP_M M-tiles at a time,
+// M fastest within a group.  tile_coords below gives workgroup id b its
+// tile: XCD-major (ids b, b+8, ... share an XCD and take consecutive linear
+// indices of one region of total / 8), so one XCD's tiles are neighbours.
+__device__ __forceinline__ void lin_coords(int lin, int n_m, int n_n, int& mt, int& nt) {
   const int group = GROUP_M * n_n;
   const int g = lin / group;
   const int first_m = g * GROUP_M;
@@ -95,6 +93,30 @@ __device__ __forceinline__ void tile_coords(int b, int n_m, int n_n, int& mt,
   const int in = lin - g * group;
   mt = first_m + in % gm;
   nt = in / gm;
+}
+
+__device__ __forceinline__ void tile_coords(int b, int n_m, int n_n, int& mt,
+                                            int& nt) {
+  const int total = n_m * n_n;
+  const int per = total / 8;
+  lin_coords((b < per * 8) ? (b % 8) * per + b / 8 : b, n_m, n_n, mt, nt);
+}
+
+// Linear index of the t-th tile left after workgroup ids [0, tile0) took
+// theirs through tile_coords: those ids fill, in region x = [x per, (x + 1)
+// per), its first ceil((min(tile0, 8 per) - x) / 8) indices and, past the
+// regions, every index below tile0; the rest is taken region by region, in
+// increasing order.
+__device__ __forceinline__ int tail_lin(int t, int total, int tile0) {
+  const int per = total / 8;
+  const int m8 = min(tile0, 8 * per);
+#pragma unroll
+  for (int x = 0; x < 8; ++x) {
+    const int done = (m8 - x + 7) / 8;
+    if (t < per - done) return x * per + done + t;
+    t -= per - done;
+  }
+  return max(8 * per, tile0) + t;
 }
 
 // Where this wave's share of one operand tile comes from: wave w loads tile
@@ -737,6 +759,12 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_gemm_proj(ProjArgs p) {
   }
 }
 
+// One sub-round of K4's tail: tail tiles [first, first + tiles), each cut
+// into `pieces` ranges of k slices.
+struct TailRound {
+  int first, tiles, pieces;
+};
+
 struct OutArgs {
   const bf16* cat;     // packed bf16 [o | act], or its packed e4m3 codes (F8)
   // weight sets; a tile takes the set of its row group
@@ -753,21 +781,10 @@ struct OutArgs {
   int nk, nk0;       // k slices of a tile, of them from wo
   int groups;        // persistent workgroups G
   int dp_rounds;     // whole-tile rounds before the split tail
-  int tail;          // tiles left to the stream-K split (0: none)
+  int tail;          // tiles left to the k-piece sub-rounds (0: none)
+  TailRound tr0, tr1;   // the sub-rounds (tr1.tiles == 0: one sub-round)
 };
 
-// Work split of K4 over G persistent workgroups.  Tiles are numbered in the
-// XCD-grouped order of tile_coords.  The first dp_rounds * G of them go
-// whole, G at a time (the workgroups of one XCD then walk the same k
-// slices of neighbouring tiles together and share them in L2).  The last
-// `tail` tiles, when they would leave over 15% of a round idle, are split
-// stream-K fashion: their k slices, laid end to end (tail tile t owns
-// slices [t nk, (t + 1) nk)), are cut into G equal ranges, range v from
-// start(v) = floor(v total / G).  A tail tile one range covers whole gets
-// its epilogue at once; a tile cut by range boundaries is summed afterwards
-// by the fixup kernel from the partials of its ranges, in k order.  A
-// range's first segment writes slot 2v, its last (when it is another tile)
-// slot 2v + 1.
 // gate_s row of the segment holding token m.
 __device__ __forceinline__ const float* gate_row(const OutArgs& p, int m) {
   return p.mod + (size_t)seg_of(p.segs, m) * 3 * p.D + 2 * p.D;
@@ -858,6 +875,19 @@ __device__ __forceinline__ void out_tile_ptrs(const OutArgs& p, int m0, int n0, 
   B1.ld = PW ? 8 * F : F;
 }
 
+// Work split of K4 over G persistent workgroups.  Tiles are numbered in the
+// XCD-grouped order of tile_coords.  The first dp_rounds * G of them go
+// whole, G at a time (the workgroups of one XCD then walk the same k
+// slices of neighbouring tiles together and share them in L2).  The `tail`
+// tiles left, when they would leave over a set share of a round idle, run
+// as one or two sub-rounds of k pieces: sub-round s cuts tail tiles [first,
+// first + tiles) into `pieces` equal k ranges, and its item i < tiles *
+// pieces -- piece i / tiles of tail tile first + i % tiles -- runs on the
+// workgroup of range index i (range_of_block), so each XCD's workgroups run
+// one k range of neighbouring tiles in step and still share slices in L2.
+// Item i leaves its partial tile in slot s G + i; the fixup kernel sums a
+// tile's pieces in k order and applies the epilogue.  Tail tiles are taken
+// in increasing linear index (tail_lin), which keeps them neighbours too.
 // F8: cat and the weights are rowwise e4m3 codes in the packed fp8 layout;
 // every product tile is scaled back by the row scales as soon as its main
 // loop ends, so whole tiles, partial tiles and the fixup see plain sums.
@@ -874,38 +904,29 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_gemm_out(OutArgs p) {
   const int n_tiles = n_m * n_n;
   const int nk = p.nk;
   const int G = p.groups;
-  // this workgroup's tail range (empty without a tail)
-  SplitK sk;
-  sk.nk = nk;
-  sk.G = G;
-  sk.total = (int64_t)p.tail * nk;
   const int tile0 = p.dp_rounds * G;
   const int v = range_of_block(blockIdx.x, G);
-  int64_t s = 0, s_end = 0;
-  if (p.tail > 0) {
-    s = sk.start(v);
-    s_end = sk.start(v + 1);
-  }
-  // one loop over the work items -- whole tiles, then the tail range's
-  // segments -- so that the main loop is instantiated once
-  int r = 0;
+  // one loop over the work items -- whole tiles, then this workgroup's item
+  // of each tail sub-round -- so that the main loop is instantiated once
+  int r = 0, sr = 0;
   bool first = true;
   for (;;) {
-    int mt, nt, kb, ke, tt = 0;
+    int mt, nt, kb = 0, ke = nk, slot = -1;
     if (r < p.dp_rounds && r * G + (int)blockIdx.x < n_tiles) {
       tile_coords(r * G + blockIdx.x, n_m, n_n, mt, nt);
-      kb = 0;
-      ke = nk;
       ++r;
-    } else if (s < s_end) {
-      r = p.dp_rounds;
-      tt = (int)(s / nk);
-      kb = (int)(s - (int64_t)tt * nk);
-      ke = (int)min<int64_t>(nk, kb + (s_end - s));
-      tile_coords(tile0 + tt, n_m, n_n, mt, nt);
-      s += ke - kb;
     } else {
-      break;
+      r = p.dp_rounds;
+      if (sr == 0 && v >= p.tr0.tiles * p.tr0.pieces) sr = 1;
+      if (sr == 1 && v >= p.tr1.tiles * p.tr1.pieces) sr = 2;
+      if (sr == 2) break;
+      const TailRound tr = sr == 0 ? p.tr0 : p.tr1;
+      const int piece = v / tr.tiles;
+      lin_coords(tail_lin(tr.first + v % tr.tiles, n_tiles, tile0), n_m, n_n, mt, nt);
+      kb = piece * nk / tr.pieces;
+      ke = (piece + 1) * nk / tr.pieces;
+      slot = sr * G + v;
+      ++sr;
     }
     const RowMap grp = row_map(p.rg, mt * BM);
     Src A, B0, B1;
@@ -919,10 +940,10 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_gemm_out(OutArgs p) {
       const float* const a_run[4] = {a0, a0 + 32, a0 + 64, a0 + 96};
       scale_acc(acc, a_run, p.sw[grp.w] + nt * BN + wn * 128, lane);
     }
-    if (kb == 0 && ke == nk) {
+    if (slot < 0) {
       out_epilogue(p, acc, mt * BM, nt * BN, wm, wn, lane, grp);
     } else {
-      float4* dst = slot_base(p, sk.slot(v, tt)) + (size_t)wave * 64 * 64 + lane;
+      float4* dst = slot_base(p, slot) + (size_t)wave * 64 * 64 + lane;
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -939,34 +960,26 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_gemm_out(OutArgs p) {
 
 constexpr int FIX_SPLIT = 16;   // fixup workgroups per split tile
 
-// Sums the partials of every tail tile cut by a range boundary, in k order,
-// and applies the epilogue.  Workgroups (i, c) look at the boundary between
-// ranges i and i + 1 and take part c of its tile if no earlier boundary
-// falls inside the tile.  A thread takes the float4s of four neighbouring
-// lanes of one accumulator group -- 4 rows x 4 consecutive columns, 64
-// contiguous bytes of a slot -- so that it updates x with float4 accesses;
-// x and gate are loaded before the partials are summed.
+// Sums the k pieces of every tail tile in k order and applies the
+// epilogue; FIX_SPLIT workgroups share a tile.  A thread takes the float4s
+// of four neighbouring lanes of one accumulator group -- 4 rows x 4
+// consecutive columns, 64 contiguous bytes of a slot -- so that it updates x
+// with float4 accesses; x and gate are loaded before the partials are
+// summed.
 __global__ __launch_bounds__(NTHREADS) void k_gemm_out_fixup(OutArgs p) {
   const int n_n = p.D / BN;
   const int n_m = p.rows / BM;
-  SplitK sk;
-  sk.nk = p.nk;
-  sk.G = p.groups;
-  sk.total = (int64_t)p.tail * sk.nk;
-  const int i = blockIdx.x / FIX_SPLIT, chunk = blockIdx.x % FIX_SPLIT;
-  const int64_t b = sk.start(i + 1);
-  if (b % sk.nk == 0) return;                       // boundary on a tile edge
-  const int tt = (int)(b / sk.nk);
-  if (sk.start(i) > (int64_t)tt * sk.nk) return;    // an earlier boundary owns the tile
-  const int v_first = sk.range_of((int64_t)tt * sk.nk);
-  const int v_last = sk.range_of((int64_t)(tt + 1) * sk.nk - 1);
+  const int tt = blockIdx.x / FIX_SPLIT, chunk = blockIdx.x % FIX_SPLIT;
+  const bool second = p.tr1.tiles > 0 && tt >= p.tr1.first;
+  const TailRound tr = second ? p.tr1 : p.tr0;
+  const int slot0 = (second ? p.groups : 0) + (tt - tr.first);
 
   // float4 f0 .. f0 + 3 of the slot: lanes l0 .. l0 + 3 of group (w, q)
   const int f0 = 4 * (chunk * NTHREADS + threadIdx.x);
   const int l0 = f0 & 63, q = (f0 >> 6) & 63, w = f0 >> 12;
   const int ij = q >> 2, g = q & 3, ii = ij >> 2, jj = ij & 3;
   int mt, nt;
-  tile_coords(p.dp_rounds * p.groups + tt, n_m, n_n, mt, nt);
+  lin_coords(tail_lin(tt, n_m * n_n, p.dp_rounds * p.groups), n_m, n_n, mt, nt);
   const int m = mt * BM + (w >> 1) * 128 + ii * 32 + 8 * g + 4 * (l0 >> 5);   // workspace row
   const int n = nt * BN + (w & 1) * 128 + jj * 32 + (l0 & 31);
   const RowMap grp = row_map(p.rg, mt * BM);
@@ -980,9 +993,8 @@ __global__ __launch_bounds__(NTHREADS) void k_gemm_out_fixup(OutArgs p) {
   float4 sum[4];
 #pragma unroll
   for (int u = 0; u < 4; ++u) sum[u] = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int v = v_first; v <= v_last; ++v) {
-    if (sk.start(v + 1) == sk.start(v)) continue;   // empty range (fewer slices than ranges)
-    const float4* src = slot_base(p, sk.slot(v, tt)) + f0;
+  for (int piece = 0; piece < tr.pieces; ++piece) {
+    const float4* src = slot_base(p, slot0 + piece * tr.tiles) + f0;
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const float4 x = src[u];
@@ -1264,20 +1276,40 @@ hipError_t launch_gemm_out(const BlockShape& bs, const WeightSets& sets,
   const int G = p.groups;
   p.dp_rounds = n_tiles / G;
   p.tail = n_tiles % G;
-  // The leftover tiles run as one more round of whole tiles unless they are
-  // few.  A split slice costs about 1.6x (bf16) / 2x (fp8) a whole-tile one:
-  // split ranges do not walk the same slices as their XCD neighbours, so
-  // their operands come from the Infinity Cache instead of L2.  Measured
-  // per bf16 launch, split against whole: 240 tokens (12 tiles, 5% of a
-  // round) 70 us against 222 us; 8432 tokens (55%) 611 against 650; 4096
-  // tokens (75%) 306 against 314; 4336 tokens (80%) 392 against 316.  fp8
-  // prefers whole
-  // tiles from about half a round (8432 tokens: 328 split, 310 whole).
+  // The leftover tiles run as one more round of whole tiles unless they
+  // fill little enough of a round (threshold below); then as k-piece
+  // sub-rounds.  Measured per launch, sub-rounds against a whole round:
+  // bf16 8432 tokens (140 tiles, 55% of a round) 567 us against ~650 (an
+  // even stream-K split of the same tail, whose ranges start at scattered k
+  // offsets and share nothing in L2: 607); 4096 tokens (75%) 300 against
+  // 303; 4336 tokens (80%) 320 against 306; 240 tokens (12 tiles) 51 (the
+  // stream-K split: 67).  fp8 slices are half as long and favour whole
+  // tiles sooner: 8432 tokens 318 split, 304 whole.  Without a partial-slot
+  // region (ws.part null) every tile runs whole.
   const int split_pct = w.fp8 ? 45 : 78;
-  // without a partial-slot region (ws.part null) every tile runs whole
-  if (p.tail * 100 >= G * split_pct || ws.part == nullptr) {
+  if (p.tail * 100 >= G * split_pct || ws.part == nullptr || G < 2) {
+    p.dp_rounds += p.tail > 0 ? 1 : 0;
+    p.tail = 0;
+  }
+  // Sub-round plan: pieces = max(2, G / tiles left), as many tiles as that
+  // many pieces fit in G items, at least 4 k slices a piece.  Two sub-rounds
+  // always suffice: after the first (pieces 2, G / 2 tiles) fewer than G / 2
+  // tiles are left, and G / left pieces of each fit.
+  p.tr0 = TailRound{0, 0, 1};
+  p.tr1 = TailRound{0, 0, 1};
+  int left = p.tail, first = 0;
+  for (int sr = 0; sr < 2 && left > 0; ++sr) {
+    const int pieces = std::min(std::max(2, G / left), std::max(1, p.nk / 4));
+    const int tiles = std::min(left, G / pieces);
+    (sr == 0 ? p.tr0 : p.tr1) = TailRound{first, tiles, pieces};
+    first += tiles;
+    left -= tiles;
+  }
+  if (left > 0) {   // not reached with the plan above; run whole instead
     p.dp_rounds += 1;
     p.tail = 0;
+    p.tr0 = TailRound{0, 0, 1};
+    p.tr1 = TailRound{0, 0, 1};
   }
   if (w.fp8)
     hipLaunchKernelGGL((k_gemm_out<true, true>), dim3(G), dim3(NTHREADS), 0, s, p);
@@ -1286,8 +1318,8 @@ hipError_t launch_gemm_out(const BlockShape& bs, const WeightSets& sets,
   else
     hipLaunchKernelGGL((k_gemm_out<false, false>), dim3(G), dim3(NTHREADS), 0, s, p);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || p.tail == 0 || G < 2) return e;
-  hipLaunchKernelGGL(k_gemm_out_fixup, dim3((G - 1) * FIX_SPLIT), dim3(NTHREADS), 0, s, p);
+  if (e != hipSuccess || p.tail == 0) return e;
+  hipLaunchKernelGGL(k_gemm_out_fixup, dim3(p.tail * FIX_SPLIT), dim3(NTHREADS), 0, s, p);
   return hipGetLastError();
 }
 

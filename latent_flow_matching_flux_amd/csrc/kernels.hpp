@@ -70,7 +70,7 @@ struct WsPtrs {
   float* scat; // [n_pad]
 };
 
-// Upper bound on the persistent workgroups of the stream-K output GEMM (one
+// Upper bound on the persistent workgroups of the output GEMM (one
 // per CU, at most this many); the workspace holds two partial tiles for each.
 constexpr int kMaxSplitGroups = 256;
 constexpr size_t kSplitSlotBytes = 256 * 256 * 4;
