@@ -40,7 +40,6 @@ stays the bf16 stack.
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
 """
 import argparse
-import hashlib
 import json
 import os
 import sys
@@ -54,21 +53,12 @@ PEAK_FP8_TFLOPS = 5033.2       # 256 CU x 2.4 GHz x 8192 dense fp8 FLOP/clk/CU
 PEAK_HBM_GBS = 8000.0
 N_PM, N_JOINT = 5, 28
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_proj_edit8432_traffic.json")
-KERNEL_SOURCES = ("gemm.hip", "common.hpp")
 
 
 def gemm_flops_per_token(d):
     proj = 2 * d.width * (3 * d.width + 2 * d.mlp_hidden)
     out = 2 * (d.width + d.mlp_hidden) * d.width
     return proj, out
-
-
-def source_hash():
-    h = hashlib.sha256()
-    for name in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, "latent_flow_matching_flux_amd", "csrc", name), "rb") as f:
-            h.update(f.read())
-    return h.hexdigest()[:16]
 
 
 def measured_traffic(launch_tokens):
@@ -79,6 +69,7 @@ def measured_traffic(launch_tokens):
             t = json.load(f)
     except (OSError, ValueError):
         return None
+    from latent_flow_matching_flux_amd.profile_summary import source_hash
     if t.get("source_hash") != source_hash() or t.get("tokens") != launch_tokens:
         return None
     return t.get("bytes_per_launch")

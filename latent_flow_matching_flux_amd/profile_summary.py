@@ -3,6 +3,8 @@
     python -m latent_flow_matching_flux_amd.profile_summary trace DIR
     python -m latent_flow_matching_flux_amd.profile_summary pmc DIR [DIR ...]
     python -m latent_flow_matching_flux_amd.profile_summary report TRACE_DIR PMC_DIR ...
+    python -m latent_flow_matching_flux_amd.profile_summary traffic FETCH_DIR WRITE_DIR
+    python -m latent_flow_matching_flux_amd.profile_summary stack DIR
 
 `trace` reads the *_kernel_trace.csv files under DIR (rocprofv3
 --kernel-trace --output-format csv) and gives, per kernel and per grid size,
@@ -29,10 +31,26 @@ counters support:
 (the joint block at 8432 tokens) into one table per block kernel, with the
 algorithmic bytes of each kernel at that size beside the measured ones.
 
+`traffic` turns a FETCH_SIZE pass and a WRITE_SIZE pass of the same
+command into the JSON record `bench.py` reports as roofline.traffic (bytes
+per gemm_proj dispatch, each counter scaled by what it reads for the block
+input's plain device copy of known size), stamped with the sha256 prefix of
+the GEMM sources so that a record taken on other kernel code is not used.
+
+`stack` reads the kernel trace of a stack bench (`bench.py --no-block`) and
+groups the block kernels' launches by the block call they belong to, in
+launch order from the first k_rope_tables launch: a k_ln_modulate opens a
+call, the k_gemm_proj grid gives its rows (grid / 108 tiles per 256 rows at
+the model dims), and a call with several k_attention launches is a grouped
+per-mode call (one attention launch per stream, in stream order); calls
+whose LayerNorm is k_ln_modulate_f8 are the rowwise-FP8 ones.
+
 Kernel names are shortened to the function name (k_gemm_proj, ...).
 """
 import csv
 import glob
+import hashlib
+import json
 import os
 import re
 import statistics
@@ -46,12 +64,14 @@ SHADER_ENGINES = 32   # 8 XCDs x 4 shader engines
 
 
 def short(name):
-    m = re.search(r"(k_[a-z0-9_]+)", name)
+    m = re.search(r"(k_[a-z0-9_]+)(<(true|false), (true|false)>)?", name)
     if m:
         base = m.group(1)
-        t = re.search(r"ILb([01])ELb([01])E", name)
+        t = re.search(r"ILb([01])ELb([01])E", name)   # mangled names
         if t:
             base += f"<{'T' if t.group(1) == '1' else 'F'},{'T' if t.group(2) == '1' else 'F'}>"
+        elif m.group(2):
+            base += f"<{m.group(3)[0].upper()},{m.group(4)[0].upper()}>"
         return base
     return name.split("(")[0][:48]
 
@@ -152,14 +172,17 @@ def pmc(dirs):
                 print(f"- {n}: {v}")
 
 
-def _block_kernels(dirs):
+def _block_kernels(dirs, base_names=False):
     """Mean counter values per dispatch of each kernel's most frequent
-    launch shape, merged over the counter passes."""
+    launch shape, merged over the counter passes (keyed by the function
+    name alone with base_names)."""
     vals = defaultdict(lambda: defaultdict(list))
     for d in dirs:
         for r in _rows("*counter_collection.csv", d):
-            vals[(short(r["Kernel_Name"]), _grid(r))][r["Counter_Name"]].append(
-                float(r["Counter_Value"]))
+            k = short(r["Kernel_Name"])
+            if base_names:
+                k = k.split("<")[0]
+            vals[(k, _grid(r))][r["Counter_Name"]].append(float(r["Counter_Value"]))
     best = {}
     for (k, g), c in vals.items():
         n = max(len(v) for v in c.values())
@@ -174,11 +197,11 @@ def report(trace_dir, pmc_dirs, tokens=8432, D=3072, F=9216, H=24):
     dur = defaultdict(list)
     scratch = {}
     for r in rows:
-        k = short(r["Kernel_Name"])
+        k = short(r["Kernel_Name"]).split("<")[0]
         dur[k].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
         scratch[k] = max(scratch.get(k, 0), int(_get(r, "Private_Segment_Size", "Scratch_Size",
                                                      default="0")))
-    c = _block_kernels(pmc_dirs)
+    c = _block_kernels(pmc_dirs, base_names=True)
     n_pad = (tokens + 255) // 256 * 256
     mb = 1e6
     alg = {  # algorithmic HBM bytes per launch at this size
@@ -224,6 +247,114 @@ def report(trace_dir, pmc_dirs, tokens=8432, D=3072, F=9216, H=24):
               f"{a / mb if a else float('nan'):.1f} | {scratch.get(k, 0)} |")
 
 
+# the sources whose hash stamps a traffic record (bench.py checks the same)
+KERNEL_SOURCES = ("gemm.hip", "common.hpp")
+
+
+def source_hash():
+    h = hashlib.sha256()
+    here = os.path.dirname(os.path.abspath(__file__))
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(here, "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic(fetch_dir, write_dir, tokens=8432, D=3072, F=9216):
+    """JSON record of gemm_proj's HBM-side bytes per dispatch."""
+    c = _block_kernels([fetch_dir, write_dir], base_names=True)
+    copy = c["__amd_rocclr_copyBuffer"][2]
+    g, n, v = c["k_gemm_proj"]
+    nbytes = tokens * D * 4
+    fscale = nbytes / (copy["FETCH_SIZE"] * 1024)
+    wscale = nbytes / (copy["WRITE_SIZE"] * 1024)
+    n_pad = (tokens + 255) // 256 * 256
+    rec = {
+        "kernel": "gemm_proj",
+        "workload": f"joint block over the {tokens}-token edit sequence (bench.py --block-only: "
+                    f"5 warm-up + 20 timed calls)",
+        "tokens": tokens,
+        "source_hash": source_hash(),
+        "dispatches": n,
+        "fetch_kib_mean": v["FETCH_SIZE"],
+        "write_kib_mean": v["WRITE_SIZE"],
+        "fetch_scale": fscale,
+        "write_scale": wscale,
+        "bytes_per_launch": v["FETCH_SIZE"] * 1024 * fscale + v["WRITE_SIZE"] * 1024 * wscale,
+        "memory_side_read_bytes": 32 * v.get("TCC_EA0_RDREQ_DRAM_32B", 0.0),
+        "algorithmic_bytes": float(n_pad * D * 2 + (3 * D + 2 * F) * D * 2 + 3 * n_pad * D * 2
+                                   + n_pad * F * 2),
+        "commands": [
+            f"rocprofv3 --pmc FETCH_SIZE TCC_EA0_RDREQ_DRAM_32B --output-format csv -d {fetch_dir} "
+            f"-o pmc3 -- python3 bench.py --block-only",
+            f"rocprofv3 --pmc WRITE_SIZE TCC_EA0_WRREQ_WRITE_DRAM_32B --output-format csv -d "
+            f"{write_dir} -o pmc4 -- python3 bench.py --block-only",
+            f"python -m latent_flow_matching_flux_amd.profile_summary traffic {fetch_dir} {write_dir}"],
+    }
+    print(json.dumps(rec, indent=1))
+
+
+BLOCK_KERNELS = ("k_ln_modulate", "k_quant_rows", "k_gemm_proj", "k_attention",
+                 "k_attention_fixup", "k_gemm_out", "k_gemm_out_fixup")
+
+
+def stack(d, n_n=108):
+    """Launches of a stack trace by block call (see the module docstring)."""
+    rows = sorted(_rows("*kernel_trace.csv", d), key=lambda r: int(r["Start_Timestamp"]))
+    start = next((i for i, r in enumerate(rows) if short(r["Kernel_Name"]) == "k_rope_tables"), 0)
+    rows = rows[start:]
+    by = defaultdict(list)
+    scratch = {}
+    order = []
+    call = []   # the current block call's launches: (kernel, duration)
+
+    def close():
+        if not call:
+            return
+        grid = next((g for k, _, g in call if k.startswith("k_gemm_proj")), 0)
+        tokens = grid // n_n * 256
+        n_attn = sum(1 for k, _, _ in call if k == "k_attention")
+        fp8 = any(k == "k_ln_modulate_f8" for k, _, _ in call)
+        label = (("fp8r, " if fp8 else "") + f"{tokens} rows"
+                 + (", per-mode (grouped)" if n_attn > 1 else ""))
+        a = 0
+        for k, dur, _ in call:
+            if k == "k_attention" and n_attn > 1:
+                a += 1
+            key = (k, label + (f", stream {a}" if k.startswith("k_attention") and n_attn > 1
+                               else ""))
+            if key not in by:
+                order.append(key)
+            by[key].append(dur)
+        call.clear()
+
+    for r in rows:
+        k = short(r["Kernel_Name"])
+        dur = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+        scratch[k] = max(scratch.get(k, 0), int(_get(r, "Private_Segment_Size", "Scratch_Size",
+                                                     default="0")))
+        base = k.split("<")[0]
+        if base == "k_ln_modulate" or base == "k_ln_modulate_f8":
+            close()
+        if base.startswith("k_ln_modulate") or (base in BLOCK_KERNELS and call):
+            call.append((k, dur, _grid(r)))
+        else:
+            close()   # any other launch ends the block call (weight quantisation at load, ...)
+            if (k, "-") not in by:
+                order.append((k, "-"))
+            by[(k, "-")].append(dur)
+    close()
+    total = sum(sum(v) for v in by.values())
+    print("| kernel | block call | launches | mean (us) | min (us) | max (us) | share of GPU time "
+          "| scratch B/lane |")
+    print("|---|---|---|---|---|---|---|---|")
+    for key in order:
+        k, label = key
+        v = by[key]
+        print(f"| {k} | {label} | {len(v)} | {statistics.mean(v):.1f} | {min(v):.1f} | "
+              f"{max(v):.1f} | {100 * sum(v) / total:.1f}% | {scratch[k]} |")
+
+
 if __name__ == "__main__":
     if len(sys.argv) >= 3 and sys.argv[1] == "trace":
         trace(sys.argv[2])
@@ -231,6 +362,10 @@ if __name__ == "__main__":
         pmc(sys.argv[2:])
     elif len(sys.argv) >= 4 and sys.argv[1] == "report":
         report(sys.argv[2], sys.argv[3:])
+    elif len(sys.argv) == 3 and sys.argv[1] == "stack":
+        stack(sys.argv[2])
+    elif len(sys.argv) == 4 and sys.argv[1] == "traffic":
+        traffic(sys.argv[2], sys.argv[3])
     else:
         print(__doc__)
         sys.exit(2)
