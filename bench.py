@@ -31,6 +31,10 @@ flux3_transformer_forward (input linears from 20,480-value text vectors and
 output layer) and one 16-step distilled flux3_sample over the same blocks.  Peak: the 2516.6 TFLOP/s of
 AMD's MI355X spec, next to CUs x clock x 4096 from the device query.
 
+"graph" replays the same step recorded once as a HIP graph (torch.cuda.graph
+over the library's launches): the same kernels without the host's launch
+gaps, its result checked bit for bit against the eager step.
+
 "fp8r" repeats the joint block and the step loop with the blocks' weights in
 the rowwise-FP8 form (flux3_weights_quantize_fp8r: e4m3 codes, one scale per
 output row; the GEMM inputs quantised per token inside each block), its GEMM
@@ -202,6 +206,30 @@ def time_whole_calls(F, dims, lay, segs, n, rand, per_mode, joint, emb_w, mod_w,
                     f"{steps} distilled steps (call + Euler step each), shift 6.93"}
 
 
+def time_graph_steps(torch, step, x, steps, passes, eager_ms):
+    """The step captured once as a HIP graph and replayed `steps` times: the
+    same kernels without the host's launch gaps.  The replayed result must
+    equal the eager step's bit for bit."""
+    want = x.clone()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    g.replay()
+    torch.cuda.synchronize()
+    assert torch.equal(x, want), "graph replay differs from the eager step"
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        g.replay()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms = (t1 - t0) / steps * 1e3
+    del g
+    return {"ms_per_step": ms, "block_tokens_per_s": passes / (ms * 1e-3),
+            "eager_over_graph": eager_ms / ms,
+            "what": "the same step (rope tables, both stages' modulation, x restore, 5+28 "
+                    "blocks) recorded once with torch.cuda.graph and replayed"}
+
+
 def cpu_baseline(workload_name, blocks=2):
     """The oracle, as it stands, on `blocks` joint blocks of the same
     workload: NumPy float32 with the BLAS library and the oracle's attention
@@ -312,14 +340,16 @@ def main():
     mws = torch.empty(F.modulation_workspace_bytes(dims), dtype=torch.uint8, device=dev)
     rope = torch.empty((n, 64, 2), dtype=torch.float32, device=dev)
     ws = torch.empty(F.workspace_bytes(dims, n), dtype=torch.uint8, device=dev)
-    stream = torch.cuda.current_stream()
 
     def step(pm=per_mode, jt=joint):
-        F.rope_tables_build(lay, rope, stream=stream)
-        F.modulation_forward(dims, mod_w[0], t_by_mode, segs, m1, mws, stream=stream)
-        F.modulation_forward(dims, mod_w[1], t_by_mode, segs, m2, mws, stream=stream)
+        # on the current stream: the launch stream, or the capture stream
+        # while the step is recorded as a graph
+        s = torch.cuda.current_stream()
+        F.rope_tables_build(lay, rope, stream=s)
+        F.modulation_forward(dims, mod_w[0], t_by_mode, segs, m1, mws, stream=s)
+        F.modulation_forward(dims, mod_w[1], t_by_mode, segs, m2, mws, stream=s)
         x.copy_(x0)
-        F.stack_forward(dims, pm, jt, x, segs, m1, m2, rope, ws, stream=stream)
+        F.stack_forward(dims, pm, jt, x, segs, m1, m2, rope, ws, stream=s)
 
     for _ in range(args.warmup):
         step()
@@ -344,6 +374,7 @@ def main():
 
     ms_per_step = (t1 - t0) / args.steps * 1e3
     passes = (N_PM + N_JOINT) * n
+    graph = time_graph_steps(torch, step, x, args.steps, passes, ms_per_step)
     value = passes / (ms_per_step / 1e3)
     proj_fpt, out_fpt = gemm_flops_per_token(dims)
 
@@ -499,6 +530,7 @@ def main():
         "whole_call": whole,
         "peak": peak,
         "roofline": roofline,
+        "graph": graph,
         "fp8r": fp8,
         "cpu_baseline": cpu,
     }
