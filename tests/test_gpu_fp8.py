@@ -368,11 +368,24 @@ def test_transformer_call_with_fp8_blocks():
     assert_close(got, want, "fp8 transformer velocity", maxabs_tol=3e-2 * max(1.0, rms))
 
 
-def test_stack_mixes_weight_layouts():
+# (layout, per-mode layout of block b for mode m, expected per-mode projection
+# launches): streams too long for one grouped launch; streams that fit, with
+# one layout per block (grouped launches in each layout); streams that fit
+# but whose modes' block-b weights differ in layout (one launch per stream)
+MIXED_CASES = {
+    "per_stream": (synth.RopeLayout(40, 6, 8, ((6, 8),)), lambda b, m: b, 9),
+    "grouped": (synth.RopeLayout(200, 16, 16, ((12, 20),)), lambda b, m: b, 3),
+    "modes_differ": (synth.RopeLayout(200, 16, 16, ((12, 20),)), lambda b, m: (b + m) % 3, 9),
+}
+
+
+@pytest.mark.parametrize("case", list(MIXED_CASES))
+def test_stack_mixes_weight_layouts(case):
     """One stack whose blocks come in all three layouts (Linear bf16, packed
-    bf16, rowwise FP8): each block follows its own weights' arithmetic."""
+    bf16, rowwise FP8): each block follows its own weights' arithmetic, in
+    grouped per-mode launches or one per stream."""
     dims = SMALL
-    layout = synth.RopeLayout(40, 6, 8, ((6, 8),))
+    layout, kind_of, pm_launches = MIXED_CASES[case]
     segs = layout.segments()
     n = layout.n_tokens
     kinds = ("linear", "packed", "fp8")
@@ -397,14 +410,21 @@ def test_stack_mixes_weight_layouts():
         keep.append((pw, buf))
         return pw
 
-    pm = {m: [dev(w, kinds[b]) for b, w in enumerate(ws)] for m, ws in pm_np.items()}
+    pm = {m: [dev(w, kinds[kind_of(b, m)]) for b, w in enumerate(ws)] for m, ws in pm_np.items()}
     jt = [dev(w, kinds[(b + 1) % 3]) for b, w in enumerate(jt_np)]
     x = torch.from_numpy(x_np).to(DEV)
-    F.stack_forward(dims, pm, jt, x, segs,
-                    torch.from_numpy(np.ascontiguousarray(m1, np.float32)).to(DEV),
-                    torch.from_numpy(np.ascontiguousarray(m2, np.float32)).to(DEV),
-                    rope_dev(layout), workspace(dims, n))
-    torch.cuda.synchronize()
+    F.profile_reset()
+    F.profile_enable(True)
+    try:
+        F.stack_forward(dims, pm, jt, x, segs,
+                        torch.from_numpy(np.ascontiguousarray(m1, np.float32)).to(DEV),
+                        torch.from_numpy(np.ascontiguousarray(m2, np.float32)).to(DEV),
+                        rope_dev(layout), workspace(dims, n))
+        torch.cuda.synchronize()
+    finally:
+        F.profile_enable(False)
+    assert F.profile_read("gemm_proj")["launches"] == pm_launches + 3
+    F.profile_reset()
     got = x.cpu().numpy()
 
     def block(xb, w, sg, md, rp, dtype=np.float64):
@@ -412,9 +432,9 @@ def test_stack_mixes_weight_layouts():
             return O.block_forward_fp8(xb, w, sg, md, rp, dtype=dtype)
         return O.block_forward(xb, w, sg, md, rp, dtype=dtype)
 
-    pm_o = {m: [oracle_fp8(w) if kinds[b] == "fp8" else w for b, w in enumerate(ws)]
+    pm_o = {m: [oracle_fp8(w) if kinds[kind_of(b, m)] == "fp8" else w for b, w in enumerate(ws)]
             for m, ws in pm_np.items()}
     jt_o = [oracle_fp8(w) if kinds[(b + 1) % 3] == "fp8" else w for b, w in enumerate(jt_np)]
     want = O.stack_forward(x_np, pm_o, jt_o, seg_tuples(segs), m1, m2, oracle_rope(layout),
                            block_fn=block)
-    assert_close_stack(got, want, x_np, "mixed-layout stack")
+    assert_close_stack(got, want, x_np, f"mixed-layout stack, {case}")
