@@ -8,6 +8,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 
 #include <vector>
@@ -19,7 +20,7 @@
 namespace {
 
 thread_local char g_detail[512] = "";
-int g_debug_sync = 0;
+std::atomic<int> g_debug_sync{0};   // process-wide; any thread may set it
 
 // Kernel timing records (flux3_profile_*), kept per calling thread.  The
 // HIP events of a record are created when its launch is enqueued with
@@ -213,7 +214,7 @@ flux3::BlockWeightsDev dev_weights(const flux3_block_weights& w) {
 
 flux3_status after_launch(hipError_t e, const char* what, hipStream_t s) {
   if (e != hipSuccess) return fail(FLUX3_E_HIP, "%s launch: %s", what, hipGetErrorString(e));
-  if (g_debug_sync) {
+  if (g_debug_sync.load(std::memory_order_relaxed)) {
     e = hipStreamSynchronize(s);
     if (e != hipSuccess) return fail(FLUX3_E_HIP, "%s execution: %s", what, hipGetErrorString(e));
   }
@@ -1095,7 +1096,7 @@ flux3_status flux3_device_query(int32_t device, flux3_device_info* out) {
   return ok();
 }
 
-void flux3_set_debug_sync(int32_t on) { g_debug_sync = on; }
+void flux3_set_debug_sync(int32_t on) { g_debug_sync.store(on, std::memory_order_relaxed); }
 
 void flux3_profile_enable(int32_t on) { g_prof_on = on != 0; }
 
