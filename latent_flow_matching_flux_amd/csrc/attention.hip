@@ -198,8 +198,9 @@ __device__ __forceinline__ float score(const STile& Sc, int idx, int key0, int M
 // MFMA j of tile t-1 (key block j/8, 16-key half (j/4)%2, dim block j%4)
 // with probabilities Pp.  Softmax of tile t (scores Sc -> Pc) rides along,
 // one exponential per slot against the current reference (odd slots pack
-// the pair to bf16 and add it to the sum), slot 31 checking the sum -- an
-// even share of VALU work beside every MFMA.  Every exp2(s - m_ref) is
+// the pair of two slots earlier to bf16 and add it to the sum; slot 31 also
+// the last pair), slot 31 checking the sum -- an even share of VALU work
+// beside every MFMA.  Every exp2(s - m_ref) is
 // bounded by the lane's sum
 // of them, so while that sum stays within 2^TAU no probability exceeds
 // 2^TAU and the tile needs no max; otherwise (or on NaN: the first tile,
@@ -231,7 +232,7 @@ __device__ __forceinline__ void region(STile& Sn, uint32_t k_off, f32x16 (&o)[4]
   static_for<0, PREFETCH>(load);
 
   float l = 0.f;
-  f32x2 pp;
+  f32x4 pq;   // the last four probabilities, by slot % 4
   static_for<0, 32>([&](auto ic) {
     constexpr int i = decltype(ic)::value;
     constexpr int j = i / 2;
@@ -248,18 +249,22 @@ __device__ __forceinline__ void region(STile& Sn, uint32_t k_off, f32x16 (&o)[4]
     }
     if constexpr (i + PREFETCH < 32) load(std::integral_constant<int, i + PREFETCH>{});
     if constexpr (SM) {
-      // one exponential per slot; odd slots pack the pair and add it
-      pp[i & 1] = __builtin_amdgcn_exp2f(
+      // one exponential per slot; odd slots pack the pair of two slots
+      // earlier, so the conversion never waits on an exponential just issued
+      pq[i & 3] = __builtin_amdgcn_exp2f(
           __builtin_fmaf(score<MASK>(Sc, i, key0, M, hh), scale, -st.m_ref));
-      if constexpr (i & 1) {
-        constexpr int idx = i - 1;
+      auto pack = [&](auto jc) {
+        constexpr int idx = decltype(jc)::value;
+        const f32x2 pp = {pq[idx & 3], pq[(idx + 1) & 3]};
         const bf16x2 pb = __builtin_convertvector(pp, bf16x2);
         // the running sum takes the bf16 probabilities the PV product uses
         l = __builtin_amdgcn_fdot2_f32_bf16(pb, kOnes2, l, false);
         uint32_t w = __builtin_bit_cast(uint32_t, pb);
         pin(w);
         Pc[idx >> 4][(idx >> 3) & 1][(idx & 7) >> 1] = w;
-      }
+      };
+      if constexpr ((i & 1) && i >= 3) pack(std::integral_constant<int, i - 3>{});
+      if constexpr (i == 31) pack(std::integral_constant<int, 30>{});
       if constexpr (i == 31) {
         st.moved = __any(!(l <= kTauExp));
         st.l_sum += st.moved ? 0.f : l;
