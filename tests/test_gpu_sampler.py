@@ -72,6 +72,10 @@ SAMPLE_CASES = {
     # model width 3072 with the 20,480-wide text linear, 80 text + 16x16
     # image tokens, 1 + 1 blocks, two distilled steps
     "full_width_distilled2": (synth.DIMS, synth.TEXT_DIM, synth.RopeLayout(80, 16, 16), 2, True),
+    # model width, the pages' 16 distilled steps on an edit layout
+    # [80 text | 16x16 image | 16x16 reference] (grouped per-mode blocks)
+    "full_width_edit_distilled16": (synth.DIMS, synth.TEXT_DIM,
+                                    synth.RopeLayout(80, 16, 16, ((16, 16),)), 16, True),
 }
 
 
