@@ -502,7 +502,8 @@ typedef struct {
   int64_t launches;
   double total_ms;
   double tokens;     /* sum of M over launches   */
-  double tokens_sq;  /* sum of M*M over launches */
+  double tokens_sq;  /* sum of M*M over launches; an attention launch over
+                        several equal-length streams adds each stream's M*M */
 } flux3_kernel_stats;
 void flux3_profile_enable(int32_t on);
 void flux3_profile_reset(void);

@@ -28,7 +28,7 @@ std::atomic<int> g_debug_sync{0};   // process-wide; any thread may set it
 struct ProfRec {
   int kind;
   hipEvent_t a, b;
-  double m;
+  double m, m2;   // tokens; sum of squared sequence lengths (attention work)
 };
 thread_local bool g_prof_on = false;
 thread_local std::vector<ProfRec> g_prof;
@@ -40,9 +40,10 @@ hipEvent_t new_event() {
 }
 
 // Records the start event of a launch when profiling; returns its index.
-int prof_begin(int kind, double m, hipStream_t s) {
+// m2 < 0 stands for m * m (one sequence of m tokens).
+int prof_begin(int kind, double m, hipStream_t s, double m2 = -1.0) {
   if (!g_prof_on) return -1;
-  ProfRec r{kind, new_event(), new_event(), m};
+  ProfRec r{kind, new_event(), new_event(), m, m2 < 0 ? m * m : m2};
   if (!r.a || !r.b || hipEventRecord(r.a, s) != hipSuccess) {
     if (r.a) (void)hipEventDestroy(r.a);
     if (r.b) (void)hipEventDestroy(r.b);
@@ -269,20 +270,24 @@ flux3_status run_block_groups(const flux3_dims* d, const flux3::WeightSets& sets
   e = flux3::launch_gemm_proj(bs, sets, rope, wp, kEpsRMS, s);
   prof_end(pi, s);
   if ((r = after_launch(e, "gemm_proj", s)) != FLUX3_OK) return r;
-  // attention within each group: its q, k, v^T and output rows start at the
-  // group's first workspace row (a multiple of 256, so the packed output
-  // layout shifts by whole row blocks)
+  // attention within each group, from the group's first workspace row (a
+  // multiple of 256, so the packed output layout shifts by whole row
+  // blocks); groups of equal length share a launch, whose units then cover
+  // heads x groups
+  bool done[16] = {};
   for (int g = 0; g < rg.n; ++g) {
-    flux3::WsPtrs wg = wp;
-    const size_t r0 = (size_t)rg.ws_start[g];
-    wg.q = static_cast<char*>(wp.q) + r0 * 128 * 2;
-    wg.k = static_cast<char*>(wp.k) + r0 * 128 * 2;
-    wg.vt = static_cast<char*>(wp.vt) + r0 * 2;
-    wg.cat = static_cast<char*>(wp.cat) + r0 * (size_t)(bs.D + bs.F) * 2;
+    if (done[g]) continue;
+    int32_t rows0[16];
+    int n_eq = 0;
+    for (int h = g; h < rg.n; ++h)
+      if (!done[h] && rg.count[h] == rg.count[g]) {
+        rows0[n_eq++] = rg.ws_start[h];
+        done[h] = true;
+      }
     flux3::BlockShape bg = bs;
     bg.M = rg.count[g];
-    pi = prof_begin(FLUX3_K_ATTENTION, (double)bg.M, s);
-    e = flux3::launch_attention(bg, wg, s);
+    pi = prof_begin(FLUX3_K_ATTENTION, (double)bg.M * n_eq, s, (double)bg.M * bg.M * n_eq);
+    e = flux3::launch_attention(bg, wp, rows0, n_eq, s);
     prof_end(pi, s);
     if ((r = after_launch(e, "attention", s)) != FLUX3_OK) return r;
   }
@@ -1125,7 +1130,7 @@ flux3_status profile_stats(int32_t kernel, int64_t m, flux3_kernel_stats* out) {
     st.launches += 1;
     st.total_ms += ms;
     st.tokens += r.m;
-    st.tokens_sq += r.m * r.m;
+    st.tokens_sq += r.m2;
   }
   *out = st;
   return ok();

@@ -8,7 +8,9 @@
 // 1/sqrt(128).
 //
 // Work split: a workgroup is 8 waves x 32 queries of one head, two waves per
-// SIMD.  A wave keeps its 32 queries in registers and computes
+// SIMD.  One launch attends within one sequence or within several of equal
+// length (streams of the per-mode stage sharing a launch): its heads are
+// then the model's heads times the sequences, each with its own first row.  A wave keeps its 32 queries in registers and computes
 // S^T = K . Q^T with the 32x32x16 bf16 MFMA, so every lane owns one query
 // (lane % 32) and 16 of each 32 keys; O^T = V^T . P^T then takes the
 // probabilities straight from those registers as the B operand (V arrives
@@ -63,7 +65,11 @@ struct AttnArgs {
   const bf16 *q, *k, *vt;
   bf16* out;         // cat buffer, packed operand layout of width ldo
   float* part;       // partial-result slots of split query blocks (256 KiB each)
-  int M, n_pad, H, ldo;
+  int M, n_pad, H, ldo;   // H: heads of the launch, heads x sequences
+  int heads;         // model heads
+  // first workspace row of each sequence of M tokens the launch attends
+  // within (several when equal-length streams share a launch)
+  int32_t seq_row[kMaxSegs];
   float scale_log2;  // log2(e) / sqrt(head_dim)
   int groups;        // persistent workgroups G
   int dp_rounds;     // whole-unit rounds before the split tail
@@ -83,6 +89,16 @@ __device__ __forceinline__ void unit_coords(int L, int nqb, int H, int& head, in
     head = L / nqb;
     qblk = L % nqb;
   }
+}
+
+// Launch head hl -> model head and the first workspace row of its sequence.
+__device__ __forceinline__ void head_rows(const AttnArgs& p, int hl, int& head, int& row0) {
+  const int sq = hl / p.heads;
+  head = hl - sq * p.heads;
+  row0 = 0;
+#pragma unroll
+  for (int i = 0; i < kMaxSegs; ++i)
+    if (sq == i) row0 = p.seq_row[i];
 }
 
 // Partial result of a split unit, in a 256-KiB slot: O (unnormalised, fp32)
@@ -316,14 +332,16 @@ __device__ __forceinline__ void settle(f32x16 (&o)[4], SoftState& st, const STil
 // [t0, t0 + nt): normalised into the concatenation buffer when slot is
 // null, else the unnormalised O with its m and l into the slot.
 __device__ __forceinline__ void attend(const AttnArgs& p, const lds_u8* smem, uint32_t lds0,
-                                       int head, int qblk, int t0, int nt, float* slot) {
+                                       int hl, int qblk, int t0, int nt, float* slot) {
   const int t = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6), lane = t & 63;
   const int r32 = lane & 31, hh = lane >> 5;
   const int q0 = qblk * AQ + wave * QW;
-  const bf16* qh = p.q + (size_t)head * p.n_pad * kHeadDim;
-  const bf16* kh = p.k + (size_t)head * p.n_pad * kHeadDim;
-  const bf16* vh = p.vt + (size_t)head * kHeadDim * p.n_pad;
+  int head, row0;
+  head_rows(p, hl, head, row0);
+  const bf16* qh = p.q + ((size_t)head * p.n_pad + row0) * kHeadDim;
+  const bf16* kh = p.k + ((size_t)head * p.n_pad + row0) * kHeadDim;
+  const bf16* vh = p.vt + (size_t)head * kHeadDim * p.n_pad + row0;
   const int M = p.M;
   const float sc = p.scale_log2;
   const int kbase = t0 * AKV;   // first key of the range
@@ -451,7 +469,7 @@ __device__ __forceinline__ void attend(const AttnArgs& p, const lds_u8* smem, ui
 #pragma unroll
         for (int e = 0; e < 4; ++e) v[e] = f2bf(o[d][4 * g + e] * inv);
         const int col = head * kHeadDim + d * 32 + 8 * g + 4 * hh;
-        *reinterpret_cast<bf16x4*>(p.out + packed_index(qi, col, p.ldo)) = v;
+        *reinterpret_cast<bf16x4*>(p.out + packed_index(row0 + qi, col, p.ldo)) = v;
       }
   }
 }
@@ -607,8 +625,9 @@ __global__ __launch_bounds__(64 * NW) void k_attention_fixup(AttnArgs p) {
       fold_piece(m, l, acc, mw, s_l[w][lane], ow);
     }
   }
-  int head, qblk;
-  unit_coords(p.dp_rounds * p.groups + u, nqb, p.H, head, qblk);
+  int hl, qblk, head, row0;
+  unit_coords(p.dp_rounds * p.groups + u, nqb, p.H, hl, qblk);
+  head_rows(p, hl, head, row0);
   const int qi = qblk * AQ + qw;
   if (qi >= p.M) return;
   const float inv = 1.0f / l;
@@ -623,13 +642,15 @@ __global__ __launch_bounds__(64 * NW) void k_attention_fixup(AttnArgs p) {
       o[2] = f2bf(x.z * inv);
       o[3] = f2bf(x.w * inv);
       const int col = head * kHeadDim + d * 32 + 8 * g + 4 * hh;
-      *reinterpret_cast<bf16x4*>(p.out + packed_index(qi, col, p.ldo)) = o;
+      *reinterpret_cast<bf16x4*>(p.out + packed_index(row0 + qi, col, p.ldo)) = o;
     }
 }
 
 }  // namespace
 
-hipError_t launch_attention(const BlockShape& bs, const WsPtrs& ws, hipStream_t s) {
+hipError_t launch_attention(const BlockShape& bs, const WsPtrs& ws, const int32_t* seq_row,
+                            int n_seq, hipStream_t s) {
+  if (n_seq < 1 || n_seq > kMaxSegs) return hipErrorInvalidValue;
   AttnArgs p;
   p.q = static_cast<const bf16*>(ws.q);
   p.k = static_cast<const bf16*>(ws.k);
@@ -638,12 +659,14 @@ hipError_t launch_attention(const BlockShape& bs, const WsPtrs& ws, hipStream_t 
   p.part = static_cast<float*>(ws.part);
   p.M = bs.M;
   p.n_pad = bs.n_pad;
-  p.H = bs.H;
+  p.heads = bs.H;
+  p.H = bs.H * n_seq;
+  for (int i = 0; i < kMaxSegs; ++i) p.seq_row[i] = i < n_seq ? seq_row[i] : 0;
   p.ldo = bs.D + bs.F;
   p.scale_log2 = 1.4426950408889634f / sqrtf((float)kHeadDim);
   const int nqb = (bs.M + AQ - 1) / AQ;
   const int nkv = (bs.M + AKV - 1) / AKV;
-  const int units = nqb * bs.H;
+  const int units = nqb * p.H;
   const int G = stream_k_groups();
   p.groups = G;
   p.dp_rounds = units / G;

@@ -168,8 +168,11 @@ hipError_t launch_quant_weight_rows(const void* a, int Ka, const void* b, int Kb
 hipError_t launch_gemm_proj(const BlockShape& bs, const WeightSets& w,
                             const float* rope, const WsPtrs& ws, float eps,
                             hipStream_t s);
-hipError_t launch_attention(const BlockShape& bs, const WsPtrs& ws,
-                            hipStream_t s);
+// Attention within n_seq sequences of bs.M tokens each, sequence i at
+// workspace rows [seq_row[i], seq_row[i] + bs.M) of q, k, v^T and the output
+// (n_seq <= 16; one sequence at row 0 for a plain block).
+hipError_t launch_attention(const BlockShape& bs, const WsPtrs& ws, const int32_t* seq_row,
+                            int n_seq, hipStream_t s);
 int stream_k_groups();
 hipError_t launch_gemm_out(const BlockShape& bs, const WeightSets& w,
                            const WsPtrs& ws, float* x, const float* mod,

@@ -292,6 +292,26 @@ def test_stack_stage1_grouped_launch():
     assert_close_stack(a, want1, x, "grouped stage 1")
 
 
+def test_stack_stage1_equal_streams_share_attention():
+    """Image and reference streams of equal length attend in one launch
+    (heads x streams), each within itself: full depth against the oracle,
+    one projection and two attention launches per per-mode block."""
+    dims = SMALL
+    layout = synth.RopeLayout(200, 16, 16, ((16, 16),))
+    segs, pm, jt, x, m1, m2 = _stack_inputs(dims, layout, 5, 2, seed=37)
+    got = _run_stack(dims, layout, segs, pm, jt, x, m1, m2, False)
+    want = O.stack_forward(x, pm, jt, seg_tuples(segs), m1, m2, oracle_rope(layout))
+    assert_close_stack(got, want, x, "equal streams stack")
+    a, n_proj, n_attn = _stage1_launches(dims, layout, segs, pm, x, m1)
+    assert (n_proj, n_attn) == (5, 10)
+    x2 = x.copy()
+    x2[200:456] += 1.0                       # the image stream only
+    b = _run_stack(dims, layout, segs, pm, [], x2, m1, m1, False)
+    np.testing.assert_array_equal(a[:200], b[:200])
+    np.testing.assert_array_equal(a[456:], b[456:])
+    assert not np.array_equal(a[200:456], b[200:456])
+
+
 def test_stack_stage1_per_stream_fallback_launches():
     """Streams whose padded rows exceed the workspace run one launch
     sequence per stream."""
