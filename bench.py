@@ -230,7 +230,7 @@ def time_graph_steps(torch, step, x, steps, passes, eager_ms):
                     "blocks) recorded once with torch.cuda.graph and replayed"}
 
 
-def cpu_baseline(workload_name, blocks=2):
+def cpu_baseline(workload_name, blocks=5):
     """The oracle, as it stands, on `blocks` joint blocks of the same
     workload: NumPy float32 with the BLAS library and the oracle's attention
     threads on the process's CPU share (at most 16 cores); value in block
