@@ -42,8 +42,8 @@ groups the block kernels' launches by the block call they belong to, in
 launch order from the first k_rope_tables launch: a k_ln_modulate opens a
 call, the k_gemm_proj grid gives its rows (grid / 108 tiles per 256 rows at
 the model dims), and a call with several k_attention launches is a grouped
-per-mode call (one attention launch per stream, in stream order); calls
-whose LayerNorm is k_ln_modulate_f8 are the rowwise-FP8 ones.
+per-mode call (one attention launch per stream length, in launch order);
+calls whose LayerNorm is k_ln_modulate_f8 are the rowwise-FP8 ones.
 
 Kernel names are shortened to the function name (k_gemm_proj, ...).
 """
@@ -321,8 +321,8 @@ def stack(d, n_n=108):
         for k, dur, _ in call:
             if k == "k_attention" and n_attn > 1:
                 a += 1
-            key = (k, label + (f", stream {a}" if k.startswith("k_attention") and n_attn > 1
-                               else ""))
+            key = (k, label + (f", attention launch {a} of {n_attn}"
+                               if k.startswith("k_attention") and n_attn > 1 else ""))
             if key not in by:
                 order.append(key)
             by[key].append(dur)
