@@ -122,9 +122,8 @@ __host__ __device__ __forceinline__ size_t packed8_index(size_t row, int k, int 
 }
 
 // Even split of a run of work items over G persistent workgroups (the
-// stream-K tails of the output GEMM and of attention).  Units of nk items
-// each (a GEMM tile's k slices, an attention query block's key tiles) lie
-// end to end, unit t owning items [t nk, (t + 1) nk); range v covers items
+// stream-K tail of attention).  Units of nk items each (an attention query
+// block's key tiles) lie end to end, unit t owning items [t nk, (t + 1) nk); range v covers items
 // [start(v), start(v + 1)) with start(v) = floor(v total / G).  A unit cut
 // by range boundaries leaves one partial result per range that touches it:
 // a range's first segment in slot 2v, its last (when in another unit) in

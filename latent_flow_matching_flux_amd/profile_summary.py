@@ -35,7 +35,8 @@ algorithmic bytes of each kernel at that size beside the measured ones.
 command into the JSON record `bench.py` reports as roofline.traffic (bytes
 per gemm_proj dispatch, each counter scaled by what it reads for the block
 input's plain device copy of known size), stamped with the sha256 prefix of
-the GEMM sources so that a record taken on other kernel code is not used.
+the GEMM sources' code (comments and whitespace ignored) so that a record
+taken on other kernel code is not used.
 
 `stack` reads the kernel trace of a stack bench (`bench.py --no-block`) and
 groups the block kernels' launches by the block call they belong to, in
@@ -251,12 +252,25 @@ def report(trace_dir, pmc_dirs, tokens=8432, D=3072, F=9216, H=24):
 KERNEL_SOURCES = ("gemm.hip", "common.hpp")
 
 
-def source_hash():
-    h = hashlib.sha256()
+def code_text(src):
+    """C++ source without comments and with whitespace runs collapsed, so
+    that a comment-only edit keeps the hash."""
+    src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+    src = re.sub(r"//[^\n]*", " ", src)
+    return " ".join(src.split())
+
+
+def source_hash(read=None):
+    """sha256 prefix of the GEMM sources' code (comments ignored); `read`
+    maps a file name to its text (default: the working tree)."""
     here = os.path.dirname(os.path.abspath(__file__))
+    if read is None:
+        def read(name):
+            with open(os.path.join(here, "csrc", name)) as f:
+                return f.read()
+    h = hashlib.sha256()
     for name in KERNEL_SOURCES:
-        with open(os.path.join(here, "csrc", name), "rb") as f:
-            h.update(f.read())
+        h.update(code_text(read(name)).encode())
     return h.hexdigest()[:16]
 
 
