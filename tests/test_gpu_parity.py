@@ -312,6 +312,18 @@ def test_stack_stage1_equal_streams_share_attention():
     assert not np.array_equal(a[200:456], b[200:456])
 
 
+def test_stack_grouped_per_block_modulation():
+    """Grouped per-mode launches with per-block modulation vectors
+    (mod_block_stride): each grouped block reads its own block's vectors
+    for every stream."""
+    dims = SMALL
+    segs, pm, jt, x, m1, m2 = _stack_inputs(dims, GROUPED, 5, 3, seed=39, per_block=True)
+    got = _run_stack(dims, GROUPED, segs, pm, jt, x, m1, m2, True)
+    want = O.stack_forward(x, pm, jt, seg_tuples(segs), m1, m2, oracle_rope(GROUPED),
+                           per_block_mod=True)
+    assert_close_stack(got, want, x, "grouped stack, per-block modulation")
+
+
 def test_stack_stage1_per_stream_fallback_launches():
     """Streams whose padded rows exceed the workspace run one launch
     sequence per stream."""
