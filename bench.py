@@ -255,9 +255,16 @@ def cpu_baseline(workload_name, blocks=5):
             x = O.block_forward(x, w, segs, mod, rope, dtype=np.float32, attn_chunk=2048)
         dt = time.perf_counter() - t0
     assert np.isfinite(x).all()
+    model = "unknown CPU"
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next(l.split(":", 1)[1].strip() for l in f if l.startswith("model name"))
+    except (OSError, StopIteration):
+        pass
     return {"value": blocks * n / dt, "unit": "block tokens/s", "cores": cores, "kind": "oracle",
             "sample": f"{blocks} joint blocks over the {n}-token {workload_name} sequence, "
-                      f"NumPy float32 ({cores} BLAS and attention threads), {dt:.1f} s"}
+                      f"NumPy float32 ({cores} BLAS and attention threads on {model}), "
+                      f"{dt:.1f} s"}
 
 
 def main():
