@@ -312,6 +312,21 @@ def test_stack_stage1_equal_streams_share_attention():
     assert not np.array_equal(a[200:456], b[200:456])
 
 
+def test_stack_stage1_five_equal_streams_one_attention_launch():
+    """[256 text | 16x16 image | three 16x16 references]: five row groups in
+    each grouped per-mode launch (the references sharing the reference-mode
+    weights), all five streams in one attention launch."""
+    dims = SMALL
+    layout = synth.RopeLayout(256, 16, 16, ((16, 16), (16, 16), (16, 16)))
+    segs, pm, jt, x, m1, m2 = _stack_inputs(dims, layout, 3, 2, seed=41)
+    assert [s.count for s in segs] == [256] * 5
+    got = _run_stack(dims, layout, segs, pm, jt, x, m1, m2, False)
+    want = O.stack_forward(x, pm, jt, seg_tuples(segs), m1, m2, oracle_rope(layout))
+    assert_close_stack(got, want, x, "five streams stack")
+    _, n_proj, n_attn = _stage1_launches(dims, layout, segs, pm, x, m1)
+    assert (n_proj, n_attn) == (3, 3)
+
+
 def test_stack_grouped_per_block_modulation():
     """Grouped per-mode launches with per-block modulation vectors
     (mod_block_stride): each grouped block reads its own block's vectors
