@@ -21,8 +21,8 @@
 // of tile t-1, one of each per slot, with LDS fragments fetched four slots
 // ahead; the order inside a tile is pinned with scheduling barriers.  K and
 // V^T stream from global memory straight into two 4-deep LDS rings (gfx950
-// direct loads, XOR-swizzled rows), K four tiles and V^T two tiles ahead of
-// their use, one workgroup barrier per tile.
+// direct loads, XOR-swizzled rows, spread over the tile's slots), K four
+// tiles and V^T two tiles ahead of their use, one workgroup barrier per tile.
 //
 // Online softmax with lazy rescaling: scores are kept in the log2 domain
 // (log2(e)/sqrt(128) folded into one FMA with the reference); a tile's
@@ -222,11 +222,18 @@ __device__ __forceinline__ float score(const STile& Sc, int idx, int key0, int M
 // 2^TAU and the tile needs no max; otherwise (or on NaN: the first tile,
 // where m_ref is still -inf) `moved` is set and settle() redoes the tile
 // against its true max after the region.
-template <bool QK, bool PV, bool SM, bool MASK>
+// A region's direct loads: none, or a callable taking the load number
+// 0..3 (slots 5, 13, 21 and 29 issue one each).
+struct NoLoads {
+  template <class Q>
+  __device__ void operator()(Q) const {}
+};
+
+template <bool QK, bool PV, bool SM, bool MASK, class Loads = NoLoads>
 __device__ __forceinline__ void region(STile& Sn, uint32_t k_off, f32x16 (&o)[4], uint32_t v_off,
                                        const PTile& Pp, const STile& Sc, PTile& Pc, SoftState& st,
                                        const bf16x8 (&qf)[8], const lds_u8* smem, float scale,
-                                       int key0, int M, int lane) {
+                                       int key0, int M, int lane, const Loads& loads = Loads{}) {
   const int r = lane & 31, hh = lane >> 5;
   // fragment addresses: row base with the lane's swizzle term, the k-step
   // part of the chunk index is xor-ed in per slot
@@ -264,6 +271,7 @@ __device__ __forceinline__ void region(STile& Sn, uint32_t k_off, f32x16 (&o)[4]
       o[d] = mfma32(fr[i], pfrag(Pp[kb][tt]), o[d]);
     }
     if constexpr (i + PREFETCH < 32) load(std::integral_constant<int, i + PREFETCH>{});
+    if constexpr (i % 8 == 5) loads(std::integral_constant<int, i / 8>{});
     if constexpr (SM) {
       // one exponential per slot; odd slots pack the pair of two slots
       // earlier, so the conversion never waits on an exponential just issued
@@ -351,9 +359,9 @@ __device__ __forceinline__ void attend(const AttnArgs& p, const lds_u8* smem, ui
   for (int ks = 0; ks < 8; ++ks)
     qf[ks] = *reinterpret_cast<const bf16x8*>(qh + (size_t)(q0 + r32) * kHeadDim + ks * 16 + hh * 8);
 
-  // DMA group g (issued at the top of tile g of the range): K tile g+4 and
-  // V^T tile g+2, indices clamped to the range; the prologue issues groups
-  // -4..-1.
+  // DMA group g (issued at the top of tile g of the range, or over tile g's
+  // slots in the steady loop): K tile g+4 and V^T tile g+2, indices clamped
+  // to the range; the prologue issues groups -4..-1.
   const DmaLanes dl = dma_lanes(p.n_pad, wave, lane);
   auto k_stage = [](int tile) { return (uint32_t)((tile & (NSTAGE - 1)) * K_BYTES); };
   auto v_stage = [](int tile) { return (uint32_t)(V_RING + (tile & (NSTAGE - 1)) * V_BYTES); };
@@ -382,6 +390,28 @@ __device__ __forceinline__ void attend(const AttnArgs& p, const lds_u8* smem, ui
     __syncthreads();
     issue_group(it);
   };
+  // In the steady loop a tile's group goes out one load per eight slots of
+  // its region instead of all four at the top: eight waves issuing 32 loads
+  // at once after the barrier fill the vector memory queue, and a wave
+  // stalled behind a queued load stalls its MFMAs too.
+  auto top_wait = [&]() {
+    wait_vm<2 * DMA_PER_GROUP>();
+    __syncthreads();
+  };
+  auto spread_group = [&](int g) {
+    return [&, g](auto qc) {
+      constexpr int q = decltype(qc)::value;   // K halves, then V^T halves
+      if constexpr (q < 2) {
+        const int kt = g + 4;
+        const bf16* base = kh + (size_t)(kbase + min(kt, nt - 1) * AKV) * kHeadDim;
+        dma16(base, dl.k[q], lds0 + k_stage(kt) + (8 * wave + 4 * q) * K_ROW);
+      } else {
+        const int vt = g + 2;
+        const bf16* base = vh + kbase + max(0, min(vt, nt - 1)) * AKV;
+        dma16(base, dl.v[q - 2], lds0 + v_stage(vt) + (16 * wave + 8 * (q - 2)) * V_ROW);
+      }
+    };
+  };
 
   // scores of tile 0 (group -4 landed: the later 3 groups may be in flight)
   wait_vm<3 * DMA_PER_GROUP>();
@@ -404,13 +434,13 @@ __device__ __forceinline__ void attend(const AttnArgs& p, const lds_u8* smem, ui
     int it = 1;
     for (; it + 1 < nt - 1; it += 2) {
       // it odd: scores in S1, probabilities to P1; then it+1 even
-      top(it);
+      top_wait();
       region<true, true, true, false>(S0, k_stage(it + 1), o, v_stage(it - 1), P0, S1, P1, st, qf,
-                                      smem, sc, kbase + it * AKV, M, lane);
+                                      smem, sc, kbase + it * AKV, M, lane, spread_group(it));
       settle<false>(o, st, S1, P1, sc, kbase + it * AKV, M, lane);
-      top(it + 1);
+      top_wait();
       region<true, true, true, false>(S1, k_stage(it + 2), o, v_stage(it), P1, S0, P0, st, qf,
-                                      smem, sc, kbase + (it + 1) * AKV, M, lane);
+                                      smem, sc, kbase + (it + 1) * AKV, M, lane, spread_group(it + 1));
       settle<false>(o, st, S0, P0, sc, kbase + (it + 1) * AKV, M, lane);
     }
     if (it < nt - 1) {

@@ -291,11 +291,15 @@ struct Stream {
 // MFMA number IDX (block i = IDX/4, j = IDX%4) of a k-step, followed by its
 // share of the memory instructions, then a scheduling barrier so that the
 // exact order is kept.  bf16 (four k-steps): MFMAs 0..7 of an early k-step
-// read the next k-step's fragments, MFMAs 8..15 of k-step 0 carry the
-// shallow operand's 8 loads of the pending slice, those of k-step 1 the deep
-// operand's.  fp8 (two k-steps, each MFMA twice as long): k-step 0 carries
-// all of them -- fragment reads and shallow loads in MFMAs 0..7, deep loads
-// in 8..15.
+// read the next k-step's fragments; the 16 direct loads of the pending
+// slices go one per four MFMAs over the whole slice -- MFMAs 8, 10, 12, 14
+// of k-steps 0 and 1 the shallow operand's, of k-step 2 and MFMAs 1, 3, 5, 7
+// of the last k-step (before its barrier) the deep operand's -- so that the
+// four waves never queue more direct loads than the vector memory path
+// drains while one MFMA runs (a wave stalled on a full queue also holds back
+// the MFMAs behind the load).  fp8 (two k-steps, each MFMA twice as long):
+// k-step 0 carries all of them -- fragment reads and shallow loads in MFMAs
+// 0..7, deep loads in 8..15.
 template <int KK, int IDX, bool F8, class ST>
 __device__ __forceinline__ void kstep_op(const ST& st, const Frags<F8>& cur, Frags<F8>& nxt,
                                          Acc& acc, const lds_u8* As, const lds_u8* Bs,
@@ -312,10 +316,13 @@ __device__ __forceinline__ void kstep_op(const ST& st, const Frags<F8>& cur, Fra
       if constexpr (IDX < 8) st.template load_shallow<IDX>();
       else st.template load_deep<IDX - 8>();
     } else {
-      if constexpr (IDX >= 8 && KK == 0) st.template load_shallow<IDX - 8>();
-      if constexpr (IDX >= 8 && KK == 1) st.template load_deep<IDX - 8>();
+      constexpr int L = (IDX - 8) / 2;
+      if constexpr (IDX >= 8 && IDX % 2 == 0 && KK == 0) st.template load_shallow<L>();
+      if constexpr (IDX >= 8 && IDX % 2 == 0 && KK == 1) st.template load_shallow<4 + L>();
+      if constexpr (IDX >= 8 && IDX % 2 == 0 && KK == 2) st.template load_deep<L>();
     }
   } else {
+    if constexpr (!F8 && IDX < 8 && IDX % 2 == 1) st.template load_deep<4 + IDX / 2>();
     if constexpr (IDX >= 8) read_frag<IDX - 8>(nxt, As, Bs, st.wm, st.wn, st.lane, 0);
   }
   __builtin_amdgcn_sched_barrier(0);
@@ -331,9 +338,10 @@ __device__ __forceinline__ void kstep_ops(const ST& st, const Frags<F8>& cur, Fr
 // k-step KK of slice kt.  Early k-steps read the next k-step's fragments
 // during their first 8 MFMAs and carry direct loads during the other 8
 // (the shallow operand's slice kt + 1, the deep operand's slice kt + 2).
-// The last k-step runs 8 MFMAs, waits until only the deep operand's loads
-// of this slice are in flight (so both operands' slice kt + 1 has landed
-// for this wave) and meets the other waves at the workgroup barrier --
+// The last k-step runs 8 MFMAs (bf16: with the deep operand's last four
+// loads), waits until only the deep operand's loads of this slice are in
+// flight (so both operands' slice kt + 1 has landed for this wave) and
+// meets the other waves at the workgroup barrier --
 // after which slice kt's buffers are free and slice kt + 1 is complete --
 // then reads slice kt + 1's first fragments during its last 8 MFMAs.
 template <int KK, bool F8, class ST>
