@@ -173,7 +173,6 @@ typedef f32x16 STile[2];        // S^T of one tile: [32-key block]
 typedef uint32_t PTile[2][2][4];
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
-constexpr bf16x2 kOnes2 = {(__bf16)1.0f, (__bf16)1.0f};
 
 __device__ __forceinline__ bf16x8 pfrag(const uint32_t (&w)[4]) {
   const u32x4 v = {w[0], w[1], w[2], w[3]};
@@ -190,7 +189,7 @@ __device__ __forceinline__ void pin(T& v) {
 // Per-query online softmax state of one lane.
 struct SoftState {
   float m_ref;   // reference max, log2 domain
-  float l_sum;   // running sum of the bf16-rounded exp2(s - m_ref) over this lane's keys
+  float l_sum;   // running sum of exp2(s - m_ref) (fp32) over this lane's keys
   bool moved;    // wave-uniform: the last softmax region left its tile to settle()
 };
 
@@ -281,8 +280,9 @@ __device__ __forceinline__ void region(STile& Sn, uint32_t k_off, f32x16 (&o)[4]
         constexpr int idx = decltype(jc)::value;
         const f32x2 pp = {pq[idx & 3], pq[(idx + 1) & 3]};
         const bf16x2 pb = __builtin_convertvector(pp, bf16x2);
-        // the running sum takes the bf16 probabilities the PV product uses
-        l = __builtin_amdgcn_fdot2_f32_bf16(pb, kOnes2, l, false);
+        // the running sum adds the fp32 probabilities (two full-rate adds
+        // cost less than one v_dot2c of the bf16 pair)
+        l += pp[0] + pp[1];
         uint32_t w = __builtin_bit_cast(uint32_t, pb);
         pin(w);
         Pc[idx >> 4][(idx >> 3) & 1][(idx & 7) >> 1] = w;
@@ -326,7 +326,7 @@ __device__ __forceinline__ void settle(f32x16 (&o)[4], SoftState& st, const STil
       pp[u] = __builtin_amdgcn_exp2f(
           __builtin_fmaf(score<MASK>(Sc, idx + u, key0, M, hh), scale, -m_new));
     const bf16x2 pb = __builtin_convertvector(pp, bf16x2);
-    l = __builtin_amdgcn_fdot2_f32_bf16(pb, kOnes2, l, false);
+    l += pp[0] + pp[1];
     Pc[idx >> 4][(idx >> 3) & 1][(idx & 7) >> 1] = __builtin_bit_cast(uint32_t, pb);
   }
   st.l_sum = st.l_sum * alpha + l;

@@ -11,7 +11,7 @@ even) exactly where the HIP kernels keep a value in bf16:
   q, k after RMS normalisation and the rotation (the attention inputs)
   v    the value projection
   P    the softmax numerators before the P.V product (the running sum adds
-       the same rounded values)
+       them unrounded, in fp32, as the attention kernel does)
   o    the normalised attention output
   act  silu(gate) * up (the output GEMM's second input)
 
@@ -78,8 +78,8 @@ def block(x, w, segs, mod, rope, eps=1e-6):
     sc = 1.0 / np.sqrt(hd)
     for hh in range(H):
         s = (q[:, hh] @ k[:, hh].T) * sc
-        p = _bf(torch.exp(s - s.max(-1, keepdim=True).values))
-        o[:, hh] = (p @ v[:, hh]) / p.sum(-1, keepdim=True)
+        p = torch.exp(s - s.max(-1, keepdim=True).values)
+        o[:, hh] = (_bf(p) @ v[:, hh]) / p.sum(-1, keepdim=True)
     o = _bf(o.reshape(n, D))
     g = h @ wf["w_gate"].T
     act = _bf(g * torch.sigmoid(g) * (h @ wf["w_up"].T))
