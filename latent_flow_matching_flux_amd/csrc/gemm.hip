@@ -145,6 +145,16 @@ __device__ __forceinline__ void dma16(const bf16* g, uint32_t lds_off) {
                : "m0");
 }
 
+// The same load from base + voff: a base uniform over the wave (SGPRs) and
+// a per-lane byte offset, so that a slice's k offset moves only the scalar
+// base and the lanes' offsets stay fixed over the main loop.
+__device__ __forceinline__ void dma16s(const bf16* base, uint32_t voff, uint32_t lds_off) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               :
+               : "v"(voff), "s"(base), "s"(lds_off)
+               : "m0");
+}
+
 template <int N>
 __device__ __forceinline__ void wait_vm() {
   asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
@@ -160,16 +170,19 @@ template <int I, bool P>
 __device__ __forceinline__ void issue_load(const Src& S, int koff, uint32_t dst, int wave,
                                            int lane) {
   constexpr int i = I % LOADS_PER_OP;
-  const bf16* g;
+  const bf16* base;
+  uint32_t off;   // bytes from the slice's base; fits 32 bits for rows shorter than 2^24 elements
   if constexpr (P) {
-    g = S.lo + i * S.ld + koff + lane * 8;
+    base = S.lo + koff;
+    off = (uint32_t)(i * S.ld + lane * 8) * 2u;
   } else {
     const int rsub = lane / CPR, slot = lane % CPR;
     const int rr = i * ROWS_PER_KB + rsub;                 // row within this wave's 64
     const int c = slot ^ ((rr / SWZ_DIV) % CPR);
-    g = (i * ROWS_PER_KB < 32 ? S.lo : S.hi) + (rr & 31) * S.ld + koff + c * 8;
+    base = (i * ROWS_PER_KB < 32 ? S.lo : S.hi) + koff;
+    off = (uint32_t)((rr & 31) * S.ld + c * 8) * 2u;
   }
-  dma16(g, dst + (uint32_t)((64 * wave + i * ROWS_PER_KB) * ROW_BYTES));
+  dma16s(base, off, dst + (uint32_t)((64 * wave + i * ROWS_PER_KB) * ROW_BYTES));
 }
 
 // Element offset of k (a multiple of BK) in a row-major or packed operand.
