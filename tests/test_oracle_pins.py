@@ -408,6 +408,26 @@ def test_block_token_permutation_equivariance():
     np.testing.assert_allclose(b, a[perm], rtol=1e-12, atol=1e-12)
 
 
+def test_block_identical_tokens_equal_one_token_block():
+    """Identical input rows in one segment give identical value rows, and
+    attention over equal values returns that value whatever the weights, so
+    each output row is the block over that token alone -- at any position
+    (the premise of the maximum-size GPU test)."""
+    D, F = 256, 32
+    w = _tiny_weights(D, F)
+    x1 = _rand(1, D)
+    mod = _rand(1, 3, D) * 0.2
+    tab = O.rope_tables(O.token_positions(0, 3, 4))
+    want = O.block_forward(x1, w, [(0, 1, 1)], mod, tab[5:6])
+    got = O.block_forward(np.repeat(x1, 12, 0), w, [(0, 12, 1)], mod, tab)
+    np.testing.assert_allclose(got, np.repeat(want, 12, 0), rtol=1e-12, atol=1e-12)
+    # distinct rows do mix through attention
+    x2 = np.repeat(x1, 12, 0)
+    x2[7] += _rand(D)   # (a constant shift would vanish in the LayerNorm)
+    got2 = O.block_forward(x2, w, [(0, 12, 1)], mod, tab)
+    assert np.abs(got2[0] - want[0]).max() > 1e-6
+
+
 def test_block_rows_matches_full_block():
     D, F = 256, 32
     w = _tiny_weights(D, F)
