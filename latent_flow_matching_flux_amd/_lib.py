@@ -340,26 +340,14 @@ def stack_forward(dims, per_mode, joint, x, segs, mod_stage1, mod_stage2, rope, 
                   mod_block_stride=0, n_tokens=None, workspace_nbytes=None, stream=None):
     """flux3_stack_forward.  per_mode: {mode: [weights dict, ...]} (equal
     lengths) or a flat list of 3*n_pm weights; joint: list of weights."""
-    if isinstance(per_mode, dict):
-        n_pm = max((len(v) for v in per_mode.values()), default=0)
-        flat = []
-        for m in range(3):
-            blocks = per_mode.get(m, [])
-            for b in range(n_pm):
-                flat.append(make_weights(blocks[b]) if b < len(blocks) else BlockWeights())
-    else:
-        flat = [make_weights(w) for w in per_mode]
-        n_pm = len(flat) // 3
-    pm_arr = (BlockWeights * max(len(flat), 1))(*flat)
-    jn = [make_weights(w) for w in joint]
-    j_arr = (BlockWeights * max(len(jn), 1))(*jn)
+    pm_arr, n_pm, j_arr, n_joint = _block_arrays(per_mode, joint)
     seg_arr, n_segs = make_segments(segs)
     if n_tokens is None:
         n_tokens = x.shape[0]
     if workspace_nbytes is None:
         workspace_nbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check(load().flux3_stack_forward(ctypes.byref(make_dims(dims)), pm_arr, n_pm, j_arr,
-                                      len(jn), _ptr(x), n_tokens, seg_arr, n_segs,
+                                      n_joint, _ptr(x), n_tokens, seg_arr, n_segs,
                                       _ptr(mod_stage1), _ptr(mod_stage2), mod_block_stride,
                                       _ptr(rope), _ptr(workspace), workspace_nbytes,
                                       _stream_handle(stream)))
@@ -375,10 +363,7 @@ def modulation_forward(dims, w, t_by_mode, segs, mod, workspace, t_target=None,
     vectors from timesteps.  w: dict with w1, w2, optional w1_tgt, w2_tgt,
     and w_mod (a {mode: tensor} dict or a 3-list, None for unused modes);
     t_by_mode: 3 timesteps (text, image, reference)."""
-    wm = w.get("w_mod", {})
-    mods = [wm.get(m) if isinstance(wm, dict) else wm[m] for m in range(3)]
-    W = ModulationWeights(_ptr(w.get("w1")), _ptr(w.get("w2")), _ptr(w.get("w1_tgt")),
-                          _ptr(w.get("w2_tgt")), (ctypes.c_void_p * 3)(*[_ptr(t) for t in mods]))
+    W = _modulation_weights(w)
     t = (ctypes.c_float * 3)(*[float(v) for v in t_by_mode])
     seg_arr, n_segs = make_segments(segs)
     if workspace_nbytes is None:
