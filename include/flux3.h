@@ -32,9 +32,9 @@
  *     failing call.
  *   - bf16 is bfloat16 (IEEE binary32 upper half); accumulation is fp32.
  *   - Device pointers must be 16-byte aligned (FLUX3_E_ALIGN otherwise).
- *   - Supported dims: head_dim == 128, heads a positive even number,
- *     width == heads * 128, mlp_hidden a positive multiple of 128
- *     (FLUX3_E_UNSUPPORTED otherwise); n_tokens at most 2^20.
+ *   - Supported dims: head_dim == 128, heads a positive even number up
+ *     to 512, width == heads * 128, mlp_hidden a positive multiple of 128
+ *     up to 262144 (FLUX3_E_UNSUPPORTED otherwise); n_tokens at most 2^20.
  *     The model's are width 3072, 24 heads, 128, SwiGLU hidden 9216 [P4].
  */
 #ifndef FLUX3_H
@@ -372,8 +372,8 @@ flux3_status flux3_modulation_forward(const flux3_dims *dims,
 
 /* Token vector sizes at the call's edges: text_dim = 20480 (8 stacked
  * 2,560-value text-encoder states), latent_dim = 128 (one 2x2 patch of the
- * 32-channel latent).  text_dim % 64 == 0; latent_dim % 64 == 0 and
- * latent_dim <= 256. */
+ * 32-channel latent).  text_dim % 64 == 0 and text_dim <= 262144;
+ * latent_dim % 64 == 0 and latent_dim <= 256. */
 typedef struct {
   int32_t text_dim;
   int32_t latent_dim;

@@ -75,6 +75,11 @@ constexpr float kEpsRMS = 1e-6f;
 constexpr int64_t kRowAlign = 256;     // workspace rows are padded to this
 constexpr size_t kBufAlign = 256;      // byte alignment of each workspace buffer
 constexpr int64_t kMaxTokens = 1 << 20;
+// Caps on the dims, far above the model family's (24 heads, hidden 9216), so
+// that the int arithmetic on widths (3 D + 2 F GEMM rows, D + F) stays exact.
+constexpr int kMaxHeads = 512;        // width at most 65536
+constexpr int kMaxHidden = 1 << 18;   // SwiGLU hidden at most 262144
+constexpr int kMaxTextDim = 1 << 18;  // text-encoder feature width at most 262144
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -84,12 +89,14 @@ flux3_status check_dims(const flux3_dims* d) {
   if (!d) return fail(FLUX3_E_INVALID, "dims is NULL");
   if (d->head_dim != 128)
     return fail(FLUX3_E_UNSUPPORTED, "head_dim %d unsupported (must be 128)", d->head_dim);
-  if (d->heads < 2 || d->heads % 2 != 0)
-    return fail(FLUX3_E_UNSUPPORTED, "heads %d unsupported (must be a positive even number)", d->heads);
+  if (d->heads < 2 || d->heads % 2 != 0 || d->heads > kMaxHeads)
+    return fail(FLUX3_E_UNSUPPORTED, "heads %d unsupported (must be a positive even number, at most %d)",
+                d->heads, kMaxHeads);
   if (d->width != d->heads * 128)
     return fail(FLUX3_E_UNSUPPORTED, "width %d != heads*128 (%d)", d->width, d->heads * 128);
-  if (d->mlp_hidden <= 0 || d->mlp_hidden % 128 != 0)
-    return fail(FLUX3_E_UNSUPPORTED, "mlp_hidden %d unsupported (positive multiple of 128)", d->mlp_hidden);
+  if (d->mlp_hidden <= 0 || d->mlp_hidden % 128 != 0 || d->mlp_hidden > kMaxHidden)
+    return fail(FLUX3_E_UNSUPPORTED, "mlp_hidden %d unsupported (positive multiple of 128, at most %d)",
+                d->mlp_hidden, kMaxHidden);
   return FLUX3_OK;
 }
 
@@ -860,7 +867,7 @@ flux3_status flux3_modulation_forward(const flux3_dims* dims, const flux3_modula
 size_t flux3_transformer_workspace_bytes(const flux3_dims* dims, const flux3_io_dims* io_dims,
                                          int64_t n_tokens) {
   if (check_dims(dims) != FLUX3_OK || !io_dims || io_dims->text_dim <= 0 ||
-      io_dims->text_dim % 64 != 0 || io_dims->latent_dim <= 0 || io_dims->latent_dim % 64 != 0 ||
+      io_dims->text_dim % 64 != 0 || io_dims->text_dim > kMaxTextDim || io_dims->latent_dim <= 0 || io_dims->latent_dim % 64 != 0 ||
       io_dims->latent_dim > 256 || n_tokens < 0 || n_tokens > kMaxTokens)
     return 0;
   TransformerLayout L;
@@ -882,8 +889,9 @@ flux3_status flux3_transformer_forward(const flux3_dims* dims, const flux3_io_di
   if (r != FLUX3_OK) return r;
   if (!io_dims) return fail(FLUX3_E_INVALID, "io_dims is NULL");
   const int TD = io_dims->text_dim, LD = io_dims->latent_dim;
-  if (TD <= 0 || TD % 64 != 0)
-    return fail(FLUX3_E_UNSUPPORTED, "text_dim %d unsupported (positive multiple of 64)", TD);
+  if (TD <= 0 || TD % 64 != 0 || TD > kMaxTextDim)
+    return fail(FLUX3_E_UNSUPPORTED, "text_dim %d unsupported (positive multiple of 64, at most %d)",
+                TD, kMaxTextDim);
   if (LD <= 0 || LD % 64 != 0 || LD > 256)
     return fail(FLUX3_E_UNSUPPORTED, "latent_dim %d unsupported (multiple of 64, <= 256)", LD);
   if (!io) return fail(FLUX3_E_INVALID, "io weights struct is NULL");

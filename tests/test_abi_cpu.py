@@ -91,6 +91,10 @@ def test_layout_tokens():
     (_dims(width=3000), E_UNSUPPORTED),
     (_dims(hidden=9200), E_UNSUPPORTED),
     (_dims(hidden=0), E_UNSUPPORTED),
+    (_dims(width=514 * 128, heads=514), E_UNSUPPORTED),
+    (_dims(width=2 ** 30, heads=2 ** 23), E_UNSUPPORTED),
+    (_dims(hidden=(1 << 18) + 128), E_UNSUPPORTED),
+    (_dims(hidden=2 ** 31 - 128), E_UNSUPPORTED),
 ])
 def test_block_rejects_unsupported_dims(dims, status):
     assert _call_block(dims=dims) == status
@@ -353,7 +357,8 @@ def test_transformer_workspace_and_validation():
     n = 336
     need = F.transformer_workspace_bytes(synth.DIMS, io_dims, n)
     assert need >= F.workspace_bytes(synth.DIMS, n) + n * 3072 * 4
-    for bad in (L.IoDims(20480, 100), L.IoDims(20480, 512), L.IoDims(100, 128)):
+    for bad in (L.IoDims(20480, 100), L.IoDims(20480, 512), L.IoDims(100, 128),
+                L.IoDims((1 << 18) + 64, 128), L.IoDims(2 ** 31 - 64, 128)):
         assert F.transformer_workspace_bytes(synth.DIMS, bad, n) == 0
     io = L.IoWeights(*[FAKE + 4096 * i for i in range(5)])
     mw = (L.ModulationWeights * 2)()
@@ -378,6 +383,7 @@ def test_transformer_workspace_and_validation():
 
     assert call(iod=None) == E_INVALID
     assert call(iod=L.IoDims(20480, 96)) == E_UNSUPPORTED
+    assert call(iod=L.IoDims((1 << 18) + 64, 128)) == E_UNSUPPORTED
     assert call(iow=None) == E_INVALID
     assert call(m=None) == E_INVALID
     assert call(segs=((0, 80, 0), (80, 128, 2))) == E_SHAPE                 # no image
